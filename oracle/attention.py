@@ -1,0 +1,150 @@
+"""fp64 masked attention, forward and backward, by the plain definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Definition ("FlashAttention vs. RingAttention", FlashAttention-1 "problem and
+bottleneck"): Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V, with the
+mask applied to the score matrix before the softmax.  The method the pages
+describe is exact (same page: FlashAttention "is not an approximation"), so
+the oracle is the definition itself: full score rows are materialised in fp64,
+masked explicitly, and normalised with an exact two-pass softmax.  There is no
+tiling, no online recurrence and no reordering beyond row blocks.
+
+Readings taken where the pages are silent:
+* scale = 1/sqrt(d) with d the head dimension;
+* the one merged softmax statistic kept for the backward (FlashAttention-2
+  "core optimisations") is the natural-log log-sum-exp, LSE_i = m_i +
+  ln sum_j exp(s_ij - m_i), stored as [B, Hq, S];
+* GQA: query head h reads KV head h // (Hq / Hkv);
+* a row with no allowed key has O_i = 0, LSE_i = -inf and zero gradients.
+
+Backward (standard softmax calculus; the dQ form dQ_i = sum_j dS_ij K_j is
+the dependency named in FlashAttention-2 "core optimisations"):
+  D_i   = dO_i . O_i
+  dP_ij = dO_i . v_j
+  dS_ij = p_ij (dP_ij - D_i)
+  dQ_i  = scale sum_j dS_ij k_j
+  dK_j  = scale sum_i dS_ij q_i
+  dV_j  = sum_i p_ij dO_i
+with dK, dV of a KV head summed over the query heads of its group.
+
+Inputs are float64 arrays already holding the bf16 values (upcast exactly).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import masks
+
+
+def _probs(s, a):
+    """Exact masked softmax of score rows ``s`` under boolean ``a``.
+
+    Returns (p, lse) with p = 0 on masked entries and on empty rows.
+    """
+    sm = np.where(a, s, -np.inf)
+    m = sm.max(axis=1)
+    has = np.isfinite(m)
+    m_safe = np.where(has, m, 0.0)
+    e = np.where(a, np.exp(sm - m_safe[:, None]), 0.0)
+    l = e.sum(axis=1)
+    p = np.where(has[:, None], e / np.where(has, l, 1.0)[:, None], 0.0)
+    lse = np.where(has, m_safe + np.log(np.where(has, l, 1.0)), -np.inf)
+    return p, lse
+
+
+def forward(q, k, v, spec, scale=None, heads=None, row_block=512):
+    """O and LSE for the selected query heads.
+
+    q: [B,S,Hq,d], k/v: [B,S,Hkv,d] float64.  ``heads`` lists the query heads
+    to compute (default: all).  Returns o [B,S,len(heads),d] and
+    lse [B,len(heads),S].
+    """
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    o = np.zeros((B, S, len(heads), d))
+    lse = np.zeros((B, len(heads), S))
+    for b in range(B):
+        for hi, h in enumerate(heads):
+            kv = h // G
+            hm = masks.mask_head(spec, h, Hq, Hkv)
+            kT = k[b, :, kv, :].T
+            vv = v[b, :, kv, :]
+            for i0 in range(0, S, row_block):
+                i1 = min(S, i0 + row_block)
+                s = (q[b, i0:i1, h, :] @ kT) * scale
+                p, l = _probs(s, masks.allowed(spec, i0, i1, hm))
+                o[b, i0:i1, hi, :] = p @ vv
+                lse[b, hi, i0:i1] = l
+    return o, lse
+
+
+def backward(q, k, v, do, spec, scale=None, kv_heads=None, row_block=512):
+    """dQ, dK, dV (and O, LSE) for the selected KV heads and their groups.
+
+    Returns a dict with dq [B,S,G*n,d] for the query heads of the selected KV
+    heads (in order), dk/dv [B,S,n,d], o and lse for the same query heads,
+    and ``heads``, the query head indices covered.
+    """
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kv_heads = list(range(Hkv)) if kv_heads is None else list(kv_heads)
+    heads = [kv * G + g for kv in kv_heads for g in range(G)]
+    nq = len(heads)
+    dq = np.zeros((B, S, nq, d))
+    dk = np.zeros((B, S, len(kv_heads), d))
+    dv = np.zeros((B, S, len(kv_heads), d))
+    o = np.zeros((B, S, nq, d))
+    lse = np.zeros((B, nq, S))
+    for b in range(B):
+        for hi, h in enumerate(heads):
+            kvi = hi // G
+            kv = kv_heads[kvi]
+            hm = masks.mask_head(spec, h, Hq, Hkv)
+            kk = k[b, :, kv, :]
+            vv = v[b, :, kv, :]
+            for i0 in range(0, S, row_block):
+                i1 = min(S, i0 + row_block)
+                qi = q[b, i0:i1, h, :]
+                doi = do[b, i0:i1, h, :]
+                s = (qi @ kk.T) * scale
+                p, l = _probs(s, masks.allowed(spec, i0, i1, hm))
+                oi = p @ vv
+                o[b, i0:i1, hi, :] = oi
+                lse[b, hi, i0:i1] = l
+                D = (doi * oi).sum(axis=1)
+                dp = doi @ vv.T
+                ds = p * (dp - D[:, None])
+                dq[b, i0:i1, hi, :] = (ds @ kk) * scale
+                dk[b, :, kvi, :] += (ds.T @ qi) * scale
+                dv[b, :, kvi, :] += p.T @ doi
+    return {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": lse, "heads": heads}
+
+
+def output_rows(q, k, v, spec, h, rows, scale=None):
+    """O and LSE of query head ``h`` for an arbitrary set of rows only.
+
+    Used to check sampled outputs at sizes where the whole tensor would take
+    too long.  Returns o [len(rows), d], lse [len(rows)] for batch 0.
+    """
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    hm = masks.mask_head(spec, h, Hq, Hkv)
+    kv = h // G
+    o = np.zeros((len(rows), d))
+    lse = np.zeros(len(rows))
+    for r, i in enumerate(rows):
+        s = (k[0, :, kv, :] @ q[0, i, h, :]) * scale
+        p, l = _probs(s[None, :], masks.allowed(spec, i, i + 1, hm))
+        o[r] = p[0] @ v[0, :, kv, :]
+        lse[r] = l[0]
+    return o, lse

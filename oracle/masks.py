@@ -1,0 +1,171 @@
+"""Mask predicates mask(i, j) for the LongCA-bench families, vectorised.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The families are named in the "Long-Context Attention Benchmark" review
+(xllm-io), section 3, mask taxonomy: six regular masks (FULL, CAUSAL, FULL /
+CAUSAL SLIDING WINDOW, FULL / CAUSAL DOCUMENT), six heterogeneous ones (SHARED
+QUESTION, GLOBAL SLIDING, CAUSAL BLOCKWISE, PREFIX LM CAUSAL, PREFIX LM
+DOCUMENT, BLOCK CAUSAL DOCUMENT) and two dynamic block masks (uniform, e.g.
+64x64, and variable-size blocks).  The page gives names only; each predicate
+below states the reading it takes.  ``i`` is the query row, ``j`` the key
+column, both in [0, S) of one packed sequence (Sq = Sk = S).
+
+Every function returns a boolean array ``allowed[i - i0, j]`` for the rows
+[i0, i1) and all S columns.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _doc_ids(doc_lens):
+    return np.repeat(np.arange(len(doc_lens)), doc_lens)
+
+
+def _doc_starts(doc_lens):
+    return np.concatenate([[0], np.cumsum(doc_lens)[:-1]]).astype(np.int64)
+
+
+def base_allowed(spec, i0, i1):
+    """allowed[i-i0, j] for the base family of ``spec`` (no bitmap)."""
+    S = int(spec["S"])
+    i = np.arange(i0, i1, dtype=np.int64)[:, None]
+    j = np.arange(S, dtype=np.int64)[None, :]
+    fam = spec["family"]
+
+    if fam == "full":
+        # FULL: every key is visible.
+        return np.ones((i1 - i0, S), dtype=bool)
+
+    if fam == "causal":
+        # CAUSAL with Sq = Sk: keys up to and including the query position.
+        return j <= i
+
+    if fam == "sliding":
+        # SLIDING WINDOW of width w.  Reading: CAUSAL SW keeps 0 <= i-j < w
+        # (w keys including self); FULL SW keeps |i-j| < w.
+        w = int(spec["window"])
+        if spec["causal"]:
+            return (j <= i) & (i - j < w)
+        return np.abs(i - j) < w
+
+    if fam == "document":
+        # DOCUMENT (packed variable-length sequences): a token sees only its
+        # own document; CAUSAL DOCUMENT additionally requires j <= i.
+        doc = _doc_ids(spec["doc_lens"])
+        same = doc[i0:i1][:, None] == doc[None, :]
+        return same & (j <= i) if spec["causal"] else same
+
+    if fam == "prefix_lm_causal":
+        # PREFIX LM CAUSAL with prefix p: j < p or j <= i (prefix tokens see
+        # the whole prefix bidirectionally; the rest is causal).
+        p = int(spec["prefix"])
+        return (j < p) | (j <= i)
+
+    if fam == "shared_question":
+        # SHARED QUESTION: a question of q tokens followed by answers laid out
+        # consecutively.  Reading: causal everywhere; an answer token sees the
+        # question and its own answer, never another answer.
+        q = int(spec["question"])
+        lens = [q] + list(spec["answers"])
+        seg = _doc_ids(lens)            # 0 = question, k = answer k
+        same = seg[i0:i1][:, None] == seg[None, :]
+        return (j <= i) & ((j < q) | same)
+
+    if fam == "global_sliding":
+        # GLOBAL SLIDING with g global tokens and window w.  Reading: causal;
+        # a key is visible if it is global (j < g) or inside the window
+        # (i - j < w).  Alternative reading (bidirectional): j < g or i < g or
+        # |i - j| < w.
+        g, w = int(spec["globals"]), int(spec["window"])
+        if spec.get("bidirectional", False):
+            return (j < g) | (i < g) | (np.abs(i - j) < w)
+        return (j <= i) & ((j < g) | (i - j < w))
+
+    if fam == "causal_blockwise":
+        # CAUSAL BLOCKWISE with block b, n = ceil(S / b) blocks.  Reading:
+        # rows of blocks 0..n-2 are causal inside their own block; rows of the
+        # last block are causal over the whole sequence.  Alternative reading
+        # (block-causal): blk(j) <= blk(i).
+        b = int(spec["block"])
+        n = (S + b - 1) // b
+        bi, bj = i // b, j // b
+        if spec.get("reading", "last_block_global") == "block_causal":
+            return bj <= bi
+        return (j <= i) & ((bi == bj) | (bi == n - 1))
+
+    if fam == "prefix_lm_document":
+        # PREFIX LM DOCUMENT: the prefix-LM rule applied inside each document,
+        # with that document's own prefix length.
+        lens = spec["doc_lens"]
+        doc = _doc_ids(lens)
+        start = _doc_starts(lens)
+        pre = np.asarray(spec["prefix_lens"], dtype=np.int64)
+        di = doc[i0:i1][:, None]
+        same = di == doc[None, :]
+        return same & ((j < start[di] + pre[di]) | (j <= i))
+
+    if fam == "block_causal_document":
+        # BLOCK CAUSAL DOCUMENT: inside a document, blocks of b tokens counted
+        # from the document start; a token sees every block up to its own.
+        b = int(spec["block"])
+        lens = spec["doc_lens"]
+        doc = _doc_ids(lens)
+        start = _doc_starts(lens)
+        pos = np.arange(S, dtype=np.int64) - start[doc]
+        blk = pos // b
+        same = doc[i0:i1][:, None] == doc[None, :]
+        return same & (blk[None, :] <= blk[i0:i1][:, None])
+
+    raise ValueError(f"unknown mask family {fam!r}")
+
+
+def bitmap_allowed(bitmap, hm, i0, i1, S):
+    """allowed[i-i0, j] = bits[hm][qblk(i)][kblk(j)] for a block bitmap.
+
+    Uniform or variable-size blocks (page 1 section 3, dynamic masks): the
+    block of a position is the b with offsets[b] <= x < offsets[b+1].
+    """
+    qo = np.asarray(bitmap["q_offsets"], dtype=np.int64)
+    ko = np.asarray(bitmap["k_offsets"], dtype=np.int64)
+    qb = np.searchsorted(qo, np.arange(i0, i1), side="right") - 1
+    kb = np.searchsorted(ko, np.arange(S), side="right") - 1
+    bits = bitmap["bits"][hm]
+    return bits[qb][:, kb].astype(bool)
+
+
+def mask_head(spec, h, Hq, Hkv):
+    """Which bitmap head applies to query head h (bitmap heads in {1,Hkv,Hq})."""
+    if "bitmap" not in spec:
+        return 0
+    nh = spec["bitmap"]["bits"].shape[0]
+    if nh == 1:
+        return 0
+    if nh == Hq:
+        return h
+    if nh == Hkv:
+        return h // (Hq // Hkv)
+    raise ValueError("bitmap head count must be 1, Hkv or Hq")
+
+
+def allowed(spec, i0, i1, hm=0):
+    """Full predicate rows [i0, i1): base family AND the optional bitmap."""
+    a = base_allowed(spec, i0, i1)
+    if "bitmap" in spec:
+        a = a & bitmap_allowed(spec["bitmap"], hm, i0, i1, int(spec["S"]))
+    return a
+
+
+def dense_mask(spec, hm=0):
+    """The whole S x S boolean mask (small S only)."""
+    return allowed(spec, 0, int(spec["S"]), hm)
+
+
+def nnz(spec, hm=0, row_block=1024):
+    """Number of allowed (i, j) pairs, by popcount of the predicate."""
+    S = int(spec["S"])
+    tot = 0
+    for i0 in range(0, S, row_block):
+        tot += int(allowed(spec, i0, min(S, i0 + row_block), hm).sum())
+    return tot
