@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark: effective masked-attention TFLOP/s, forward + backward, on one
+MI355X.
+
+A step is one pass of the hot path (forward, backward preprocess, dK/dV
+pass, dQ pass) over every (sequence length, mask) pair of the workload.
+Plans (mask compilation) are built before the timed region: one mask serves
+every layer of a model, so it is compiled once; its build time is reported.
+
+Effective FLOPs count only allowed (i, j) pairs: 4*d per pair per head for
+the forward (Q K^T and P V), 10*d for the backward (five products), whatever
+the kernels recompute.  Inputs are seeded synthetic N(0, 1) tensors rounded
+to bf16, resident in HBM before timing starts.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "effective masked-attention TFLOP/s fwd+bwd (fraction of bf16 MFMA peak)"
+
+# Algorithmic work per allowed (i, j) pair per query head, in units of d
+# flops, of each kernel: forward = Q K^T + P V; dK/dV pass = Q K^T, dO V^T,
+# P^T dO, dS^T Q; dQ pass = Q K^T, dO V^T, dS K.
+KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dkdv": 8, "dq": 6}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload(name, seqs):
+    import synthetic as syn
+    out = []
+    if name == "dense":
+        for S in seqs:
+            for label, spec in syn.config_mask_specs("dense", S):
+                out.append((f"S{S // 1024}K_{label}", S, 64, 8, spec))
+        desc = ("dense regular masks: B=1, GQA Hq=64/Hkv=8, d=128, bf16, S in {"
+                + ", ".join(f"{s // 1024}K" for s in seqs)
+                + "} x {FULL, CAUSAL, causal sliding window w=1024}, fwd+bwd")
+    elif name == "document":
+        for label, spec in syn.config_mask_specs("document"):
+            out.append((label, spec["S"], 64, 8, spec))
+        desc = "document masks: B=1, S=64K, GQA 64:8, d=128, log-uniform lengths in [256, 16K] (seed 0), FULL and CAUSAL DOCUMENT, fwd+bwd"
+    elif name == "hetero":
+        for label, spec in syn.config_mask_specs("hetero"):
+            out.append((label, spec["S"], 64, 8, spec))
+        desc = "heterogeneous masks: B=1, S=32K, GQA 64:8, d=128: PREFIX LM CAUSAL, SHARED QUESTION, GLOBAL SLIDING, CAUSAL BLOCKWISE, fwd+bwd"
+    elif name == "sparse":
+        S = seqs[0] if seqs else 32768
+        for label, spec in syn.config_mask_specs("sparse", S, Hq=64, Hkv=8):
+            out.append((label, S, 64, 8, spec))
+        desc = f"block-sparse masks: B=1, S={S // 1024}K, GQA 64:8, d=128, 50% density, uniform 64/128 and variable blocks, fwd+bwd"
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    return out, desc
+
+
+def cpu_baseline(seconds_cap=30.0):
+    """The fp64 oracle on the host: forward + backward of one query head at
+    S = 8K for each dense mask (FULL, CAUSAL, causal SW w=1024)."""
+    import numpy as np
+    import synthetic as syn
+    from oracle import attention as ora
+    from oracle import masks as om
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    S, d = 8192, 128
+    x = syn.attention_inputs(1, S, 1, 1, d, seed=0)
+    f = {n: syn.bf16_bits_to_f32(x[n]).astype(np.float64) for n in x}
+    flops, secs, done = 0.0, 0.0, []
+    for label, spec in syn.config_mask_specs("dense", S):
+        nnz = om.nnz(spec)
+        t0 = time.perf_counter()
+        ora.backward(f["q"], f["k"], f["v"], f["do"], spec)
+        dt = time.perf_counter() - t0
+        flops += 14.0 * d * nnz
+        secs += dt
+        done.append(label)
+        log(f"cpu oracle {label}: {dt:.2f} s")
+        if secs > seconds_cap:
+            break
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle, forward+backward of 1 query head at S=8K, d=128 for "
+                      f"masks {done}: {secs:.1f} s, effective flops as for the GPU"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="dense", choices=["dense", "document", "hetero", "sparse"])
+    ap.add_argument("--seqs", default="1024,8192,16384,49152")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_masked_amd as lcm
+    import synthetic as syn
+
+    dev = torch.device("cuda:0")
+    seqs = [int(s) for s in args.seqs.split(",") if s]
+    cases, desc = workload(args.workload, seqs)
+    d = 128
+
+    def t(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    tensors = {}
+    runs = []
+    plan_secs = 0.0
+    for label, S, Hq, Hkv, spec in cases:
+        if S not in tensors:
+            log(f"inputs S={S}")
+            x = syn.attention_inputs(1, S, Hq, Hkv, d, seed=0)
+            q, k, v, do = t(x["q"]), t(x["k"]), t(x["v"]), t(x["do"])
+            tensors[S] = dict(q=q, k=k, v=v, do=do, o=torch.empty_like(q),
+                              lse=torch.empty((1, Hq, S), dtype=torch.float32, device=dev),
+                              dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
+        t0 = time.perf_counter()
+        plan = lcm.Plan(1, S, Hq, Hkv, d, spec)
+        plan_secs += time.perf_counter() - t0
+        plan.bind(dev)
+        ws = torch.empty(plan.workspace_bytes() + 256, dtype=torch.uint8, device=dev)
+        runs.append(dict(label=label, S=S, plan=plan, ws=ws, nnz=plan.stats["nnz_total"]))
+        log(f"plan {label}: nnz {plan.stats['nnz_total']:.4g}, fwd partial tiles "
+            f"{plan.stats['fwd_tiles_partial']}, full {plan.stats['fwd_tiles_full']}")
+
+    L = lcm._lib
+    lib = L.lib()
+    P = lambda x: __import__("ctypes").c_void_p(x)
+    stream = torch.cuda.current_stream(dev)
+    sp = P(stream.cuda_stream)
+
+    def one_step(record):
+        for r in runs:
+            tt = tensors[r["S"]]
+            h = r["plan"].handle
+            wptr = r["ws"].data_ptr()
+            wptr += (-wptr) % 256
+            nws = r["plan"].workspace_bytes()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+            if record:
+                ev[0].record(stream)
+            L.check(lib.attn_fwd(h, P(tt["q"].data_ptr()), P(tt["k"].data_ptr()), P(tt["v"].data_ptr()),
+                                 P(tt["o"].data_ptr()), P(tt["lse"].data_ptr()), sp))
+            if record:
+                ev[1].record(stream)
+            L.check(lib.attn_bwd_preprocess(h, P(tt["o"].data_ptr()), P(tt["do"].data_ptr()),
+                                            P(wptr), nws, sp))
+            if record:
+                ev[2].record(stream)
+            L.check(lib.attn_bwd_dkdv(h, P(tt["q"].data_ptr()), P(tt["k"].data_ptr()), P(tt["v"].data_ptr()),
+                                      P(tt["lse"].data_ptr()), P(tt["do"].data_ptr()), P(tt["dk"].data_ptr()),
+                                      P(tt["dv"].data_ptr()), P(wptr), nws, sp))
+            if record:
+                ev[3].record(stream)
+            L.check(lib.attn_bwd_dq(h, P(tt["q"].data_ptr()), P(tt["k"].data_ptr()), P(tt["v"].data_ptr()),
+                                    P(tt["lse"].data_ptr()), P(tt["do"].data_ptr()), P(tt["dq"].data_ptr()),
+                                    P(wptr), nws, sp))
+            if record:
+                ev[4].record(stream)
+                r.setdefault("events", []).append(ev)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    kern = {"fwd": 0.0, "pre": 0.0, "dkdv": 0.0, "dq": 0.0}
+    alg = {"fwd": 0.0, "dkdv": 0.0, "dq": 0.0}
+    launches = {"fwd": 0, "dkdv": 0, "dq": 0, "pre": 0}
+    pre_bytes = 0.0
+    detail = {}
+    eff_fwd = eff_bwd = 0.0
+    for r in runs:
+        ms = np.zeros(4)
+        for ev in r["events"]:
+            ms += [ev[j].elapsed_time(ev[j + 1]) for j in range(4)]
+        n = len(r["events"])
+        for j, key in enumerate(("fwd", "pre", "dkdv", "dq")):
+            kern[key] += ms[j] / 1e3
+            launches[key] += n
+        for key in alg:
+            alg[key] += KERNEL_FLOPS_PER_PAIR[key] * d * r["nnz"] * n
+        Hq = 64
+        pre_bytes += 2.0 * r["S"] * Hq * d * 2 * n + r["S"] * Hq * 4 * n
+        ffl, bfl = 4.0 * d * r["nnz"], 10.0 * d * r["nnz"]
+        eff_fwd += ffl * n
+        eff_bwd += bfl * n
+        detail[r["label"]] = {"fwd_tflops": round(ffl * n / (ms[0] / 1e3) / 1e12, 1),
+                              "bwd_tflops": round(bfl * n / (ms[1:].sum() / 1e3) / 1e12, 1),
+                              "fwd_ms": round(ms[0] / n, 3), "bwd_ms": round(ms[1:].sum() / n, 3)}
+    total_flops = eff_fwd + eff_bwd
+    value = total_flops / wall / 1e12
+    t_fwd = kern["fwd"]
+    t_bwd = kern["pre"] + kern["dkdv"] + kern["dq"]
+    dom = max(("fwd", "dkdv", "dq"), key=lambda k: kern[k])
+    achieved = alg[dom] / kern[dom] / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "global_batch": 1, "seq_len": max(r["S"] for r in runs),
+                   "cases": [r["label"] for r in runs]},
+        "fraction_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"tflops": round(eff_fwd / t_fwd / 1e12, 2),
+                "fraction_of_peak": round(eff_fwd / t_fwd / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"tflops": round(eff_bwd / t_bwd / 1e12, 2),
+                "fraction_of_peak": round(eff_bwd / t_bwd / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "preprocess_GBps": round(pre_bytes / kern["pre"] / 1e9, 1)},
+        "kernel_ms_per_launch": {k: round(kern[k] / launches[k] * 1e3, 4) for k in kern},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "plan_build_s": round(plan_secs, 3),
+        "detail": detail,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+/*
+ * attn.h -- masked attention, forward and backward, for MI355X (gfx950).
+ *
+ * Computes O = softmax(mask(Q K^T * scale)) V and its gradients, the core
+ * attention of "FlashAttention vs. RingAttention" (dtcms), FlashAttention-1
+ * "problem and bottleneck" (softmax(Q K^T / sqrt(d_k)) V), under the mask
+ * families of the "Long-Context Attention Benchmark" review (xllm-io),
+ * section 3 "mask taxonomy".  That review's kernel adapter gives all kernels
+ * one input representation; this header is that representation for one GPU.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every call returns attn_status.  On any status other than ATTN_OK,
+ *   attn_last_error() returns a message (thread-local, valid until the next
+ *   call on the same thread).  No C++ exception crosses this interface.
+ * - All validation happens before any GPU work is enqueued: on an error
+ *   nothing is launched and no output buffer is written.
+ * - The library allocates no device memory.  The caller allocates and owns
+ *   every device buffer (tensors, workspace, the plan's device blob) and keeps
+ *   it alive until the work enqueued on `stream` has completed.
+ * - Device tensors are contiguous, bf16 unless stated, 16-byte aligned:
+ *     Q, O, dO, dQ : [B, S, Hq,  d]   (d innermost)
+ *     K, V, dK, dV : [B, S, Hkv, d]
+ *     LSE          : [B, Hq, S] float32, natural log of the softmax
+ *                    normaliser (the single merged statistic of
+ *                    FlashAttention-2, "core optimisations"); -inf on a row
+ *                    that no key may attend to (whose O row is then 0).
+ *   Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
+ * - Sq = Sk = S: self-attention over one packed sequence per batch entry;
+ *   the mask is the same for every batch entry.
+ * - Supported: d in {64, 128}, Hq % Hkv == 0, 1 <= S < 2^30.
+ * - Launches are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *   stream).  Device faults surface at the caller's next synchronisation.
+ */
+#ifndef LCM_ATTN_H
+#define LCM_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *attn_stream_t; /* same object as hipStream_t */
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = 1,     /* malformed argument or descriptor            */
+  ATTN_ERR_UNSUPPORTED = 2, /* well-formed but outside what is implemented */
+  ATTN_ERR_NOMEM = 3,       /* host allocation failed                      */
+  ATTN_ERR_DEVICE = 4       /* a HIP call or kernel launch failed          */
+} attn_status;
+
+/*
+ * Mask families.  i is the query row, j the key column, both in [0, S).
+ *   FULL           every pair allowed.
+ *   CAUSAL         j <= i.
+ *   SLIDING        i - j < window_left and j - i < window_right; with
+ *                  causal = 1 also j <= i (window_right is then ignored).
+ *                  CAUSAL SLIDING WINDOW w: window_left = w, causal = 1
+ *                  (w keys including the diagonal); FULL SLIDING WINDOW w:
+ *                  window_left = window_right = w (|i - j| < w).
+ *   DOCUMENT       doc(i) == doc(j) for documents cut by cu_seqlens; with
+ *                  causal = 1 also j <= i.
+ *   PREFIX_LM      doc(i) == doc(j) and (j < start(doc) + prefix_lens[doc]
+ *                  or j <= i).  One document of length S is PREFIX LM CAUSAL.
+ *   COLUMN_BOUNDS  per key column j, four int32 {lts, lte, uts, ute}: row i
+ *                  is masked for column j iff lts <= i < lte or
+ *                  uts <= i < ute (the column-wise representation the review
+ *                  attributes to FlashMask).  Any of the twelve static
+ *                  families can be written this way; SHARED QUESTION, GLOBAL
+ *                  SLIDING, CAUSAL BLOCKWISE and BLOCK CAUSAL DOCUMENT are.
+ *                  Each query row must end up with at most two maximal runs
+ *                  of allowed keys (true of all twelve families), else
+ *                  ATTN_ERR_UNSUPPORTED.
+ * Optional block bitmap (the review's dynamic block masks, uniform such as
+ * 64x64 or variable-size): the final mask is base(i, j) AND
+ * bitmap[hm][qblk(i)][kblk(j)], where qblk(i) is the b with
+ * q_blk_offsets[b] <= i < q_blk_offsets[b+1] (likewise kblk) and hm is the
+ * bitmap head of query head h: 0 if bitmap_heads == 1, h / (Hq / Hkv) if
+ * bitmap_heads == Hkv, h if bitmap_heads == Hq (the last only when
+ * Hq == Hkv).
+ */
+typedef enum {
+  ATTN_MASK_FULL = 0,
+  ATTN_MASK_CAUSAL = 1,
+  ATTN_MASK_SLIDING = 2,
+  ATTN_MASK_DOCUMENT = 3,
+  ATTN_MASK_PREFIX_LM = 4,
+  ATTN_MASK_COLUMN_BOUNDS = 5
+} attn_mask_kind;
+
+typedef struct {
+  int64_t B, S, Hq, Hkv, d;
+  float scale; /* softmax scale; 0 selects 1/sqrt(d) */
+} attn_shape;
+
+/* All arrays are host memory, read during attn_plan_create only (copied). */
+typedef struct {
+  int32_t kind;                  /* attn_mask_kind                              */
+  int32_t causal;                /* SLIDING, DOCUMENT: 0 or 1                   */
+  int32_t window_left;           /* SLIDING: >= 1                               */
+  int32_t window_right;          /* SLIDING with causal = 0: >= 1               */
+  int32_t num_docs;              /* DOCUMENT, PREFIX_LM: >= 1                   */
+  const int32_t *cu_seqlens;     /* [num_docs+1], 0 = c_0 < c_1 < ... = S       */
+  const int32_t *prefix_lens;    /* PREFIX_LM: [num_docs], 0 <= p_k <= len_k    */
+  const int32_t *col_bounds;     /* COLUMN_BOUNDS: [S][4], each in [0, S]       */
+  const uint8_t *block_bitmap;   /* optional: [bitmap_heads][n_qblk][n_kblk]   */
+  int32_t bitmap_heads, n_qblk, n_kblk;
+  const int32_t *q_blk_offsets;  /* [n_qblk+1], 0 = o_0 < ... < o_n = S        */
+  const int32_t *k_blk_offsets;  /* [n_kblk+1], likewise                       */
+} attn_mask_desc;
+
+typedef struct attn_plan attn_plan;
+
+typedef struct {
+  int64_t nnz_per_batch;   /* allowed (i,j) pairs summed over the Hq heads   */
+  int64_t nnz_total;       /* nnz_per_batch * B                              */
+  double flops_fwd;        /* 4 * d * nnz_total  (QK^T and PV)               */
+  double flops_bwd;        /* 10 * d * nnz_total (five products)             */
+  int64_t fwd_items, fwd_tiles_full, fwd_tiles_partial;   /* forward / dQ    */
+  int64_t bwd_items, bwd_tiles_full, bwd_tiles_partial;   /* dK/dV pass      */
+  int64_t fwd_tile_rows, fwd_tile_cols, bwd_tile_rows, bwd_tile_cols;
+  int64_t heads_per_item;  /* query heads sharing one K/V tile in fwd / dQ   */
+  int64_t device_bytes;    /* size of the device blob                        */
+} attn_stats;
+
+/*
+ * Compile the mask for `shape`: validate, classify every (Q-tile, K-tile)
+ * pair as empty, full or partial, build the per-Q-tile (forward, dQ) and
+ * per-K-tile (dK/dV) work lists and order them longest-first.  Host only: no
+ * HIP call is made.  On success *out owns host memory only.
+ */
+attn_status attn_plan_create(const attn_shape *shape, const attn_mask_desc *desc,
+                             attn_plan **out);
+
+/* Bytes of device memory the caller must provide to attn_plan_bind. */
+size_t attn_plan_device_bytes(const attn_plan *plan);
+
+/*
+ * Copy the plan's metadata (work lists, row/column bounds, bitmap) into the
+ * caller's device buffer `dev_buf` (>= attn_plan_device_bytes, 256-byte
+ * aligned) with an asynchronous host-to-device copy on `stream`, and record
+ * the buffer in the plan.  Must precede attn_fwd / attn_bwd; binding again
+ * replaces the recorded buffer.  Not thread-safe against concurrent use of
+ * the same plan.
+ */
+attn_status attn_plan_bind(attn_plan *plan, void *dev_buf, size_t bytes,
+                           attn_stream_t stream);
+
+attn_status attn_plan_stats(const attn_plan *plan, attn_stats *out);
+
+/* Host view of the device blob and its section offsets (tests, tooling). */
+typedef struct {
+  const void *blob;
+  int64_t blob_bytes;
+  int64_t off_rowb, off_colb;           /* int32 [S][4] each               */
+  int64_t off_fwd_items, n_fwd_items;   /* int32 [n][4]: tile, h0, off, len */
+  int64_t off_fwd_list, n_fwd_list;     /* uint32 [n]: tile | partial<<31  */
+  int64_t off_bwd_items, n_bwd_items;   /* int32 [n][4]: tile, kvh, off, len */
+  int64_t off_bwd_list, n_bwd_list;     /* uint32 [n]                      */
+  int64_t off_bits, off_qblk, off_kblk, off_qoffs, off_koffs; /* -1 if none */
+} attn_plan_layout;
+
+attn_status attn_plan_get_layout(const attn_plan *plan, attn_plan_layout *out);
+
+/* Bytes of device workspace attn_bwd needs (the per-row D = rowsum(dO*O)). */
+size_t attn_bwd_workspace_bytes(const attn_plan *plan);
+
+/*
+ * Forward: O and LSE.  Q-split: one workgroup per (Q-tile, group of query
+ * heads sharing a KV head), iterating over its non-empty K-tiles (the Q-split
+ * of FlashAttention-2, "core optimisations"; online softmax with deferred
+ * rescaling of FlashAttention-1/2).
+ */
+attn_status attn_fwd(const attn_plan *plan, const void *q, const void *k,
+                     const void *v, void *o, float *lse, attn_stream_t stream);
+
+/*
+ * Backward: dQ, dK, dV from Q, K, V, the forward's O and LSE, and dO.
+ * Three launches on `stream`: D = rowsum(dO * O) into `ws`; a KV-split pass
+ * (one workgroup per K-tile and KV head) accumulating dK and dV; a Q-split
+ * pass accumulating dQ = scale * sum_j dS_ij K_j (the row/column two-axis
+ * split of FlashAttention-2, "core optimisations").  dK and dV of a KV head
+ * are summed over its query-head group.  `ws` is a device buffer of at least
+ * attn_bwd_workspace_bytes(plan) bytes, 256-byte aligned.
+ */
+attn_status attn_bwd(const attn_plan *plan, const void *q, const void *k,
+                     const void *v, const void *o, const float *lse,
+                     const void *dout, void *dq, void *dk, void *dv, void *ws,
+                     size_t ws_bytes, attn_stream_t stream);
+
+/*
+ * The three stages of attn_bwd, callable one at a time on the same stream
+ * and in this order (attn_bwd is exactly these three calls).  They exist so
+ * that callers can interleave other work between stages and time them.
+ *   attn_bwd_preprocess: ws <- D = rowsum(dO * O), fp32 [B, Hq, S].
+ *   attn_bwd_dkdv:       dK, dV from Q, K, V, LSE, dO and D in ws.
+ *   attn_bwd_dq:         dQ from Q, K, V, LSE, dO and D in ws.
+ * Arguments have the meaning and requirements given for attn_bwd.
+ */
+attn_status attn_bwd_preprocess(const attn_plan *plan, const void *o, const void *dout,
+                                void *ws, size_t ws_bytes, attn_stream_t stream);
+attn_status attn_bwd_dkdv(const attn_plan *plan, const void *q, const void *k,
+                          const void *v, const float *lse, const void *dout, void *dk,
+                          void *dv, const void *ws, size_t ws_bytes, attn_stream_t stream);
+attn_status attn_bwd_dq(const attn_plan *plan, const void *q, const void *k,
+                        const void *v, const float *lse, const void *dout, void *dq,
+                        const void *ws, size_t ws_bytes, attn_stream_t stream);
+
+void attn_plan_destroy(attn_plan *plan);
+
+const char *attn_last_error(void);
+
+/* Library version string. */
+const char *attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCM_ATTN_H */

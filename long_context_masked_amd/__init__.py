@@ -1,0 +1,177 @@
+"""MI355X-native masked attention (forward and backward) for long contexts.
+
+Python face of libattn.so (include/attn.h).  PyTorch supplies device memory
+and the current stream; every step of the computation (mask compilation,
+forward, backward) runs in the library.  There is no fallback path: if the
+library is not built, every call raises.
+
+    plan = Plan(B, S, Hq, Hkv, d, mask_spec)        # compile + upload the mask
+    o, lse = fwd(plan, q, k, v)                      # q [B,S,Hq,d] bf16, k/v [B,S,Hkv,d]
+    dq, dk, dv = bwd(plan, q, k, v, o, lse, do)
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from . import _lib as L
+from .masks import MaskDescriptor, column_bounds  # noqa: F401
+
+__all__ = ["Plan", "fwd", "bwd", "attention", "MaskDescriptor", "column_bounds",
+           "AttnError", "library_path"]
+
+AttnError = L.AttnError
+library_path = L.LIB_PATH
+
+
+class Plan:
+    """A compiled mask for one shape: work lists, bounds and bitmap.
+
+    Creation runs on the host only; ``bind()`` (called lazily by fwd/bwd)
+    uploads the metadata into a torch-allocated device buffer.
+    """
+
+    def __init__(self, B, S, Hq, Hkv, d, mask, scale=0.0):
+        self.shape = (int(B), int(S), int(Hq), int(Hkv), int(d))
+        self.desc = mask if isinstance(mask, MaskDescriptor) else MaskDescriptor(mask)
+        if self.desc.S != int(S):
+            raise ValueError(f"mask is for S={self.desc.S}, shape has S={S}")
+        sh = L.Shape(int(B), int(S), int(Hq), int(Hkv), int(d), float(scale))
+        h = C.c_void_p()
+        L.check(L.lib().attn_plan_create(C.byref(sh), C.byref(self.desc.c), C.byref(h)))
+        self._h = h
+        st = L.Stats()
+        L.check(L.lib().attn_plan_stats(h, C.byref(st)))
+        self.stats = {name: getattr(st, name) for name, _ in L.Stats._fields_}
+        self._dev = None
+        self._dev_index = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def device_bytes(self):
+        return int(L.lib().attn_plan_device_bytes(self._h))
+
+    def workspace_bytes(self):
+        return int(L.lib().attn_bwd_workspace_bytes(self._h))
+
+    def bind(self, device=None):
+        import torch
+        dev = torch.device("cuda" if device is None else device)
+        idx = dev.index if dev.index is not None else torch.cuda.current_device()
+        if self._dev is not None and self._dev_index == idx:
+            return self
+        n = self.device_bytes()
+        buf = torch.empty(max(n, 256) + 256, dtype=torch.uint8, device=dev)
+        ptr = buf.data_ptr()
+        off = (-ptr) % 256
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        L.check(L.lib().attn_plan_bind(self._h, C.c_void_p(ptr + off), C.c_size_t(n),
+                                       C.c_void_p(stream)))
+        self._dev, self._dev_index = buf, idx
+        return self
+
+    def layout(self):
+        """Host copy of the device blob's sections as numpy arrays."""
+        lay = L.Layout()
+        L.check(L.lib().attn_plan_get_layout(self._h, C.byref(lay)))
+        raw = np.ctypeslib.as_array((C.c_uint8 * lay.blob_bytes).from_address(lay.blob)).copy()
+        S = self.shape[1]
+
+        def i32(off, n):
+            return raw[off:off + 4 * n].view(np.int32)
+
+        out = {
+            "rowb": i32(lay.off_rowb, 4 * S).reshape(S, 4),
+            "colb": i32(lay.off_colb, 4 * S).reshape(S, 4),
+            "fwd_items": i32(lay.off_fwd_items, 4 * lay.n_fwd_items).reshape(-1, 4),
+            "fwd_list": raw[lay.off_fwd_list:lay.off_fwd_list + 4 * lay.n_fwd_list].view(np.uint32),
+            "bwd_items": i32(lay.off_bwd_items, 4 * lay.n_bwd_items).reshape(-1, 4),
+            "bwd_list": raw[lay.off_bwd_list:lay.off_bwd_list + 4 * lay.n_bwd_list].view(np.uint32),
+        }
+        return out
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                L.lib().attn_plan_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+
+def _check_tensor(t, name, shape, torch):
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+
+
+def fwd(plan: Plan, q, k, v, out=None, lse=None):
+    """O [B,S,Hq,d] bf16 and LSE [B,Hq,S] fp32 (natural log)."""
+    import torch
+    B, S, Hq, Hkv, d = plan.shape
+    _check_tensor(q, "q", (B, S, Hq, d), torch)
+    _check_tensor(k, "k", (B, S, Hkv, d), torch)
+    _check_tensor(v, "v", (B, S, Hkv, d), torch)
+    plan.bind(q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    L.check(L.lib().attn_fwd(plan.handle, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
+                             C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()),
+                             C.c_void_p(lse.data_ptr()), C.c_void_p(stream)))
+    return o, lse
+
+
+def bwd(plan: Plan, q, k, v, o, lse, do, workspace=None, grads=None):
+    """dQ, dK, dV (bf16) from the forward's O and LSE and the output gradient dO."""
+    import torch
+    B, S, Hq, Hkv, d = plan.shape
+    for t, n, s in ((q, "q", (B, S, Hq, d)), (k, "k", (B, S, Hkv, d)), (v, "v", (B, S, Hkv, d)),
+                    (o, "o", (B, S, Hq, d)), (do, "do", (B, S, Hq, d))):
+        _check_tensor(t, n, s, torch)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, Hq, S]")
+    plan.bind(q.device)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = grads
+    nws = plan.workspace_bytes()
+    ws = torch.empty(nws + 256, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    wptr = ws.data_ptr()
+    wptr += (-wptr) % 256
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    P = C.c_void_p
+    L.check(L.lib().attn_bwd(plan.handle, P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
+                             P(o.data_ptr()), P(lse.data_ptr()), P(do.data_ptr()),
+                             P(dq.data_ptr()), P(dk.data_ptr()), P(dv.data_ptr()), P(wptr),
+                             C.c_size_t(nws), P(stream)))
+    return dq, dk, dv
+
+
+def attention(q, k, v, plan: Plan):
+    """Differentiable masked attention through torch.autograd."""
+    import torch
+
+    class _Attn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q_, k_, v_):
+            o, lse = fwd(plan, q_, k_, v_)
+            ctx.save_for_backward(q_, k_, v_, o, lse)
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q_, k_, v_, o, lse = ctx.saved_tensors
+            return bwd(plan, q_, k_, v_, o, lse, do.contiguous())
+
+    return _Attn.apply(q, k, v)

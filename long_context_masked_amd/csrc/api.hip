@@ -1,0 +1,250 @@
+// C-ABI entry points that touch the GPU: plan binding, forward, backward.
+// All argument checks run before anything is enqueued.
+#include <cstdint>
+#include <cstdlib>
+
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace lcm {
+hipError_t launch_fwd(const FwdArgs &a, int d, int HG, int n_items, int B, hipStream_t st);
+hipError_t launch_bwd_pre(const BwdArgs &a, int d, int B, hipStream_t st);
+hipError_t launch_dkdv(const BwdArgs &a, int d, int B, hipStream_t st);
+hipError_t launch_dq(const BwdArgs &a, int d, int HG, int B, hipStream_t st);
+}  // namespace lcm
+
+using namespace lcm;
+
+namespace {
+
+template <typename T>
+const T *sect(const attn_plan *p, int64_t off) {
+  return off < 0 ? nullptr
+                 : reinterpret_cast<const T *>(static_cast<const uint8_t *>(p->dev_blob) + off);
+}
+
+MaskArgs mask_args(const attn_plan *p) {
+  MaskArgs m{};
+  m.rowb = sect<int4>(p, p->lay.rowb);
+  m.colb = sect<int4>(p, p->lay.colb);
+  m.bits = sect<uint8_t>(p, p->lay.bits);
+  m.qblk = sect<int>(p, p->lay.qblk);
+  m.kblk = sect<int>(p, p->lay.kblk);
+  m.qoffs = sect<int>(p, p->lay.qoffs);
+  m.koffs = sect<int>(p, p->lay.koffs);
+  m.nqb = p->nqb;
+  m.nkb = p->nkb;
+  m.bm_heads = p->bitmap_heads;
+  return m;
+}
+
+bool misaligned(const void *x, uintptr_t a) { return (reinterpret_cast<uintptr_t>(x) & (a - 1)) != 0; }
+
+attn_status check_tensor(const void *x, const char *name, uintptr_t align) {
+  if (!x) return fail(ATTN_ERR_INVALID, "%s is NULL", name);
+  if (misaligned(x, align)) return fail(ATTN_ERR_INVALID, "%s is not %u-byte aligned", name, (unsigned)align);
+  return ATTN_OK;
+}
+
+// Host-forced device error, to exercise the error path without a GPU.
+bool forced_device_error() {
+  const char *e = std::getenv("ATTN_FORCE_DEVICE_ERROR");
+  return e && e[0] == '1';
+}
+
+attn_status check_plan(const attn_plan *p) {
+  if (!p) return fail(ATTN_ERR_INVALID, "plan is NULL");
+  if (!p->dev_blob) return fail(ATTN_ERR_INVALID, "plan is not bound to device memory");
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" attn_status attn_plan_bind(attn_plan *plan, void *dev_buf, size_t bytes,
+                                      attn_stream_t stream) {
+  clear_error();
+  if (!plan) return fail(ATTN_ERR_INVALID, "plan is NULL");
+  if (!dev_buf) return fail(ATTN_ERR_INVALID, "dev_buf is NULL");
+  if (misaligned(dev_buf, 256)) return fail(ATTN_ERR_INVALID, "dev_buf is not 256-byte aligned");
+  if (bytes < (size_t)plan->lay.total)
+    return fail(ATTN_ERR_INVALID, "dev_buf holds %zu bytes; the plan needs %lld", bytes,
+                (long long)plan->lay.total);
+  if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dev_buf, plan->blob.data(), (size_t)plan->lay.total,
+                                hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host blob may be freed after return
+  if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "plan upload failed: %s", hipGetErrorString(e));
+  plan->dev_blob = dev_buf;
+  plan->dev_bytes = bytes;
+  return ATTN_OK;
+}
+
+extern "C" attn_status attn_fwd(const attn_plan *p, const void *q, const void *k, const void *v,
+                                void *o, float *lse, attn_stream_t stream) {
+  clear_error();
+  attn_status s;
+  if ((s = check_plan(p)) != ATTN_OK) return s;
+  if ((s = check_tensor(q, "q", 16)) != ATTN_OK) return s;
+  if ((s = check_tensor(k, "k", 16)) != ATTN_OK) return s;
+  if ((s = check_tensor(v, "v", 16)) != ATTN_OK) return s;
+  if ((s = check_tensor(o, "o", 16)) != ATTN_OK) return s;
+  if ((s = check_tensor(lse, "lse", 4)) != ATTN_OK) return s;
+  if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
+  FwdArgs a{};
+  a.q = static_cast<const bf16 *>(q);
+  a.k = static_cast<const bf16 *>(k);
+  a.v = static_cast<const bf16 *>(v);
+  a.o = static_cast<bf16 *>(o);
+  a.lse = lse;
+  a.S = (int)p->shape.S;
+  a.Hq = (int)p->shape.Hq;
+  a.Hkv = (int)p->shape.Hkv;
+  a.G = p->G;
+  a.sl2 = p->scale * kLog2e;
+  a.items = sect<int4>(p, p->lay.fwd_items);
+  a.list = sect<uint32_t>(p, p->lay.fwd_list);
+  a.m = mask_args(p);
+  (void)hipGetLastError();
+  const hipError_t e = launch_fwd(a, (int)p->shape.d, p->HG, (int)p->lay.n_fwd_items,
+                                  (int)p->shape.B, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+namespace {
+
+// Fill the backward argument block; tensors the stage does not use may be
+// NULL (checked by the caller).
+BwdArgs bwd_args(const attn_plan *p, const void *q, const void *k, const void *v,
+                 const void *o, const float *lse, const void *dout, void *dq, void *dk,
+                 void *dv, const void *ws) {
+  BwdArgs a{};
+  a.q = static_cast<const bf16 *>(q);
+  a.k = static_cast<const bf16 *>(k);
+  a.v = static_cast<const bf16 *>(v);
+  a.o = static_cast<const bf16 *>(o);
+  a.dout = static_cast<const bf16 *>(dout);
+  a.lse = lse;
+  a.dws = static_cast<float *>(const_cast<void *>(ws));
+  a.dq = static_cast<bf16 *>(dq);
+  a.dk = static_cast<bf16 *>(dk);
+  a.dv = static_cast<bf16 *>(dv);
+  a.S = (int)p->shape.S;
+  a.Hq = (int)p->shape.Hq;
+  a.Hkv = (int)p->shape.Hkv;
+  a.G = p->G;
+  a.scale = p->scale;
+  a.sl2 = p->scale * kLog2e;
+  a.fitems = sect<int4>(p, p->lay.fwd_items);
+  a.flist = sect<uint32_t>(p, p->lay.fwd_list);
+  a.bitems = sect<int4>(p, p->lay.bwd_items);
+  a.blist = sect<uint32_t>(p, p->lay.bwd_list);
+  a.n_fitems = (int)p->lay.n_fwd_items;
+  a.n_bitems = (int)p->lay.n_bwd_items;
+  a.m = mask_args(p);
+  return a;
+}
+
+attn_status check_ws(const attn_plan *p, const void *ws, size_t ws_bytes) {
+  attn_status s = check_tensor(ws, "ws", 256);
+  if (s != ATTN_OK) return s;
+  if (ws_bytes < attn_bwd_workspace_bytes(p))
+    return fail(ATTN_ERR_INVALID, "workspace holds %zu bytes; %zu needed", ws_bytes,
+                attn_bwd_workspace_bytes(p));
+  return ATTN_OK;
+}
+
+#define LCM_CHECK(expr)              \
+  do {                               \
+    attn_status s_ = (expr);         \
+    if (s_ != ATTN_OK) return s_;    \
+  } while (0)
+
+attn_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" attn_status attn_bwd_preprocess(const attn_plan *p, const void *o, const void *dout,
+                                           void *ws, size_t ws_bytes, attn_stream_t stream) {
+  clear_error();
+  LCM_CHECK(check_plan(p));
+  LCM_CHECK(check_tensor(o, "o", 16));
+  LCM_CHECK(check_tensor(dout, "dout", 16));
+  LCM_CHECK(check_ws(p, ws, ws_bytes));
+  if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
+  const BwdArgs a = bwd_args(p, nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr,
+                             nullptr, ws);
+  (void)hipGetLastError();
+  return launched(launch_bwd_pre(a, (int)p->shape.d, (int)p->shape.B,
+                                 reinterpret_cast<hipStream_t>(stream)), "backward preprocess");
+}
+
+extern "C" attn_status attn_bwd_dkdv(const attn_plan *p, const void *q, const void *k,
+                                     const void *v, const float *lse, const void *dout,
+                                     void *dk, void *dv, const void *ws, size_t ws_bytes,
+                                     attn_stream_t stream) {
+  clear_error();
+  LCM_CHECK(check_plan(p));
+  LCM_CHECK(check_tensor(q, "q", 16));
+  LCM_CHECK(check_tensor(k, "k", 16));
+  LCM_CHECK(check_tensor(v, "v", 16));
+  LCM_CHECK(check_tensor(lse, "lse", 4));
+  LCM_CHECK(check_tensor(dout, "dout", 16));
+  LCM_CHECK(check_tensor(dk, "dk", 16));
+  LCM_CHECK(check_tensor(dv, "dv", 16));
+  LCM_CHECK(check_ws(p, ws, ws_bytes));
+  if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
+  const BwdArgs a = bwd_args(p, q, k, v, nullptr, lse, dout, nullptr, dk, dv, ws);
+  (void)hipGetLastError();
+  return launched(launch_dkdv(a, (int)p->shape.d, (int)p->shape.B,
+                              reinterpret_cast<hipStream_t>(stream)), "dK/dV");
+}
+
+extern "C" attn_status attn_bwd_dq(const attn_plan *p, const void *q, const void *k,
+                                   const void *v, const float *lse, const void *dout, void *dq,
+                                   const void *ws, size_t ws_bytes, attn_stream_t stream) {
+  clear_error();
+  LCM_CHECK(check_plan(p));
+  LCM_CHECK(check_tensor(q, "q", 16));
+  LCM_CHECK(check_tensor(k, "k", 16));
+  LCM_CHECK(check_tensor(v, "v", 16));
+  LCM_CHECK(check_tensor(lse, "lse", 4));
+  LCM_CHECK(check_tensor(dout, "dout", 16));
+  LCM_CHECK(check_tensor(dq, "dq", 16));
+  LCM_CHECK(check_ws(p, ws, ws_bytes));
+  if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
+  const BwdArgs a = bwd_args(p, q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, ws);
+  (void)hipGetLastError();
+  return launched(launch_dq(a, (int)p->shape.d, p->HG, (int)p->shape.B,
+                            reinterpret_cast<hipStream_t>(stream)), "dQ");
+}
+
+extern "C" attn_status attn_bwd(const attn_plan *p, const void *q, const void *k, const void *v,
+                                const void *o, const float *lse, const void *dout, void *dq,
+                                void *dk, void *dv, void *ws, size_t ws_bytes,
+                                attn_stream_t stream) {
+  clear_error();
+  LCM_CHECK(check_plan(p));
+  LCM_CHECK(check_tensor(q, "q", 16));
+  LCM_CHECK(check_tensor(k, "k", 16));
+  LCM_CHECK(check_tensor(v, "v", 16));
+  LCM_CHECK(check_tensor(o, "o", 16));
+  LCM_CHECK(check_tensor(lse, "lse", 4));
+  LCM_CHECK(check_tensor(dout, "dout", 16));
+  LCM_CHECK(check_tensor(dq, "dq", 16));
+  LCM_CHECK(check_tensor(dk, "dk", 16));
+  LCM_CHECK(check_tensor(dv, "dv", 16));
+  LCM_CHECK(check_ws(p, ws, ws_bytes));
+  if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
+  const BwdArgs a = bwd_args(p, q, k, v, o, lse, dout, dq, dk, dv, ws);
+  const int d = (int)p->shape.d, B = (int)p->shape.B;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  LCM_CHECK(launched(launch_bwd_pre(a, d, B, st), "backward preprocess"));
+  LCM_CHECK(launched(launch_dkdv(a, d, B, st), "dK/dV"));
+  return launched(launch_dq(a, d, p->HG, B, st), "dQ");
+}

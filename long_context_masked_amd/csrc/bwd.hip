@@ -1,0 +1,388 @@
+// Backward kernels: D = rowsum(dO * O), a KV-split pass for dK/dV and a
+// Q-split pass for dQ.
+//
+// Method ("FlashAttention vs. RingAttention", dtcms, FlashAttention-2 "core
+// optimisations"): the backward keeps one merged softmax statistic (LSE) and
+// recomputes P from it; it is parallelised over both rows and columns
+// because of the dependency dQ_i = sum_j dS_ij K_j.  Here the column split
+// (one workgroup per K-tile and KV head) owns dK and dV in registers and the
+// row split (one workgroup per Q-tile and head group) owns dQ in registers,
+// so neither needs atomics.
+//
+// With c = scale * log2(e) and lse2 = LSE * log2(e):
+//   P  = exp2(c * Q K^T - lse2)          (masked entries 0)
+//   dP = dO V^T,  dS = P * (dP - D)
+//   dV = P^T dO,  dK = scale * dS^T Q,  dQ = scale * dS K
+#include "kernels.hpp"
+
+namespace lcm {
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// D[b, h, s] = sum_d dO[b, s, h, d] * O[b, s, h, d] (bf16 inputs, fp32 sum).
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const bf16 *dout,
+                                                           float *dws, int S, int Hq,
+                                                           int64_t nrows) {
+  constexpr int CPR = D / 8;
+  constexpr int RPB = 256 / CPR;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
+  const int c = threadIdx.x % CPR;
+  float acc = 0.f;
+  if (r < nrows) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(o + r * D + c * 8);
+    const uint4 y = *reinterpret_cast<const uint4 *>(dout + r * D + c * 8);
+    acc = bf_lo(x.x) * bf_lo(y.x) + bf_hi(x.x) * bf_hi(y.x) + bf_lo(x.y) * bf_lo(y.y) +
+          bf_hi(x.y) * bf_hi(y.y) + bf_lo(x.z) * bf_lo(y.z) + bf_hi(x.z) * bf_hi(y.z) +
+          bf_lo(x.w) * bf_lo(y.w) + bf_hi(x.w) * bf_hi(y.w);
+  }
+#pragma unroll
+  for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (r < nrows && c == 0) {
+    const int64_t bs = r / Hq;
+    const int h = (int)(r % Hq);
+    const int64_t bb = bs / S;
+    const int s = (int)(bs % S);
+    dws[(bb * Hq + h) * S + s] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: one workgroup per (K-tile of 128 keys, KV head).  Wave w owns keys
+// 32w .. 32w+31 of the tile (lane l: key 32w + l % 32), keeps K and V of
+// those keys as MFMA operands in registers and accumulates dK^T, dV^T.  For
+// each listed Q-tile of 64 rows and each query head of the group, Q, dO,
+// their transposes, LSE and D are staged in LDS (double-buffered).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  using T = Tile64<D>;
+  constexpr int NP = T::NP, TP = T::TP;
+  __shared__ __attribute__((aligned(16))) bf16 sQ[2][64 * NP];
+  __shared__ __attribute__((aligned(16))) bf16 sQT[2][D * TP];
+  __shared__ __attribute__((aligned(16))) bf16 sO[2][64 * NP];
+  __shared__ __attribute__((aligned(16))) bf16 sOT[2][D * TP];
+  __shared__ __attribute__((aligned(16))) float sL[2][64];
+  __shared__ __attribute__((aligned(16))) float sDv[2][64];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int ln = lane & 31, hh = lane >> 5;
+  const int4 item = a.bitems[blockIdx.x];
+  const int b = blockIdx.y;
+  const int S = a.S, G = a.G;
+  const int kvh = item.y;
+  const int key = item.x * 128 + wave * 32 + ln;
+  const bool key_ok = key < S;
+  const int64_t ldq = (int64_t)a.Hq * D, ldk = (int64_t)a.Hkv * D;
+
+  bf16x8 kv[KS], vv[KS];
+  {
+    const int64_t off = ((int64_t)b * S + (key_ok ? key : 0)) * ldk + (int64_t)kvh * D + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kv[ks] = *reinterpret_cast<const bf16x8 *>(a.k + off + ks * 16);
+      vv[ks] = *reinterpret_cast<const bf16x8 *>(a.v + off + ks * 16);
+      if (!key_ok) { kv[ks] = (bf16x8){}; vv[ks] = (bf16x8){}; }
+    }
+  }
+  const int4 cb = key_ok ? a.m.colb[key] : make_int4(0, S, 0, 0);
+  const int kblk = (a.m.bm_heads && key_ok) ? a.m.kblk[key] : 0;
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) { dk[i] = (f32x16){}; dv[i] = (f32x16){}; }
+  const float sl2 = a.sl2;
+
+  const uint32_t *list = a.blist + item.z;
+  const int nst = item.w * G;
+  T tq, tdo;
+  float lval = 0.f;
+
+  auto load_stage = [&](int st) {
+    const int e = st / G, g = st - e * G;
+    const int qt = (int)(list[e] & 0x7fffffffu);
+    const int h = kvh * G + g;
+    tq.load(a.q + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
+    tdo.load(a.dout + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
+    const int rr = qt * 64 + (tid & 63);
+    lval = 0.f;
+    if (tid < 128 && rr < S) {
+      const int64_t idx = ((int64_t)b * a.Hq + h) * S + rr;
+      lval = tid < 64 ? a.lse[idx] * kLog2e : a.dws[idx];
+    }
+  };
+  auto store_stage = [&](int buf) {
+    tq.store_nat(sQ[buf]);
+    tq.store_trans(sQT[buf]);
+    tdo.store_nat(sO[buf]);
+    tdo.store_trans(sOT[buf]);
+    if (tid < 64) sL[buf][tid] = lval;
+    else if (tid < 128) sDv[buf][tid - 64] = lval;
+  };
+
+  if (nst > 0) {
+    load_stage(0);
+    store_stage(0);
+  }
+  __syncthreads();
+
+  for (int st = 0; st < nst; ++st) {
+    const int e = st / G, g = st - e * G;
+    const uint32_t ent = list[e];
+    const int qt = (int)(ent & 0x7fffffffu);
+    const bool partial = (ent >> 31) != 0;
+    const int h = kvh * G + g;
+    const int buf = st & 1;
+    if (st + 1 < nst) load_stage(st + 1);
+
+    uint32_t mw[2] = {0xffffffffu, 0xffffffffu};
+    bool active = true;
+    if (partial) {
+      const int hm = bitmap_head(a.m.bm_heads, h, a.Hq, G);
+      const uint64_t mk = key_ok ? col_mask(a.m, cb, kblk, hm, qt * 64, S) : 0ull;
+      active = __ballot(mk != 0ull) != 0ull;
+      const uint64_t sh = mk >> (4 * hh);
+      mw[0] = (uint32_t)sh;
+      mw[1] = (uint32_t)(sh >> 32);
+    }
+    if (active) {
+      const bf16 *q_s = sQ[buf], *qt_s = sQT[buf], *o_s = sO[buf], *ot_s = sOT[buf];
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = (f32x16){};
+        dp[qb] = (f32x16){};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(q_s + (qb * 32 + ln) * NP + ks * 16 + hh * 8);
+          s[qb] = mfma32(aq, kv[ks], s[qb]);
+          const bf16x8 ao = *reinterpret_cast<const bf16x8 *>(o_s + (qb * 32 + ln) * NP + ks * 16 + hh * 8);
+          dp[qb] = mfma32(ao, vv[ks], dp[qb]);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&sL[buf][qb * 32 + 8 * c + 4 * hh]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sDv[buf][qb * 32 + 8 * c + 4 * hh]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * c + j;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], sl2, -l4[j]));
+            if (partial) p = keep_or(mw[qb], 8 * c + j, p, 0.f);
+            s[qb][r] = p;
+            dp[qb][r] = p * (dp[qb][r] - d4[j]);
+          }
+        }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 pb = c_to_b(s, t);
+        const bf16x8 dsb = c_to_b(dp, t);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 aot = *reinterpret_cast<const bf16x8 *>(ot_s + (db * 32 + ln) * TP + t * 16 + hh * 8);
+          dv[db] = mfma32(aot, pb, dv[db]);
+          const bf16x8 aqt = *reinterpret_cast<const bf16x8 *>(qt_s + (db * 32 + ln) * TP + t * 16 + hh * 8);
+          dk[db] = mfma32(aqt, dsb, dk[db]);
+        }
+      }
+    }
+
+    if (st + 1 < nst) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (key_ok) {
+    const int64_t off = ((int64_t)b * S + key) * ldk + (int64_t)kvh * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d0 = db * 32 + 8 * c + 4 * hh;
+        bf16x2 k0 = __builtin_convertvector((f32x2){dk[db][4 * c] * sc, dk[db][4 * c + 1] * sc}, bf16x2);
+        bf16x2 k1 = __builtin_convertvector((f32x2){dk[db][4 * c + 2] * sc, dk[db][4 * c + 3] * sc}, bf16x2);
+        *reinterpret_cast<bf16x4 *>(a.dk + off + d0) = __builtin_shufflevector(k0, k1, 0, 1, 2, 3);
+        bf16x2 v0 = __builtin_convertvector((f32x2){dv[db][4 * c], dv[db][4 * c + 1]}, bf16x2);
+        bf16x2 v1 = __builtin_convertvector((f32x2){dv[db][4 * c + 2], dv[db][4 * c + 3]}, bf16x2);
+        *reinterpret_cast<bf16x4 *>(a.dv + off + d0) = __builtin_shufflevector(v0, v1, 0, 1, 2, 3);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per forward work item (Q-tile, head group); same lane
+// ownership as the forward.  K (natural and transposed) and V (natural) tiles
+// are staged in LDS, double-buffered.  Per K-tile:
+//   S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - D),  dQ^T += K^T dS^T
+// ---------------------------------------------------------------------------
+template <int D, int HG>
+__global__ __launch_bounds__(256, 1) void attn_dq_kernel(BwdArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  using T = Tile64<D>;
+  constexpr int NP = T::NP, TP = T::TP;
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][64 * NP];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][64 * NP];
+  __shared__ __attribute__((aligned(16))) bf16 sKT[2][D * TP];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ln = lane & 31, hh = lane >> 5;
+  const int4 item = a.fitems[blockIdx.x];
+  const int b = blockIdx.y;
+  const int S = a.S;
+  const int h = item.y + wave % HG;
+  const int row = item.x * (128 / HG) + (wave / HG) * 32 + ln;
+  const int kvh = h / a.G;
+  const int64_t ldq = (int64_t)a.Hq * D, ldk = (int64_t)a.Hkv * D;
+  const bf16 *kbase = a.k + (int64_t)b * S * ldk + (int64_t)kvh * D;
+  const bf16 *vbase = a.v + (int64_t)b * S * ldk + (int64_t)kvh * D;
+  const bool row_ok = row < S;
+
+  bf16x8 qv[KS], dov[KS];
+  {
+    const int64_t off = ((int64_t)b * S + (row_ok ? row : 0)) * ldq + (int64_t)h * D + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qv[ks] = *reinterpret_cast<const bf16x8 *>(a.q + off + ks * 16);
+      dov[ks] = *reinterpret_cast<const bf16x8 *>(a.dout + off + ks * 16);
+      if (!row_ok) { qv[ks] = (bf16x8){}; dov[ks] = (bf16x8){}; }
+    }
+  }
+  float lse2 = 0.f, Dr = 0.f;
+  if (row_ok) {
+    const int64_t idx = ((int64_t)b * a.Hq + h) * S + row;
+    lse2 = a.lse[idx] * kLog2e;
+    Dr = a.dws[idx];
+  }
+  const int4 rb = row_ok ? a.m.rowb[row] : make_int4(0, 0, 0, 0);
+  const int hm = bitmap_head(a.m.bm_heads, h, a.Hq, a.G);
+  const int qb = (a.m.bm_heads && row_ok) ? a.m.qblk[row] : 0;
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dq[i] = (f32x16){};
+  const float sl2 = a.sl2;
+
+  const uint32_t *list = a.flist + item.z;
+  const int n = item.w;
+  T tk, tv;
+  if (n > 0) {
+    const int kt = (int)(list[0] & 0x7fffffffu);
+    tk.load(kbase, ldk, kt * 64, S);
+    tv.load(vbase, ldk, kt * 64, S);
+    tk.store_nat(sK[0]);
+    tk.store_trans(sKT[0]);
+    tv.store_nat(sV[0]);
+  }
+  __syncthreads();
+
+  for (int e = 0; e < n; ++e) {
+    const uint32_t ent = list[e];
+    const int kt = (int)(ent & 0x7fffffffu);
+    const bool partial = (ent >> 31) != 0;
+    const int buf = e & 1;
+    if (e + 1 < n) {
+      const int nkt = (int)(list[e + 1] & 0x7fffffffu);
+      tk.load(kbase, ldk, nkt * 64, S);
+      tv.load(vbase, ldk, nkt * 64, S);
+    }
+    uint32_t mw[2] = {0xffffffffu, 0xffffffffu};
+    bool active = true;
+    if (partial) {
+      const uint64_t mk = row_ok ? row_mask(a.m, rb, qb, hm, kt * 64, S) : 0ull;
+      active = __ballot(mk != 0ull) != 0ull;
+      const uint64_t sh = mk >> (4 * hh);
+      mw[0] = (uint32_t)sh;
+      mw[1] = (uint32_t)(sh >> 32);
+    }
+    if (active) {
+      const bf16 *k_s = sK[buf], *v_s = sV[buf], *kt_s = sKT[buf];
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = (f32x16){};
+        dp[kb] = (f32x16){};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(k_s + (kb * 32 + ln) * NP + ks * 16 + hh * 8);
+          s[kb] = mfma32(ak, qv[ks], s[kb]);
+          const bf16x8 av = *reinterpret_cast<const bf16x8 *>(v_s + (kb * 32 + ln) * NP + ks * 16 + hh * 8);
+          dp[kb] = mfma32(av, dov[ks], dp[kb]);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -lse2));
+          if (partial) p = keep_or(mw[kb], 8 * (r >> 2) + (r & 3), p, 0.f);
+          dp[kb][r] = p * (dp[kb][r] - Dr);
+        }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 dsb = c_to_b(dp, t);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 akt = *reinterpret_cast<const bf16x8 *>(kt_s + (db * 32 + ln) * TP + t * 16 + hh * 8);
+          dq[db] = mfma32(akt, dsb, dq[db]);
+        }
+      }
+    }
+    if (e + 1 < n) {
+      tk.store_nat(sK[buf ^ 1]);
+      tk.store_trans(sKT[buf ^ 1]);
+      tv.store_nat(sV[buf ^ 1]);
+    }
+    __syncthreads();
+  }
+
+  if (row_ok) {
+    bf16 *qrow = a.dq + ((int64_t)b * S + row) * ldq + (int64_t)h * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d0 = db * 32 + 8 * c + 4 * hh;
+        bf16x2 p0 = __builtin_convertvector((f32x2){dq[db][4 * c] * sc, dq[db][4 * c + 1] * sc}, bf16x2);
+        bf16x2 p1 = __builtin_convertvector((f32x2){dq[db][4 * c + 2] * sc, dq[db][4 * c + 3] * sc}, bf16x2);
+        *reinterpret_cast<bf16x4 *>(qrow + d0) = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+      }
+  }
+}
+
+hipError_t launch_bwd_pre(const BwdArgs &a, int d, int B, hipStream_t st) {
+  const int64_t nrows = (int64_t)B * a.S * a.Hq;
+  const int rpb = 256 / (d / 8);
+  const dim3 grid((unsigned)((nrows + rpb - 1) / rpb)), block(256);
+  if (d == 128) hipLaunchKernelGGL((attn_bwd_pre_kernel<128>), grid, block, 0, st, a.o, a.dout, a.dws, a.S, a.Hq, nrows);
+  else if (d == 64) hipLaunchKernelGGL((attn_bwd_pre_kernel<64>), grid, block, 0, st, a.o, a.dout, a.dws, a.S, a.Hq, nrows);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_dkdv(const BwdArgs &a, int d, int B, hipStream_t st) {
+  const dim3 grid((unsigned)a.n_bitems, (unsigned)B), block(256);
+  if (d == 128) hipLaunchKernelGGL((attn_dkdv_kernel<128>), grid, block, 0, st, a);
+  else if (d == 64) hipLaunchKernelGGL((attn_dkdv_kernel<64>), grid, block, 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_dq(const BwdArgs &a, int d, int HG, int B, hipStream_t st) {
+  const dim3 grid((unsigned)a.n_fitems, (unsigned)B), block(256);
+  if (d == 128 && HG == 2) hipLaunchKernelGGL((attn_dq_kernel<128, 2>), grid, block, 0, st, a);
+  else if (d == 128 && HG == 1) hipLaunchKernelGGL((attn_dq_kernel<128, 1>), grid, block, 0, st, a);
+  else if (d == 64 && HG == 2) hipLaunchKernelGGL((attn_dq_kernel<64, 2>), grid, block, 0, st, a);
+  else if (d == 64 && HG == 1) hipLaunchKernelGGL((attn_dq_kernel<64, 1>), grid, block, 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace lcm

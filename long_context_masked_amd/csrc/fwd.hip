@@ -1,0 +1,187 @@
+// Forward kernel: O = softmax(mask(Q K^T * scale)) V and LSE, Q-split.
+//
+// Method ("FlashAttention vs. RingAttention", dtcms): tiling with online
+// softmax and fused masking (FlashAttention-1, "core optimisations"); the
+// output is normalised once at the end, one merged statistic (LSE) is kept,
+// and the work is split along Q rows (FlashAttention-2, "core
+// optimisations").
+//
+// One workgroup = 4 waves = one work item: (Q-tile, group of HG query heads
+// that share a KV head).  Wave w owns 32 query rows of head h0 + w % HG; lane
+// l owns row 32*(w / HG) + l % 32, and the two lane halves split each K-tile's
+// 64 keys.  K (natural) and V (transposed) tiles of 64 keys are staged in LDS,
+// double-buffered, and shared by all heads of the item.  Per K-tile:
+//   S^T = K Q^T                  (MFMA, K from LDS, Q^T in registers)
+//   mask (partial tiles only)    (per-lane 64-bit allowed-key word)
+//   m, l update                  (running max kept stale within the slack)
+//   O^T += V^T P^T               (MFMA, V^T from LDS, P^T from registers)
+#include "kernels.hpp"
+
+namespace lcm {
+
+template <int D, int HG>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
+  constexpr int KS = D / 16;  // k-steps of QK^T
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  using T = Tile64<D>;
+  constexpr int NP = T::NP, TP = T::TP;
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][64 * NP];
+  __shared__ __attribute__((aligned(16))) bf16 sVT[2][D * TP];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ln = lane & 31, hh = lane >> 5;
+  const int4 item = a.items[blockIdx.x];
+  const int b = blockIdx.y;
+  const int S = a.S;
+  const int h = item.y + wave % HG;
+  const int row = item.x * (128 / HG) + (wave / HG) * 32 + ln;
+  const int kvh = h / a.G;
+  const int64_t ldq = (int64_t)a.Hq * D, ldk = (int64_t)a.Hkv * D;
+  const bf16 *kbase = a.k + (int64_t)b * S * ldk + (int64_t)kvh * D;
+  const bf16 *vbase = a.v + (int64_t)b * S * ldk + (int64_t)kvh * D;
+  const bool row_ok = row < S;
+
+  bf16x8 qv[KS];
+  {
+    const bf16 *qrow = a.q + ((int64_t)b * S + (row_ok ? row : 0)) * ldq + (int64_t)h * D + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qv[ks] = *reinterpret_cast<const bf16x8 *>(qrow + ks * 16);
+      if (!row_ok) qv[ks] = (bf16x8){};
+    }
+  }
+  const int4 rb = row_ok ? a.m.rowb[row] : make_int4(0, 0, 0, 0);
+  const int hm = bitmap_head(a.m.bm_heads, h, a.Hq, a.G);
+  const int qb = (a.m.bm_heads && row_ok) ? a.m.qblk[row] : 0;
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = (f32x16){};
+  float m_run = kMinit, l_run = 0.f;
+  const float sl2 = a.sl2;
+
+  const uint32_t *list = a.list + item.z;
+  const int n = item.w;
+  T tk, tv;
+  if (n > 0) {
+    const int kt = (int)(list[0] & 0x7fffffffu);
+    tk.load(kbase, ldk, kt * 64, S);
+    tv.load(vbase, ldk, kt * 64, S);
+    tk.store_nat(sK[0]);
+    tv.store_trans(sVT[0]);
+  }
+  __syncthreads();
+
+  for (int e = 0; e < n; ++e) {
+    const uint32_t ent = list[e];
+    const int kt = (int)(ent & 0x7fffffffu);
+    const bool partial = (ent >> 31) != 0;
+    const int buf = e & 1;
+    if (e + 1 < n) {
+      const int nkt = (int)(list[e + 1] & 0x7fffffffu);
+      tk.load(kbase, ldk, nkt * 64, S);
+      tv.load(vbase, ldk, nkt * 64, S);
+    }
+
+    uint32_t mlo = 0xffffffffu, mhi = 0xffffffffu;
+    bool active = true;
+    if (partial) {
+      const uint64_t mk = row_ok ? row_mask(a.m, rb, qb, hm, kt * 64, S) : 0ull;
+      active = __ballot(mk != 0ull) != 0ull;
+      const uint64_t sh = mk >> (4 * hh);
+      mlo = (uint32_t)sh;
+      mhi = (uint32_t)(sh >> 32);
+    }
+    if (active) {
+      const bf16 *k_s = sK[buf];
+      const bf16 *vt_s = sVT[buf];
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = (f32x16){};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8 *>(k_s + (kb * 32 + ln) * NP + ks * 16 + hh * 8);
+          s[kb] = mfma32(av, qv[ks], s[kb]);
+        }
+      }
+      if (partial) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int bit = 8 * (r >> 2) + (r & 3);
+          s[0][r] = keep_or(mlo, bit, s[0][r], kNegInf);
+          s[1][r] = keep_or(mhi, bit, s[1][r], kNegInf);
+        }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * sl2);
+      if (__ballot(m_new > m_run + kRescaleSlack) != 0ull) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      }
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -m_run));
+          s[kb][r] = p;
+          ls += p;
+        }
+      l_run += ls;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 pb = c_to_b(s, t);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8 *>(vt_s + (db * 32 + ln) * TP + t * 16 + hh * 8);
+          o[db] = mfma32(av, pb, o[db]);
+        }
+      }
+    }
+
+    if (e + 1 < n) {
+      tk.store_nat(sK[buf ^ 1]);
+      tv.store_trans(sVT[buf ^ 1]);
+    }
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (row_ok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16 *orow = a.o + ((int64_t)b * S + row) * ldq + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d0 = db * 32 + 8 * c + 4 * hh;
+        bf16x2 p0 = __builtin_convertvector((f32x2){o[db][4 * c] * inv, o[db][4 * c + 1] * inv}, bf16x2);
+        bf16x2 p1 = __builtin_convertvector((f32x2){o[db][4 * c + 2] * inv, o[db][4 * c + 3] * inv}, bf16x2);
+        *reinterpret_cast<bf16x4 *>(orow + d0) = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+      }
+    if (hh == 0)
+      a.lse[((int64_t)b * a.Hq + h) * S + row] =
+          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+hipError_t launch_fwd(const FwdArgs &a, int d, int HG, int n_items, int B, hipStream_t st) {
+  const dim3 grid((unsigned)n_items, (unsigned)B), block(256);
+  if (d == 128 && HG == 2) hipLaunchKernelGGL((attn_fwd_kernel<128, 2>), grid, block, 0, st, a);
+  else if (d == 128 && HG == 1) hipLaunchKernelGGL((attn_fwd_kernel<128, 1>), grid, block, 0, st, a);
+  else if (d == 64 && HG == 2) hipLaunchKernelGGL((attn_fwd_kernel<64, 2>), grid, block, 0, st, a);
+  else if (d == 64 && HG == 1) hipLaunchKernelGGL((attn_fwd_kernel<64, 1>), grid, block, 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace lcm

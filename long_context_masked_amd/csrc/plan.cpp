@@ -1,0 +1,591 @@
+// Mask compiler: descriptor -> row/column bounds -> tile classes -> ordered
+// work lists -> device blob.  Host only; makes no HIP call.
+//
+// Method sources (cited by page and section):
+//  * "Long-Context Attention Benchmark" review (xllm-io), section 3 "mask
+//    taxonomy" (the families) and components table (the mask generator and
+//    kernel adapter that give every kernel one input representation).
+//  * "FlashAttention vs. RingAttention" (dtcms), FlashAttention-2 "core
+//    optimisations": Q-split forward, two-axis backward, and work
+//    partitioning for load balance across thread blocks.
+//
+// Pipeline:
+//  1. validate the shape and the descriptor;
+//  2. express the base family as masked row intervals per key column
+//     (col bounds, two per column) in closed form;
+//  3. derive the allowed key runs of every query row (row bounds, at most two
+//     per row) by a sweep over rows;
+//  4. classify each 64x64 micro tile EMPTY / FULL / PARTIAL from the row
+//     bounds (difference arrays), then AND in the block bitmap per mask head;
+//  5. aggregate micro tiles into kernel tiles and emit per-Q-tile (forward,
+//     dQ) and per-K-tile (dK/dV) lists of non-empty tiles;
+//  6. order work items longest first and lay everything out in one blob.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <set>
+
+#include "plan.hpp"
+
+namespace lcm {
+
+static thread_local std::string g_err;
+
+attn_status fail(attn_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+void clear_error() { g_err.clear(); }
+
+namespace {
+
+enum : uint8_t { kEmpty = 0, kPartial = 1, kFull = 2 };
+
+struct Run { int32_t a0, b0, a1, b1; };
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+int32_t clamp_s(int64_t x, int64_t S) {
+  return (int32_t)std::max<int64_t>(0, std::min<int64_t>(x, S));
+}
+
+attn_status check_offsets(const int32_t *off, int64_t n, int64_t S, const char *what) {
+  if (!off) return fail(ATTN_ERR_INVALID, "%s is NULL", what);
+  if (off[0] != 0) return fail(ATTN_ERR_INVALID, "%s[0] must be 0", what);
+  for (int64_t i = 0; i < n; ++i)
+    if (off[i + 1] <= off[i])
+      return fail(ATTN_ERR_INVALID, "%s must be strictly increasing (at %lld)", what, (long long)i);
+  if (off[n] != S)
+    return fail(ATTN_ERR_INVALID, "%s must end at S=%lld (got %d)", what, (long long)S, off[n]);
+  return ATTN_OK;
+}
+
+// Step 2: masked row intervals {lts, lte, uts, ute} for every key column.
+attn_status build_colb(const attn_shape &sh, const attn_mask_desc &d, std::vector<int32_t> &cb) {
+  const int64_t S = sh.S;
+  cb.assign((size_t)S * 4, 0);
+  auto put = [&](int64_t j, int64_t lts, int64_t lte, int64_t uts, int64_t ute) {
+    int32_t *c = &cb[(size_t)j * 4];
+    c[0] = clamp_s(lts, S); c[1] = clamp_s(lte, S);
+    c[2] = clamp_s(uts, S); c[3] = clamp_s(ute, S);
+  };
+  switch (d.kind) {
+    case ATTN_MASK_FULL:
+      return ATTN_OK;
+    case ATTN_MASK_CAUSAL:
+      for (int64_t j = 0; j < S; ++j) put(j, 0, 0, 0, j);
+      return ATTN_OK;
+    case ATTN_MASK_SLIDING: {
+      if (d.causal != 0 && d.causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1");
+      if (d.window_left < 1) return fail(ATTN_ERR_INVALID, "window_left must be >= 1");
+      if (!d.causal && d.window_right < 1)
+        return fail(ATTN_ERR_INVALID, "window_right must be >= 1 when causal = 0");
+      const int64_t wl = d.window_left, wr = d.window_right;
+      for (int64_t j = 0; j < S; ++j) {
+        // rows i >= j + wl are outside the window below the diagonal;
+        // rows above the diagonal: i < j when causal, i <= j - wr otherwise.
+        const int64_t up_end = d.causal ? j : std::max<int64_t>(0, j - wr + 1);
+        put(j, j + wl, S, 0, up_end);
+      }
+      return ATTN_OK;
+    }
+    case ATTN_MASK_DOCUMENT:
+    case ATTN_MASK_PREFIX_LM: {
+      if (d.num_docs < 1) return fail(ATTN_ERR_INVALID, "num_docs must be >= 1");
+      attn_status st = check_offsets(d.cu_seqlens, d.num_docs, S, "cu_seqlens");
+      if (st != ATTN_OK) return st;
+      const bool prefix = d.kind == ATTN_MASK_PREFIX_LM;
+      if (!prefix && d.causal != 0 && d.causal != 1)
+        return fail(ATTN_ERR_INVALID, "causal must be 0 or 1");
+      if (prefix && !d.prefix_lens) return fail(ATTN_ERR_INVALID, "prefix_lens is NULL");
+      for (int k = 0; k < d.num_docs; ++k) {
+        const int64_t s = d.cu_seqlens[k], e = d.cu_seqlens[k + 1];
+        int64_t p = 0;
+        if (prefix) {
+          p = d.prefix_lens[k];
+          if (p < 0 || p > e - s)
+            return fail(ATTN_ERR_INVALID, "prefix_lens[%d]=%lld outside [0, %lld]", k,
+                        (long long)p, (long long)(e - s));
+        }
+        for (int64_t j = s; j < e; ++j) {
+          // other documents are masked: rows [0, s) and [e, S);
+          // inside the document, rows above the diagonal are masked unless
+          // the family keeps them (full document, or a prefix key).
+          int64_t up_end;
+          if (prefix) up_end = (j < s + p) ? s : j;
+          else up_end = d.causal ? j : s;
+          put(j, e, S, 0, up_end);
+        }
+      }
+      return ATTN_OK;
+    }
+    case ATTN_MASK_COLUMN_BOUNDS: {
+      if (!d.col_bounds) return fail(ATTN_ERR_INVALID, "col_bounds is NULL");
+      for (int64_t j = 0; j < S; ++j)
+        for (int t = 0; t < 4; ++t) {
+          const int32_t x = d.col_bounds[j * 4 + t];
+          if (x < 0 || x > S)
+            return fail(ATTN_ERR_INVALID, "col_bounds[%lld][%d]=%d outside [0, S]", (long long)j, t, x);
+          cb[(size_t)j * 4 + t] = x;
+        }
+      return ATTN_OK;
+    }
+    default:
+      return fail(ATTN_ERR_INVALID, "unknown mask kind %d", d.kind);
+  }
+}
+
+// Step 3: allowed key runs per row.  Sweep rows top to bottom keeping, per
+// column, how many masked intervals cover the current row, and the ordered
+// set of positions where "allowed" changes between neighbouring columns.
+attn_status rows_from_cols(int64_t S, const std::vector<int32_t> &cb, std::vector<Run> &rb,
+                           int64_t &nnz) {
+  std::vector<int64_t> start((size_t)S + 2, 0);
+  for (int64_t j = 0; j < S; ++j)
+    for (int t = 0; t < 2; ++t) {
+      const int32_t a = cb[j * 4 + 2 * t], b = cb[j * 4 + 2 * t + 1];
+      if (a >= b) continue;
+      start[a + 1]++;
+      if (b < S) start[b + 1]++;
+    }
+  for (int64_t i = 0; i <= S; ++i) start[i + 1] += start[i];
+  std::vector<int64_t> fillp(start.begin(), start.end() - 1);
+  std::vector<std::pair<int32_t, int8_t>> ev((size_t)start[S]);
+  for (int64_t j = 0; j < S; ++j)
+    for (int t = 0; t < 2; ++t) {
+      const int32_t a = cb[j * 4 + 2 * t], b = cb[j * 4 + 2 * t + 1];
+      if (a >= b) continue;
+      ev[fillp[a]++] = {(int32_t)j, +1};
+      if (b < S) ev[fillp[b]++] = {(int32_t)j, -1};
+    }
+  std::vector<int32_t> cover((size_t)S, 0);
+  std::set<int32_t> edges{0, (int32_t)S};
+  auto toggle = [&](int32_t p) {
+    auto it = edges.find(p);
+    if (it == edges.end()) edges.insert(p); else edges.erase(it);
+  };
+  rb.assign((size_t)S, Run{0, 0, 0, 0});
+  nnz = 0;
+  for (int64_t i = 0; i < S; ++i) {
+    for (int64_t e = start[i]; e < start[i + 1]; ++e) {
+      const int32_t j = ev[e].first;
+      const bool was = cover[j] == 0;
+      cover[j] += ev[e].second;
+      if (was != (cover[j] == 0)) { toggle(j); toggle(j + 1); }
+    }
+    if (edges.size() > 4)
+      return fail(ATTN_ERR_UNSUPPORTED,
+                  "row %lld has %zu runs of allowed keys; at most 2 are supported",
+                  (long long)i, edges.size() / 2);
+    auto it = edges.begin();
+    Run r{0, 0, 0, 0};
+    if (edges.size() >= 2) { r.a0 = *it++; r.b0 = *it++; }
+    if (edges.size() == 4) { r.a1 = *it++; r.b1 = *it++; }
+    rb[i] = r;
+    nnz += (r.b0 - r.a0) + (r.b1 - r.a1);
+  }
+  return ATTN_OK;
+}
+
+// Step 4a: micro-tile classes of the base mask from the row runs.
+void classify_base(int64_t S, const std::vector<Run> &rb, std::vector<uint8_t> &cls) {
+  const int64_t nM = (S + kMicro - 1) / kMicro;
+  cls.assign((size_t)(nM * nM), kEmpty);
+  std::vector<int32_t> full((size_t)nM + 1), touch((size_t)nM + 1);
+  for (int64_t I = 0; I < nM; ++I) {
+    std::fill(full.begin(), full.end(), 0);
+    std::fill(touch.begin(), touch.end(), 0);
+    const int64_t r0 = I * kMicro, r1 = std::min<int64_t>(S, r0 + kMicro);
+    for (int64_t i = r0; i < r1; ++i) {
+      const Run &r = rb[i];
+      const int32_t as[2] = {r.a0, r.a1}, bs[2] = {r.b0, r.b1};
+      for (int t = 0; t < 2; ++t) {
+        const int64_t a = as[t], b = bs[t];
+        if (a >= b) continue;
+        touch[a / kMicro]++;
+        touch[(b - 1) / kMicro + 1]--;
+        const int64_t jlo = (a + kMicro - 1) / kMicro;
+        const int64_t jhi = (b == S) ? nM - 1 : b / kMicro - 1;
+        if (jlo <= jhi) { full[jlo]++; full[jhi + 1]--; }
+      }
+    }
+    int32_t f = 0, tc = 0;
+    const int32_t R = (int32_t)(r1 - r0);
+    for (int64_t J = 0; J < nM; ++J) {
+      f += full[J]; tc += touch[J];
+      cls[I * nM + J] = tc == 0 ? kEmpty : (f == R ? kFull : kPartial);
+    }
+  }
+}
+
+struct Bitmap {
+  int heads = 0, nqb = 0, nkb = 0;
+  std::vector<uint8_t> bits;         // [heads][nqb][nkb], 0/1
+  std::vector<int32_t> qoffs, koffs; // [n+1]
+  std::vector<int32_t> qblk, kblk;   // block of each position [S]
+};
+
+// Step 4b: AND the bitmap of mask head hm into the base micro classes.
+void classify_bitmap(int64_t S, const std::vector<uint8_t> &base, const Bitmap &bm, int hm,
+                     std::vector<uint8_t> &cls) {
+  const int64_t nM = (S + kMicro - 1) / kMicro;
+  cls.resize(base.size());
+  const uint8_t *B = bm.bits.data() + (size_t)hm * bm.nqb * bm.nkb;
+  std::vector<int32_t> klo((size_t)nM), khi((size_t)nM);
+  for (int64_t J = 0; J < nM; ++J) {
+    klo[J] = bm.kblk[J * kMicro];
+    khi[J] = bm.kblk[std::min<int64_t>(S, J * kMicro + kMicro) - 1];
+  }
+  for (int64_t I = 0; I < nM; ++I) {
+    const int32_t qlo = bm.qblk[I * kMicro];
+    const int32_t qhi = bm.qblk[std::min<int64_t>(S, I * kMicro + kMicro) - 1];
+    for (int64_t J = 0; J < nM; ++J) {
+      const uint8_t b = base[I * nM + J];
+      if (b == kEmpty) { cls[I * nM + J] = kEmpty; continue; }
+      bool any = false, all = true;
+      for (int32_t qb = qlo; qb <= qhi; ++qb)
+        for (int32_t kb = klo[J]; kb <= khi[J]; ++kb) {
+          const bool on = B[(size_t)qb * bm.nkb + kb] != 0;
+          any |= on; all &= on;
+        }
+      cls[I * nM + J] = !any ? kEmpty : (all && b == kFull ? kFull : kPartial);
+    }
+  }
+}
+
+// Exact allowed-pair count of base AND bitmap head hm.
+int64_t nnz_with_bitmap(int64_t S, const std::vector<Run> &rb, const Bitmap &bm, int hm) {
+  const uint8_t *B = bm.bits.data() + (size_t)hm * bm.nqb * bm.nkb;
+  std::vector<int64_t> C((size_t)bm.nkb + 1);
+  int64_t tot = 0;
+  for (int32_t qb = 0; qb < bm.nqb; ++qb) {
+    C[0] = 0;
+    for (int32_t kb = 0; kb < bm.nkb; ++kb)
+      C[kb + 1] = C[kb] + (B[(size_t)qb * bm.nkb + kb] ? bm.koffs[kb + 1] - bm.koffs[kb] : 0);
+    // P(x) = allowed-by-bitmap keys in [0, x) for a row of block qb
+    auto P = [&](int64_t x) -> int64_t {
+      if (x >= S) return C[bm.nkb];
+      const int32_t kb = bm.kblk[x];
+      return C[kb] + (B[(size_t)qb * bm.nkb + kb] ? x - bm.koffs[kb] : 0);
+    };
+    for (int64_t i = bm.qoffs[qb]; i < bm.qoffs[qb + 1]; ++i) {
+      const Run &r = rb[i];
+      if (r.b0 > r.a0) tot += P(r.b0) - P(r.a0);
+      if (r.b1 > r.a1) tot += P(r.b1) - P(r.a1);
+    }
+  }
+  return tot;
+}
+
+struct Item { int32_t tile, head, off, len; double cost; };
+
+}  // namespace
+}  // namespace lcm
+
+using namespace lcm;
+
+extern "C" const char *attn_last_error(void) { return g_err.c_str(); }
+
+extern "C" const char *attn_version(void) { return "long_context_masked_amd 0.1 (gfx950)"; }
+
+static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc *desc,
+                                    attn_plan **out) {
+  if (!shp || !desc || !out) return fail(ATTN_ERR_INVALID, "NULL argument");
+  *out = nullptr;
+  const attn_shape sh = *shp;
+  if (sh.B < 1 || sh.S < 1 || sh.Hq < 1 || sh.Hkv < 1)
+    return fail(ATTN_ERR_INVALID, "B, S, Hq, Hkv must be >= 1");
+  if (sh.S >= (int64_t(1) << 30)) return fail(ATTN_ERR_UNSUPPORTED, "S must be < 2^30");
+  if (sh.Hq % sh.Hkv) return fail(ATTN_ERR_INVALID, "Hq must be a multiple of Hkv");
+  if (sh.Hq > 65535 || sh.B > 65535) return fail(ATTN_ERR_UNSUPPORTED, "Hq and B must be <= 65535");
+  if (sh.d != 64 && sh.d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%lld (supported: 64, 128)", (long long)sh.d);
+  if (!std::isfinite(sh.scale) || sh.scale < 0.f) return fail(ATTN_ERR_INVALID, "scale must be finite and >= 0");
+  const int64_t S = sh.S;
+  const int G = (int)(sh.Hq / sh.Hkv);
+
+  // bitmap
+  Bitmap bm;
+  const bool has_bm = desc->block_bitmap != nullptr;
+  if (has_bm) {
+    const int nh = desc->bitmap_heads;
+    if (nh != 1 && nh != sh.Hkv && nh != sh.Hq)
+      return fail(ATTN_ERR_INVALID, "bitmap_heads must be 1, Hkv or Hq");
+    if (nh == sh.Hq && nh != sh.Hkv)
+      return fail(ATTN_ERR_UNSUPPORTED, "per-query-head bitmaps need Hq == Hkv");
+    if (desc->n_qblk < 1 || desc->n_kblk < 1) return fail(ATTN_ERR_INVALID, "n_qblk, n_kblk must be >= 1");
+    attn_status st = check_offsets(desc->q_blk_offsets, desc->n_qblk, S, "q_blk_offsets");
+    if (st != ATTN_OK) return st;
+    st = check_offsets(desc->k_blk_offsets, desc->n_kblk, S, "k_blk_offsets");
+    if (st != ATTN_OK) return st;
+    bm.heads = nh; bm.nqb = desc->n_qblk; bm.nkb = desc->n_kblk;
+    const size_t nb = (size_t)nh * bm.nqb * bm.nkb;
+    bm.bits.resize(nb);
+    for (size_t t = 0; t < nb; ++t) bm.bits[t] = desc->block_bitmap[t] ? 1 : 0;
+    bm.qoffs.assign(desc->q_blk_offsets, desc->q_blk_offsets + bm.nqb + 1);
+    bm.koffs.assign(desc->k_blk_offsets, desc->k_blk_offsets + bm.nkb + 1);
+    bm.qblk.resize((size_t)S); bm.kblk.resize((size_t)S);
+    for (int32_t b = 0; b < bm.nqb; ++b)
+      for (int32_t x = bm.qoffs[b]; x < bm.qoffs[b + 1]; ++x) bm.qblk[x] = b;
+    for (int32_t b = 0; b < bm.nkb; ++b)
+      for (int32_t x = bm.koffs[b]; x < bm.koffs[b + 1]; ++x) bm.kblk[x] = b;
+  }
+
+  std::vector<int32_t> colb;
+  attn_status st = build_colb(sh, *desc, colb);
+  if (st != ATTN_OK) return st;
+  std::vector<Run> rowb;
+  int64_t nnz_base = 0;
+  st = rows_from_cols(S, colb, rowb, nnz_base);
+  if (st != ATTN_OK) return st;
+  std::vector<uint8_t> base;
+  classify_base(S, rowb, base);
+
+  auto *p = new attn_plan();
+  p->shape = sh;
+  p->scale = sh.scale > 0.f ? sh.scale : (float)(1.0 / std::sqrt((double)sh.d));
+  p->G = G;
+  p->HG = (G % 2 == 0) ? 2 : 1;
+  p->fwd_rows = kWgRowsHeads / p->HG;
+  p->bitmap_heads = has_bm ? bm.heads : 0;
+  p->nqb = bm.nqb; p->nkb = bm.nkb;
+
+  const int64_t nM = (S + kMicro - 1) / kMicro;
+  const int MR = p->fwd_rows / kMicro;                     // micro rows per fwd tile
+  const int64_t nFQ = (S + p->fwd_rows - 1) / p->fwd_rows;  // fwd Q tiles
+  const int MC = kBwdKeyTile / kMicro;                     // micro cols per bwd tile
+  const int64_t nBK = (S + kBwdKeyTile - 1) / kBwdKeyTile;  // bwd K tiles
+  const int n_mask_heads = has_bm ? bm.heads : 1;
+
+  std::vector<uint32_t> fwd_list, bwd_list;
+  std::vector<int64_t> fwd_off((size_t)n_mask_heads * nFQ), bwd_off((size_t)n_mask_heads * nBK);
+  std::vector<int32_t> fwd_len(fwd_off.size()), bwd_len(bwd_off.size());
+  std::vector<int32_t> fwd_npart(fwd_off.size()), bwd_npart(bwd_off.size());
+  std::vector<int64_t> nnz_head((size_t)n_mask_heads, nnz_base);
+  std::vector<uint8_t> cls;
+  for (int hm = 0; hm < n_mask_heads; ++hm) {
+    const std::vector<uint8_t> *C = &base;
+    if (has_bm) {
+      classify_bitmap(S, base, bm, hm, cls);
+      C = &cls;
+      nnz_head[hm] = nnz_with_bitmap(S, rowb, bm, hm);
+    }
+    for (int64_t qt = 0; qt < nFQ; ++qt) {
+      const size_t slot = (size_t)hm * nFQ + qt;
+      fwd_off[slot] = (int64_t)fwd_list.size();
+      int32_t npart = 0;
+      const int64_t I0 = qt * MR, I1 = std::min<int64_t>(nM, I0 + MR);
+      for (int64_t J = 0; J < nM; ++J) {
+        bool any = false, all = true;
+        for (int64_t I = I0; I < I1; ++I) {
+          const uint8_t c = (*C)[I * nM + J];
+          any |= c != kEmpty; all &= c == kFull;
+        }
+        if (!any) continue;
+        const bool ragged = (J + 1) * kFwdKeyTile > S;
+        const bool part = !all || ragged;
+        npart += part;
+        fwd_list.push_back((uint32_t)J | (part ? kPartialBit : 0u));
+      }
+      fwd_len[slot] = (int32_t)(fwd_list.size() - fwd_off[slot]);
+      fwd_npart[slot] = npart;
+    }
+    for (int64_t kt = 0; kt < nBK; ++kt) {
+      const size_t slot = (size_t)hm * nBK + kt;
+      bwd_off[slot] = (int64_t)bwd_list.size();
+      int32_t npart = 0;
+      const int64_t J0 = kt * MC, J1 = std::min<int64_t>(nM, J0 + MC);
+      for (int64_t I = 0; I < nM; ++I) {
+        bool any = false, all = true;
+        for (int64_t J = J0; J < J1; ++J) {
+          const uint8_t c = (*C)[I * nM + J];
+          any |= c != kEmpty; all &= c == kFull;
+        }
+        if (!any) continue;
+        const bool ragged = (I + 1) * kBwdRowTile > S || (J1 - J0) < MC;
+        const bool part = !all || ragged;
+        npart += part;
+        bwd_list.push_back((uint32_t)I | (part ? kPartialBit : 0u));
+      }
+      bwd_len[slot] = (int32_t)(bwd_list.size() - bwd_off[slot]);
+      bwd_npart[slot] = npart;
+    }
+  }
+  if (fwd_list.size() > 0x7fffffffu || bwd_list.size() > 0x7fffffffu) {
+    delete p;
+    return fail(ATTN_ERR_UNSUPPORTED, "work lists exceed 2^31 entries");
+  }
+
+  auto hm_of = [&](int64_t h) -> int {
+    if (!has_bm || bm.heads == 1) return 0;
+    if (bm.heads == sh.Hkv) return (int)(h / G);
+    return (int)h;
+  };
+
+  // Step 6: items and longest-first order.  A partial tile costs more than a
+  // full one (per-element masking); an item also pays a fixed epilogue.
+  const double kPartCost = 1.25, kItemCost = 0.75;
+  std::vector<Item> fi, bi;
+  for (int64_t h0 = 0; h0 < sh.Hq; h0 += p->HG) {
+    const int hm = hm_of(h0);
+    for (int64_t qt = 0; qt < nFQ; ++qt) {
+      const size_t slot = (size_t)hm * nFQ + qt;
+      const int32_t len = fwd_len[slot], np = fwd_npart[slot];
+      fi.push_back({(int32_t)qt, (int32_t)h0, (int32_t)fwd_off[slot], len,
+                    (len - np) + kPartCost * np + kItemCost});
+    }
+  }
+  for (int64_t kvh = 0; kvh < sh.Hkv; ++kvh) {
+    const int hm = hm_of(kvh * G);
+    for (int64_t kt = 0; kt < nBK; ++kt) {
+      const size_t slot = (size_t)hm * nBK + kt;
+      const int32_t len = bwd_len[slot], np = bwd_npart[slot];
+      bi.push_back({(int32_t)kt, (int32_t)kvh, (int32_t)bwd_off[slot], len,
+                    G * ((len - np) + kPartCost * np) + kItemCost});
+    }
+  }
+  auto by_cost = [](const Item &a, const Item &b) { return a.cost > b.cost; };
+  std::stable_sort(fi.begin(), fi.end(), by_cost);
+  std::stable_sort(bi.begin(), bi.end(), by_cost);
+
+  // blob layout
+  Layout &L = p->lay;
+  int64_t off = 0;
+  auto sect = [&](int64_t bytes) { const int64_t o = off; off = align256(off + bytes); return o; };
+  L.rowb = sect(S * 16);
+  L.colb = sect(S * 16);
+  L.n_fwd_items = (int64_t)fi.size();
+  L.fwd_items = sect(L.n_fwd_items * 16);
+  L.n_fwd_list = (int64_t)fwd_list.size();
+  L.fwd_list = sect(std::max<int64_t>(1, L.n_fwd_list) * 4);
+  L.n_bwd_items = (int64_t)bi.size();
+  L.bwd_items = sect(L.n_bwd_items * 16);
+  L.n_bwd_list = (int64_t)bwd_list.size();
+  L.bwd_list = sect(std::max<int64_t>(1, L.n_bwd_list) * 4);
+  if (has_bm) {
+    L.bits = sect((int64_t)bm.bits.size());
+    L.qblk = sect(S * 4);
+    L.kblk = sect(S * 4);
+    L.qoffs = sect((int64_t)(bm.nqb + 1) * 4);
+    L.koffs = sect((int64_t)(bm.nkb + 1) * 4);
+  }
+  L.total = off;
+  try {
+    p->blob.assign((size_t)L.total, 0);
+  } catch (const std::bad_alloc &) {
+    delete p;
+    return fail(ATTN_ERR_NOMEM, "host blob of %lld bytes", (long long)L.total);
+  }
+  uint8_t *blob = p->blob.data();
+  std::memcpy(blob + L.rowb, rowb.data(), (size_t)S * 16);
+  std::memcpy(blob + L.colb, colb.data(), (size_t)S * 16);
+  int32_t *it = reinterpret_cast<int32_t *>(blob + L.fwd_items);
+  int64_t ffull = 0, fpart = 0, bfull = 0, bpart = 0;
+  for (const Item &x : fi) {
+    *it++ = x.tile; *it++ = x.head; *it++ = x.off; *it++ = x.len;
+  }
+  for (int64_t h0 = 0; h0 < sh.Hq; h0 += p->HG) {
+    const int hm = hm_of(h0);
+    for (int64_t qt = 0; qt < nFQ; ++qt) {
+      const size_t slot = (size_t)hm * nFQ + qt;
+      fpart += fwd_npart[slot]; ffull += fwd_len[slot] - fwd_npart[slot];
+    }
+  }
+  if (!fwd_list.empty()) std::memcpy(blob + L.fwd_list, fwd_list.data(), fwd_list.size() * 4);
+  it = reinterpret_cast<int32_t *>(blob + L.bwd_items);
+  for (const Item &x : bi) {
+    *it++ = x.tile; *it++ = x.head; *it++ = x.off; *it++ = x.len;
+  }
+  for (int64_t kvh = 0; kvh < sh.Hkv; ++kvh) {
+    const int hm = hm_of(kvh * G);
+    for (int64_t kt = 0; kt < nBK; ++kt) {
+      const size_t slot = (size_t)hm * nBK + kt;
+      bpart += bwd_npart[slot]; bfull += bwd_len[slot] - bwd_npart[slot];
+    }
+  }
+  if (!bwd_list.empty()) std::memcpy(blob + L.bwd_list, bwd_list.data(), bwd_list.size() * 4);
+  if (has_bm) {
+    std::memcpy(blob + L.bits, bm.bits.data(), bm.bits.size());
+    std::memcpy(blob + L.qblk, bm.qblk.data(), (size_t)S * 4);
+    std::memcpy(blob + L.kblk, bm.kblk.data(), (size_t)S * 4);
+    std::memcpy(blob + L.qoffs, bm.qoffs.data(), bm.qoffs.size() * 4);
+    std::memcpy(blob + L.koffs, bm.koffs.data(), bm.koffs.size() * 4);
+  }
+
+  int64_t nnz_b = 0;
+  for (int64_t h = 0; h < sh.Hq; ++h) nnz_b += nnz_head[hm_of(h)];
+  attn_stats &s = p->stats;
+  s.nnz_per_batch = nnz_b;
+  s.nnz_total = nnz_b * sh.B;
+  s.flops_fwd = 4.0 * (double)sh.d * (double)s.nnz_total;
+  s.flops_bwd = 10.0 * (double)sh.d * (double)s.nnz_total;
+  s.fwd_items = L.n_fwd_items;
+  s.fwd_tiles_full = ffull;
+  s.fwd_tiles_partial = fpart;
+  s.bwd_items = L.n_bwd_items;
+  s.bwd_tiles_full = bfull * G;
+  s.bwd_tiles_partial = bpart * G;
+  s.fwd_tile_rows = p->fwd_rows;
+  s.fwd_tile_cols = kFwdKeyTile;
+  s.bwd_tile_rows = kBwdRowTile;
+  s.bwd_tile_cols = kBwdKeyTile;
+  s.heads_per_item = p->HG;
+  s.device_bytes = L.total;
+  *out = p;
+  return ATTN_OK;
+}
+
+extern "C" attn_status attn_plan_create(const attn_shape *shape, const attn_mask_desc *desc,
+                                        attn_plan **out) {
+  clear_error();
+  try {
+    return plan_create_impl(shape, desc, out);
+  } catch (const std::bad_alloc &) {
+    return fail(ATTN_ERR_NOMEM, "host allocation failed while compiling the mask");
+  } catch (...) {
+    return fail(ATTN_ERR_INVALID, "unexpected error while compiling the mask");
+  }
+}
+
+extern "C" size_t attn_plan_device_bytes(const attn_plan *plan) {
+  return plan ? (size_t)plan->lay.total : 0;
+}
+
+extern "C" attn_status attn_plan_stats(const attn_plan *plan, attn_stats *out) {
+  clear_error();
+  if (!plan || !out) return fail(ATTN_ERR_INVALID, "NULL argument");
+  *out = plan->stats;
+  return ATTN_OK;
+}
+
+extern "C" attn_status attn_plan_get_layout(const attn_plan *plan, attn_plan_layout *out) {
+  clear_error();
+  if (!plan || !out) return fail(ATTN_ERR_INVALID, "NULL argument");
+  const Layout &L = plan->lay;
+  out->blob = plan->blob.data();
+  out->blob_bytes = L.total;
+  out->off_rowb = L.rowb; out->off_colb = L.colb;
+  out->off_fwd_items = L.fwd_items; out->n_fwd_items = L.n_fwd_items;
+  out->off_fwd_list = L.fwd_list; out->n_fwd_list = L.n_fwd_list;
+  out->off_bwd_items = L.bwd_items; out->n_bwd_items = L.n_bwd_items;
+  out->off_bwd_list = L.bwd_list; out->n_bwd_list = L.n_bwd_list;
+  out->off_bits = L.bits; out->off_qblk = L.qblk; out->off_kblk = L.kblk;
+  out->off_qoffs = L.qoffs; out->off_koffs = L.koffs;
+  return ATTN_OK;
+}
+
+extern "C" size_t attn_bwd_workspace_bytes(const attn_plan *plan) {
+  if (!plan) return 0;
+  return (size_t)((plan->shape.B * plan->shape.Hq * plan->shape.S * 4 + 255) & ~int64_t(255));
+}
+
+extern "C" void attn_plan_destroy(attn_plan *plan) { delete plan; }

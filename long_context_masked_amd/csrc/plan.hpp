@@ -1,0 +1,53 @@
+// Internal plan representation shared by the mask compiler (plan.cpp) and
+// the launch code (api.hip).  Not part of the public interface.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "attn.h"
+
+namespace lcm {
+
+// Tile geometry.  Classification runs on 64x64 "micro tiles"; every kernel
+// tile is a whole number of them.
+constexpr int kMicro = 64;
+constexpr int kFwdKeyTile = 64;   // forward / dQ: keys per K-tile
+constexpr int kBwdKeyTile = 128;  // dK/dV: keys per workgroup (4 waves x 32)
+constexpr int kBwdRowTile = 64;   // dK/dV: query rows per Q-tile
+constexpr int kWgRowsHeads = 128; // forward / dQ: (rows x heads) per workgroup
+
+constexpr uint32_t kPartialBit = 0x80000000u;
+
+// Byte offsets of the sections of the device blob (all 256-byte aligned).
+struct Layout {
+  int64_t rowb = -1, colb = -1;
+  int64_t fwd_items = -1, fwd_list = -1, bwd_items = -1, bwd_list = -1;
+  int64_t bits = -1, qblk = -1, kblk = -1, qoffs = -1, koffs = -1;
+  int64_t n_fwd_items = 0, n_fwd_list = 0, n_bwd_items = 0, n_bwd_list = 0;
+  int64_t total = 0;
+};
+
+}  // namespace lcm
+
+struct attn_plan {
+  attn_shape shape{};
+  float scale = 0.f;
+  int G = 1;            // query heads per KV head
+  int HG = 1;           // query heads per forward / dQ workgroup
+  int fwd_rows = 128;   // query rows per forward / dQ workgroup
+  int bitmap_heads = 0; // 0 = no bitmap
+  int nqb = 0, nkb = 0;
+  std::vector<uint8_t> blob;  // host copy of the device blob
+  lcm::Layout lay;
+  attn_stats stats{};
+  void *dev_blob = nullptr;
+  size_t dev_bytes = 0;
+};
+
+namespace lcm {
+// Thread-local last error (defined in plan.cpp).
+attn_status fail(attn_status s, const char *fmt, ...);
+void clear_error();
+}  // namespace lcm

@@ -84,12 +84,33 @@ def forward(q, k, v, spec, scale=None, heads=None, row_block=512):
     return o, lse
 
 
-def backward(q, k, v, do, spec, scale=None, kv_heads=None, row_block=512):
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 value (8 significant
+    bits, ties to even), returned as float64.  Normal-range values only."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m * 2^e, 0.5 <= |m| < 1
+    scaled = m * 256.0                      # 8 significant bits before the point
+    r = np.round(scaled)                    # numpy rounds half to even
+    return np.ldexp(r / 256.0, e)
+
+
+def backward(q, k, v, do, spec, scale=None, kv_heads=None, row_block=512,
+             o_for_d="exact", magnitudes=False):
     """dQ, dK, dV (and O, LSE) for the selected KV heads and their groups.
 
     Returns a dict with dq [B,S,G*n,d] for the query heads of the selected KV
     heads (in order), dk/dv [B,S,n,d], o and lse for the same query heads,
     and ``heads``, the query head indices covered.
+
+    ``o_for_d``: the O entering D_i = dO_i . O_i.  "exact" uses the exact
+    output; "bf16" uses it rounded to bfloat16, i.e. the O a caller holds when
+    the forward returns bf16 and the backward receives that O back.
+
+    ``magnitudes``: also return, per output element x = sum_t a_t b_t of each
+    product (O = P V, dV = P^T dO, dQ = scale dS K, dK = scale dS^T Q), the
+    quadratic magnitude sqrt(sum_t (a_t b_t)^2) under keys "m_o", "m_dv",
+    "m_dq", "m_dk".  It sets the size of the error a product makes when one
+    of its operands is rounded to a narrower format term by term.
     """
     B, S, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -98,11 +119,18 @@ def backward(q, k, v, do, spec, scale=None, kv_heads=None, row_block=512):
     kv_heads = list(range(Hkv)) if kv_heads is None else list(kv_heads)
     heads = [kv * G + g for kv in kv_heads for g in range(G)]
     nq = len(heads)
+    if o_for_d not in ("exact", "bf16"):
+        raise ValueError("o_for_d must be 'exact' or 'bf16'")
     dq = np.zeros((B, S, nq, d))
     dk = np.zeros((B, S, len(kv_heads), d))
     dv = np.zeros((B, S, len(kv_heads), d))
     o = np.zeros((B, S, nq, d))
     lse = np.zeros((B, nq, S))
+    if magnitudes:
+        m_o = np.zeros_like(o)
+        m_dq = np.zeros_like(dq)
+        m_dk2 = np.zeros_like(dk)
+        m_dv2 = np.zeros_like(dv)
     for b in range(B):
         for hi, h in enumerate(heads):
             kvi = hi // G
@@ -119,13 +147,23 @@ def backward(q, k, v, do, spec, scale=None, kv_heads=None, row_block=512):
                 oi = p @ vv
                 o[b, i0:i1, hi, :] = oi
                 lse[b, hi, i0:i1] = l
-                D = (doi * oi).sum(axis=1)
+                od = oi if o_for_d == "exact" else round_bf16(oi)
+                D = (doi * od).sum(axis=1)
                 dp = doi @ vv.T
                 ds = p * (dp - D[:, None])
                 dq[b, i0:i1, hi, :] = (ds @ kk) * scale
                 dk[b, :, kvi, :] += (ds.T @ qi) * scale
                 dv[b, :, kvi, :] += p.T @ doi
-    return {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": lse, "heads": heads}
+                if magnitudes:
+                    p2, ds2 = p * p, ds * ds
+                    m_o[b, i0:i1, hi, :] = np.sqrt(p2 @ (vv * vv))
+                    m_dq[b, i0:i1, hi, :] = np.sqrt(ds2 @ (kk * kk)) * scale
+                    m_dk2[b, :, kvi, :] += (ds2.T @ (qi * qi)) * scale * scale
+                    m_dv2[b, :, kvi, :] += p2.T @ (doi * doi)
+    out = {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": lse, "heads": heads}
+    if magnitudes:
+        out.update(m_o=m_o, m_dq=m_dq, m_dk=np.sqrt(m_dk2), m_dv=np.sqrt(m_dv2))
+    return out
 
 
 def output_rows(q, k, v, spec, h, rows, scale=None):

@@ -1,0 +1,144 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases compare every element of O, LSE, dQ, dK and dV; they span
+several tiles, ragged tails, both head dims, GQA and MHA, and every mask
+family.  The gate is described in gpu_util (max-abs 2e-2 and mean-abs 2e-3
+of the oracle tensor's RMS, with room for the bf16 formats); LSE must agree
+to 5e-3 absolute and be -inf exactly on rows with no allowed key.
+"""
+import numpy as np
+import pytest
+
+import synthetic as syn
+from oracle import attention as ora
+from oracle import masks as om
+
+from gpu_util import gate, to_dev, to_f64, f64
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import long_context_masked_amd as lcm  # noqa: E402
+
+
+def run_case(spec, B, Hq, Hkv, d, seed=0, check_bwd=True):
+    S = spec["S"]
+    x = syn.attention_inputs(B, S, Hq, Hkv, d, seed)
+    q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
+    plan = lcm.Plan(B, S, Hq, Hkv, d, spec)
+    o, lse = lcm.fwd(plan, q, k, v)
+    if check_bwd:
+        dq, dk, dv = lcm.bwd(plan, q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    qf, kf, vf, dof = (f64(x[n]) for n in ("q", "k", "v", "do"))
+    ref = ora.backward(qf, kf, vf, dof, spec, o_for_d="bf16", magnitudes=True)
+    gate("O", to_f64(o), ref["o"], ref["m_o"])
+    lg = lse.cpu().numpy().astype(np.float64)
+    lr = ref["lse"]
+    fin = np.isfinite(lr)
+    assert (np.isneginf(lg) == ~fin).all()
+    assert np.abs(lg[fin] - lr[fin]).max() <= 5e-3
+    if check_bwd:
+        gate("dQ", to_f64(dq), ref["dq"], ref["m_dq"])
+        gate("dK", to_f64(dk), ref["dk"], ref["m_dk"])
+        gate("dV", to_f64(dv), ref["dv"], ref["m_dv"])
+
+
+TINY = syn.config_mask_specs("tiny", Hkv=2)
+
+
+@pytest.mark.parametrize("label,spec", TINY, ids=[l for l, _ in TINY])
+def test_tiny_config_every_family(label, spec):
+    """B=1, S=512, Hq=4, Hkv=2, d=64, every mask family, fwd + bwd."""
+    run_case(spec, 1, 4, 2, 64)
+
+
+@pytest.mark.parametrize("label", ["causal", "causal_document", "varblock_50"])
+def test_batch_of_two(label):
+    spec = dict(TINY)[label]
+    run_case(spec, 2, 4, 2, 64, seed=1)
+
+
+def _ragged_specs(S, Hkv):
+    docs = syn.sample_doc_lens(S, 16, 400, 3)
+    q = 100
+    offs, bits = syn.variable_block_bitmap(S, 32, 224, Hkv, 0.5, seed=2)
+    uoffs, ubits = syn.uniform_block_bitmap(S, 64, Hkv, 0.5, seed=4)
+    return [
+        ("full", syn.spec_full(S)), ("causal", syn.spec_causal(S)),
+        ("causal_sw", syn.spec_sliding(S, 130, True)), ("full_sw", syn.spec_sliding(S, 70, False)),
+        ("causal_document", syn.spec_document(docs, True)),
+        ("full_document", syn.spec_document(docs, False)),
+        ("prefix_lm_causal", syn.spec_prefix_lm_causal(S, 150)),
+        ("shared_question", syn.spec_shared_question(q, syn.sample_answers(S - q, 4, 1))),
+        ("global_sliding", syn.spec_global_sliding(S, 16, 100)),
+        ("causal_blockwise", syn.spec_causal_blockwise(S, 256)),
+        ("block64", syn.with_bitmap(syn.spec_full(S), uoffs, uoffs, ubits)),
+        ("varblock", syn.with_bitmap(syn.spec_full(S), offs, offs, bits)),
+    ]
+
+
+RAGGED_GQA = _ragged_specs(700, 1)
+
+
+@pytest.mark.parametrize("label,spec", RAGGED_GQA, ids=[l for l, _ in RAGGED_GQA])
+def test_d128_gqa_ragged(label, spec):
+    """d=128, Hq=8 over one KV head (two query heads per workgroup), S=700."""
+    run_case(spec, 1, 8, 1, 128, seed=5)
+
+
+RAGGED_MHA = _ragged_specs(333, 2)
+
+
+@pytest.mark.parametrize("label,spec", RAGGED_MHA, ids=[l for l, _ in RAGGED_MHA])
+def test_d128_mha_ragged(label, spec):
+    """d=128, MHA 2:2 (one head of 128 rows per workgroup), S=333."""
+    run_case(spec, 1, 2, 2, 128, seed=6)
+
+
+def test_d64_mha_odd_group_and_short():
+    """Hq=3 over Hkv=1 (odd group), S=65 and S=1."""
+    run_case(syn.spec_causal(65), 1, 3, 1, 64, seed=7)
+    run_case(syn.spec_full(1), 1, 3, 1, 64, seed=8)
+
+
+def test_empty_rows_and_keys():
+    """A bitmap that leaves whole block rows and columns empty: O = 0,
+    LSE = -inf, zero gradients there."""
+    S = 256
+    offs = [0, 64, 128, 192, 256]
+    bits = np.array([[[1, 0, 1, 0], [0, 0, 0, 0], [1, 0, 1, 0], [0, 0, 0, 1]]], dtype=np.uint8)
+    spec = syn.with_bitmap(syn.spec_full(S), offs, offs, bits)
+    run_case(spec, 1, 2, 1, 64, seed=9)
+
+
+def test_forward_is_deterministic():
+    S = 1024
+    spec = syn.spec_causal(S)
+    x = syn.attention_inputs(1, S, 8, 2, 128, 0, with_do=False)
+    q, k, v = (to_dev(x[n], torch) for n in ("q", "k", "v"))
+    plan = lcm.Plan(1, S, 8, 2, 128, spec)
+    o1, l1 = lcm.fwd(plan, q, k, v)
+    o2, l2 = lcm.fwd(plan, q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_forced_device_error_leaves_outputs_untouched(monkeypatch):
+    S = 128
+    plan = lcm.Plan(1, S, 2, 1, 64, syn.spec_causal(S))
+    x = syn.attention_inputs(1, S, 2, 1, 64, 0, with_do=False)
+    q, k, v = (to_dev(x[n], torch) for n in ("q", "k", "v"))
+    plan.bind(q.device)
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((1, 2, S), 3.0, device=q.device)
+    monkeypatch.setenv("ATTN_FORCE_DEVICE_ERROR", "1")
+    with pytest.raises(lcm.AttnError) as ei:
+        lcm.fwd(plan, q, k, v, out=o, lse=lse)
+    assert ei.value.status == 4
+    monkeypatch.delenv("ATTN_FORCE_DEVICE_ERROR")
+    torch.cuda.synchronize()
+    assert (o == 7.0).all() and (lse == 3.0).all()

@@ -1,0 +1,299 @@
+"""CPU tests of the library's host side: exports, mask compiler, scheduler,
+error statuses.  No GPU work is launched here."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synthetic as syn
+from oracle import masks as om
+
+lcm = pytest.importorskip("long_context_masked_amd")
+from long_context_masked_amd import _lib as L  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    txt = open(os.path.join(ROOT, "include", "attn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_symbols()
+    assert "attn_fwd" in names and "attn_bwd" in names and len(names) >= 10
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.SIGNATURES, f"binding lacks {n}"
+    assert b"gfx950" in lib.attn_version()
+
+
+def _tiny_specs(Hkv=2):
+    return syn.config_mask_specs("tiny", Hkv=Hkv)
+
+
+@pytest.mark.parametrize("label,spec", _tiny_specs(), ids=[l for l, _ in _tiny_specs()])
+def test_nnz_matches_oracle_popcount(label, spec):
+    Hq, Hkv = 4, 2
+    p = lcm.Plan(2, spec["S"], Hq, Hkv, 64, spec)
+    want = sum(om.nnz(spec, om.mask_head(spec, h, Hq, Hkv)) for h in range(Hq))
+    assert p.stats["nnz_per_batch"] == want
+    assert p.stats["nnz_total"] == 2 * want
+    assert p.stats["flops_fwd"] == 4 * 64 * 2 * want
+    assert p.stats["flops_bwd"] == 10 * 64 * 2 * want
+
+
+def _expand_colb(cb, S):
+    i = np.arange(S)[:, None]
+    m = ((i >= cb[None, :, 0]) & (i < cb[None, :, 1])) | ((i >= cb[None, :, 2]) & (i < cb[None, :, 3]))
+    return ~m
+
+
+def _expand_rowb(rb, S):
+    j = np.arange(S)[None, :]
+    return ((j >= rb[:, 0:1]) & (j < rb[:, 1:2])) | ((j >= rb[:, 2:3]) & (j < rb[:, 3:4]))
+
+
+def _family_specs(S, seed):
+    docs = syn.sample_doc_lens(S, 8, 300, seed)
+    q = 37
+    return [
+        syn.spec_full(S), syn.spec_causal(S), syn.spec_sliding(S, 33, True),
+        syn.spec_sliding(S, 21, False), syn.spec_document(docs, False), syn.spec_document(docs, True),
+        syn.spec_prefix_lm_causal(S, 77), syn.spec_shared_question(q, syn.sample_answers(S - q, 4, seed)),
+        syn.spec_global_sliding(S, 16, 50), syn.spec_global_sliding(S, 16, 50, True),
+        syn.spec_causal_blockwise(S, 128), syn.spec_causal_blockwise(S, 128, "block_causal"),
+        syn.spec_causal_blockwise(S, 100),
+        syn.spec_prefix_lm_document(docs, [syn.sample_prefix(0, L, seed + i) for i, L in enumerate(docs)]),
+        syn.spec_block_causal_document(docs, 40),
+    ]
+
+
+@pytest.mark.parametrize("S,seed", [(700, 0), (1024, 1), (333, 2)])
+def test_encodings_match_oracle_predicate(S, seed):
+    """Column bounds and row runs the compiler stores both expand to exactly
+    the oracle's predicate, for every static family."""
+    for spec in _family_specs(S, seed):
+        p = lcm.Plan(1, S, 2, 1, 64, spec)
+        lay = p.layout()
+        want = om.base_allowed(spec, 0, S)
+        assert (_expand_colb(lay["colb"], S) == want).all(), spec["family"]
+        assert (_expand_rowb(lay["rowb"], S) == want).all(), spec["family"]
+
+
+def _check_lists(p, spec, Hq, Hkv):
+    """Every allowed pair is covered by exactly one listed tile; a tile flagged
+    FULL is fully allowed; EMPTY tiles are never listed; every (tile, head)
+    item appears exactly once."""
+    S = spec["S"]
+    G = Hq // Hkv
+    lay = p.layout()
+    st = p.stats
+    FR, FC = st["fwd_tile_rows"], st["fwd_tile_cols"]
+    BR, BC = st["bwd_tile_rows"], st["bwd_tile_cols"]
+    HG = st["heads_per_item"]
+    dense = {}
+
+    def dm(h):
+        hm = om.mask_head(spec, h, Hq, Hkv)
+        if hm not in dense:
+            dense[hm] = om.dense_mask(spec, hm)
+        return dense[hm]
+
+    seen = set()
+    for qt, h0, off, n in lay["fwd_items"]:
+        key = (qt, h0)
+        assert key not in seen
+        seen.add(key)
+        ents = lay["fwd_list"][off:off + n]
+        tiles = (ents & 0x7FFFFFFF).astype(int)
+        assert len(set(tiles.tolist())) == len(tiles)
+        r0, r1 = qt * FR, min(S, qt * FR + FR)
+        for h in range(h0, h0 + HG):
+            a = dm(h)[r0:r1]
+            cover = np.zeros(S, dtype=bool)
+            for t, e in zip(tiles, ents):
+                c0, c1 = t * FC, min(S, t * FC + FC)
+                blk = a[:, c0:c1]
+                assert blk.any(), "empty tile listed"
+                if not (e >> 31):
+                    assert blk.all() and c1 - c0 == FC, "FULL tile not fully allowed"
+                cover[c0:c1] = True
+            assert not a[:, ~cover].any(), "allowed pair outside the listed tiles"
+    assert len(seen) == (Hq // HG) * ((S + FR - 1) // FR)
+
+    seen = set()
+    for kt, kvh, off, n in lay["bwd_items"]:
+        assert (kt, kvh) not in seen
+        seen.add((kt, kvh))
+        ents = lay["bwd_list"][off:off + n]
+        tiles = (ents & 0x7FFFFFFF).astype(int)
+        c0, c1 = kt * BC, min(S, kt * BC + BC)
+        for g in range(G):
+            a = dm(kvh * G + g)[:, c0:c1]
+            cover = np.zeros(S, dtype=bool)
+            for t, e in zip(tiles, ents):
+                r0, r1 = t * BR, min(S, t * BR + BR)
+                assert a[r0:r1].any() or G > 1
+                if not (e >> 31):
+                    assert a[r0:r1].all() and r1 - r0 == BR
+                cover[r0:r1] = True
+            assert not a[~cover].any()
+    assert len(seen) == Hkv * ((S + BC - 1) // BC)
+
+
+@pytest.mark.parametrize("label,spec", _tiny_specs(), ids=[l for l, _ in _tiny_specs()])
+def test_work_lists_cover_mask_exactly(label, spec):
+    _check_lists(lcm.Plan(1, spec["S"], 4, 2, 64, spec), spec, 4, 2)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (3, 1), (8, 2)])
+def test_work_lists_ragged_and_head_groupings(Hq, Hkv):
+    S = 200  # ragged against 64- and 128-wide tiles
+    specs = _family_specs(S, 3)[:12]
+    offs, bits = syn.variable_block_bitmap(S, 20, 90, Hkv, 0.5, seed=5)
+    specs.append(syn.with_bitmap(syn.spec_causal(S), offs, offs, bits))
+    for spec in specs:
+        _check_lists(lcm.Plan(1, S, Hq, Hkv, 128, spec), spec, Hq, Hkv)
+
+
+def _lpt_makespan(costs, m):
+    loads = np.zeros(m)
+    for c in costs:
+        loads[np.argmin(loads)] += c
+    return loads.max()
+
+
+@pytest.mark.parametrize("family", ["causal", "causal_document", "block64_50"])
+def test_schedule_is_longest_first(family):
+    """Items are issued longest first, which bounds the list-scheduling
+    makespan by Graham's LPT bound 4/3 * max(total/m, largest item)."""
+    S, Hq, Hkv = 4096, 16, 2
+    if family == "causal":
+        spec = syn.spec_causal(S)
+    elif family == "causal_document":
+        spec = syn.spec_document(syn.sample_doc_lens(S, 64, 2048, 0), True)
+    else:
+        offs, bits = syn.uniform_block_bitmap(S, 64, Hkv, 0.5, 0)
+        spec = syn.with_bitmap(syn.spec_full(S), offs, offs, bits)
+    p = lcm.Plan(1, S, Hq, Hkv, 128, spec)
+    lay = p.layout()
+    for items, lst in ((lay["fwd_items"], lay["fwd_list"]), (lay["bwd_items"], lay["bwd_list"])):
+        costs = []
+        for _, _, off, n in items:
+            e = lst[off:off + n]
+            npart = int((e >> 31).sum())
+            costs.append((n - npart) + 1.25 * npart)
+        costs = np.array(costs)
+        assert (np.diff(costs) <= 1e-9).all(), "items not in non-increasing cost order"
+        for m in (64, 256, 512):
+            bound = 4.0 / 3.0 * max(costs.sum() / m, costs.max())
+            assert _lpt_makespan(costs, m) <= bound + 1e-9
+
+
+def _status(fn):
+    try:
+        fn()
+    except L.AttnError as e:
+        return e.status
+    return L.ATTN_OK
+
+
+def _create(shape, desc):
+    sh = L.Shape(*shape)
+    h = C.c_void_p()
+    st = L.lib().attn_plan_create(C.byref(sh), C.byref(desc), C.byref(h))
+    if st == L.ATTN_OK:
+        L.lib().attn_plan_destroy(h)
+    return st
+
+
+def test_plan_create_errors():
+    S = 256
+    ok = lcm.MaskDescriptor(syn.spec_causal(S)).c
+    assert _create((1, S, 4, 2, 64, 0.0), ok) == L.ATTN_OK
+    assert _create((1, S, 4, 2, 96, 0.0), ok) == L.ATTN_ERR_UNSUPPORTED
+    assert _create((1, S, 4, 3, 64, 0.0), ok) == L.ATTN_ERR_INVALID
+    assert _create((0, S, 4, 2, 64, 0.0), ok) == L.ATTN_ERR_INVALID
+    assert _create((1, S, 4, 2, 64, float("nan")), ok) == L.ATTN_ERR_INVALID
+    assert L.lib().attn_plan_create(None, None, None) == L.ATTN_ERR_INVALID
+    assert b"NULL" in L.lib().attn_last_error()
+
+    def desc(spec, **kw):
+        d = lcm.MaskDescriptor(spec)
+        for k, v in kw.items():
+            setattr(d.c, k, v)
+        return d
+
+    d = desc(syn.spec_sliding(S, 8, True), window_left=0)
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
+    d = desc(syn.spec_sliding(S, 8, False), window_right=0)
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
+    d = desc(syn.spec_causal(S), kind=99)
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
+    d = lcm.MaskDescriptor(syn.spec_document([100, 100, 56], True))
+    bad = np.array([0, 150, 100, 256], dtype=np.int32)
+    d.c.cu_seqlens = bad.ctypes.data_as(L.P32)
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
+    bad2 = np.array([0, 100, 200, 255], dtype=np.int32)
+    d.c.cu_seqlens = bad2.ctypes.data_as(L.P32)
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
+    d = lcm.MaskDescriptor(syn.spec_prefix_lm_document([100, 156], [5, 157]))
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
+    cb = np.zeros((S, 4), dtype=np.int32)
+    cb[3, 1] = S + 1
+    d = lcm.MaskDescriptor({"family": "column_bounds", "S": S, "col_bounds": cb})
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
+    # a checkerboard of masked columns gives rows with many allowed runs
+    cb = np.zeros((S, 4), dtype=np.int32)
+    cb[1::2, 1] = S
+    d = lcm.MaskDescriptor({"family": "column_bounds", "S": S, "col_bounds": cb})
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_UNSUPPORTED
+    offs, bits = syn.uniform_block_bitmap(S, 64, 3, 0.5, 0)
+    d = lcm.MaskDescriptor(syn.with_bitmap(syn.spec_full(S), offs, offs, bits))
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
+    offs, bits = syn.uniform_block_bitmap(S, 64, 4, 0.5, 0)
+    d = lcm.MaskDescriptor(syn.with_bitmap(syn.spec_full(S), offs, offs, bits))
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_UNSUPPORTED
+    assert _create((1, S, 4, 4, 64, 0.0), d.c) == L.ATTN_OK
+    bad_offs = np.array([0, 64, 64, 192, 256], dtype=np.int32)
+    d.c.q_blk_offsets = bad_offs.ctypes.data_as(L.P32)
+    assert _create((1, S, 4, 4, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
+
+
+def test_launch_entry_points_validate_before_touching_the_gpu():
+    """Invalid arguments return ATTN_ERR_INVALID without any HIP call (this
+    runs on a host with no GPU)."""
+    S = 128
+    p = lcm.Plan(1, S, 2, 1, 64, syn.spec_causal(S))
+    lib = L.lib()
+    P = C.c_void_p
+    a = P(4096)  # never dereferenced: validation fails first
+    assert lib.attn_fwd(None, a, a, a, a, a, None) == L.ATTN_ERR_INVALID
+    assert lib.attn_fwd(p.handle, a, a, a, a, a, None) == L.ATTN_ERR_INVALID  # unbound plan
+    assert b"not bound" in lib.attn_last_error()
+    assert lib.attn_bwd(p.handle, a, a, a, a, a, a, a, a, a, a, C.c_size_t(1 << 20), None) == L.ATTN_ERR_INVALID
+    assert lib.attn_plan_bind(p.handle, None, C.c_size_t(1 << 20), None) == L.ATTN_ERR_INVALID
+    assert lib.attn_plan_bind(p.handle, P(4096 + 8), C.c_size_t(1 << 20), None) == L.ATTN_ERR_INVALID
+    assert lib.attn_plan_bind(p.handle, P(4096), C.c_size_t(16), None) == L.ATTN_ERR_INVALID
+    os.environ["ATTN_FORCE_DEVICE_ERROR"] = "1"
+    try:
+        assert lib.attn_plan_bind(p.handle, P(4096), C.c_size_t(1 << 20), None) == L.ATTN_ERR_DEVICE
+    finally:
+        del os.environ["ATTN_FORCE_DEVICE_ERROR"]
+    assert lib.attn_plan_device_bytes(None) == 0
+    assert lib.attn_bwd_workspace_bytes(p.handle) >= 2 * S * 4
+
+
+def test_scale_default_and_stats_fields():
+    S = 300
+    p = lcm.Plan(3, S, 8, 2, 128, syn.spec_sliding(S, 40, False))
+    st = p.stats
+    assert st["heads_per_item"] == 2 and st["fwd_tile_rows"] == 64
+    assert st["bwd_tile_cols"] == 128 and st["bwd_tile_rows"] == 64
+    assert st["device_bytes"] == p.device_bytes()
+    assert p.workspace_bytes() >= 3 * 8 * S * 4

@@ -324,3 +324,55 @@ def test_bf16_rounding_is_rne():
     assert b[3] == -2.5
     assert b[5] == np.float32(1.0078125)
     assert abs(b[4] - 3.0e-3) < 3.0e-3 * 2**-8
+
+
+def test_round_bf16_pins():
+    """The oracle's bf16 rounding against hand values and against the input
+    generator's independent implementation."""
+    hand = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, 1.0 + 2**-8 + 2**-30, -2.5, 0.0,
+                     3.0 * 2**-140 * 2**10])
+    want = np.array([1.0, 1.0, 1.0 + 2**-6, 1.0 + 2**-7, -2.5, 0.0, 3.0 * 2**-130])
+    np.testing.assert_array_equal(ora.round_bf16(hand), want)
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    other = syn.bf16_bits_to_f32(syn.bf16_bits_from_f32(x)).astype(np.float64)
+    np.testing.assert_array_equal(ora.round_bf16(x.astype(np.float64)), other)
+
+
+def test_magnitudes_pins():
+    """Quadratic magnitudes: a single-term product gives |x| exactly; in
+    general |x| <= sqrt(#terms) * m (Cauchy-Schwarz) and m <= sum |a b|."""
+    S, d = 16, 4
+    x = _inputs(S, 2, 1, d, seed=12)
+    spec = syn.spec_causal(S)
+    g = ora.backward(x["q"], x["k"], x["v"], x["do"], spec, magnitudes=True)
+    # row 0 sees key 0 only: O_0 = v_0 with P = 1
+    for h in range(2):
+        np.testing.assert_array_equal(g["m_o"][0, 0, h], np.abs(x["v"][0, 0, 0]))
+    # the last key is seen by the last row only, for each of the two heads
+    for name in ("o", "dq"):
+        n_terms = np.arange(1, S + 1)[None, :, None, None]
+        assert (np.abs(g[name]) <= np.sqrt(n_terms) * g["m_" + name] * (1 + 1e-12) + 1e-15).all()
+    for name in ("dk", "dv"):
+        n_terms = 2 * np.arange(S, 0, -1)[None, :, None, None]
+        assert (np.abs(g[name]) <= np.sqrt(n_terms) * g["m_" + name] * (1 + 1e-12) + 1e-15).all()
+    # dO = 1: m_dv_j = sqrt(sum over rows and heads of p_ij^2) <= sum_i p_ij
+    g1 = ora.backward(x["q"], x["k"], x["v"], np.ones_like(x["do"]), spec, magnitudes=True)
+    assert (g1["m_dv"] <= g1["dv"] * (1 + 1e-12) + 1e-15).all()
+
+
+def test_o_for_d_bf16_is_exact_when_o_is_representable():
+    """With V constant and bf16-representable, O is exactly representable, so
+    D from the rounded O equals D from the exact O; otherwise they differ."""
+    S = 40
+    x = _inputs(S, 2, 1, 4, seed=13)
+    spec = syn.spec_sliding(S, 9, True)
+    v = np.broadcast_to(x["v"][:, :1], x["v"].shape).copy()
+    a = ora.backward(x["q"], x["k"], v, x["do"], spec)
+    b = ora.backward(x["q"], x["k"], v, x["do"], spec, o_for_d="bf16")
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(a[n], b[n], atol=1e-13)
+    c = ora.backward(x["q"], x["k"], x["v"], x["do"], spec, o_for_d="bf16")
+    e = ora.backward(x["q"], x["k"], x["v"], x["do"], spec)
+    assert np.abs(c["dq"] - e["dq"]).max() > 0
+    np.testing.assert_array_equal(c["dv"], e["dv"])
