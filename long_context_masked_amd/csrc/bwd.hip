@@ -51,22 +51,22 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
 // ---------------------------------------------------------------------------
 // dK / dV: one workgroup per (K-tile of 128 keys, KV head).  Wave w owns keys
 // 32w .. 32w+31 of the tile (lane l: key 32w + l % 32), keeps K and V of
-// those keys as MFMA operands in registers and accumulates dK^T, dV^T.  For
-// each listed Q-tile of 64 rows and each query head of the group, Q, dO,
-// their transposes, LSE and D are staged in LDS (double-buffered).
+// those keys as MFMA operands in registers and accumulates dK^T and dV^T.
+// For each listed Q-tile of 64 rows and each query head of the group, Q, dO,
+// LSE and D are staged in LDS (double-buffered); Q^T and dO^T come from the
+// same tiles by transposed reads.  Each 64-row tile is processed as two
+// 32-row halves:
+//   S = Q K^T, dP = dO V^T, P = exp2(S c - lse2), dS = P (dP - D)
+//   dV^T += dO^T P,  dK^T += Q^T dS
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  using T = Tile64<D>;
-  constexpr int NP = T::NP, TP = T::TP;
-  __shared__ __attribute__((aligned(16))) bf16 sQ[2][64 * NP];
-  __shared__ __attribute__((aligned(16))) bf16 sQT[2][D * TP];
-  __shared__ __attribute__((aligned(16))) bf16 sO[2][64 * NP];
-  __shared__ __attribute__((aligned(16))) bf16 sOT[2][D * TP];
-  __shared__ __attribute__((aligned(16))) float sL[2][64];
-  __shared__ __attribute__((aligned(16))) float sDv[2][64];
+  using LQ = Lds<D, true>;
+  constexpr int OFF_DO = LQ::BYTES, OFF_L = 2 * LQ::BYTES, OFF_D = OFF_L + 256;
+  constexpr int STAGE = OFF_D + 256;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -91,6 +91,12 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   }
   const int4 cb = key_ok ? a.m.colb[key] : make_int4(0, S, 0, 0);
   const int kblk = (a.m.bm_heads && key_ok) ? a.m.kblk[key] : 0;
+  int toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    toff[db][0] = tr_off<LQ>(lane, db, 0);
+    toff[db][1] = tr_off<LQ>(lane, db, 1);
+  }
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 
   const uint32_t *list = a.blist + item.z;
   const int nst = item.w * G;
-  T tq, tdo;
+  Stage64<D> tq, tdo;
   float lval = 0.f;
 
   auto load_stage = [&](int st) {
@@ -115,18 +121,15 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       lval = tid < 64 ? a.lse[idx] * kLog2e : a.dws[idx];
     }
   };
-  auto store_stage = [&](int buf) {
-    tq.store_nat(sQ[buf]);
-    tq.store_trans(sQT[buf]);
-    tdo.store_nat(sO[buf]);
-    tdo.store_trans(sOT[buf]);
-    if (tid < 64) sL[buf][tid] = lval;
-    else if (tid < 128) sDv[buf][tid - 64] = lval;
+  auto store_stage = [&](char *stg) {
+    tq.template store<LQ>(stg);
+    tdo.template store<LQ>(stg + OFF_DO);
+    if (tid < 128) reinterpret_cast<float *>(stg + OFF_L)[tid] = lval;  // lse2 then D
   };
 
   if (nst > 0) {
     load_stage(0);
-    store_stage(0);
+    store_stage(smem);
   }
   __syncthreads();
 
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     const int qt = (int)(ent & 0x7fffffffu);
     const bool partial = (ent >> 31) != 0;
     const int h = kvh * G + g;
-    const int buf = st & 1;
+    char *stage = smem + (st & 1) * STAGE;
     if (st + 1 < nst) load_stage(st + 1);
 
     uint32_t mw[2] = {0xffffffffu, 0xffffffffu};
@@ -150,50 +153,44 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       mw[1] = (uint32_t)(sh >> 32);
     }
     if (active) {
-      const bf16 *q_s = sQ[buf], *qt_s = sQT[buf], *o_s = sO[buf], *ot_s = sOT[buf];
-      f32x16 s[2], dp[2];
+      const float *sl = reinterpret_cast<const float *>(stage + OFF_L);
+      const float *sd = reinterpret_cast<const float *>(stage + OFF_D);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = (f32x16){};
-        dp[qb] = (f32x16){};
+      for (int qh = 0; qh < 2; ++qh) {
+        f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(q_s + (qb * 32 + ln) * NP + ks * 16 + hh * 8);
-          s[qb] = mfma32(aq, kv[ks], s[qb]);
-          const bf16x8 ao = *reinterpret_cast<const bf16x8 *>(o_s + (qb * 32 + ln) * NP + ks * 16 + hh * 8);
-          dp[qb] = mfma32(ao, vv[ks], dp[qb]);
+          s = mfma32(lds_rows<LQ>(stage, qh * 32 + ln, ks * 32 + hh * 16), kv[ks], s);
+          dp = mfma32(lds_rows<LQ>(stage + OFF_DO, qh * 32 + ln, ks * 32 + hh * 16), vv[ks], dp);
         }
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&sL[buf][qb * 32 + 8 * c + 4 * hh]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sDv[buf][qb * 32 + 8 * c + 4 * hh]);
+          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sl + qh * 32 + 8 * c + 4 * hh);
+          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sd + qh * 32 + 8 * c + 4 * hh);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int r = 4 * c + j;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], sl2, -l4[j]));
-            if (partial) p = keep_or(mw[qb], 8 * c + j, p, 0.f);
-            s[qb][r] = p;
-            dp[qb][r] = p * (dp[qb][r] - d4[j]);
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[j]));
+            if (partial) p = keep_or(mw[qh], 8 * c + j, p, 0.f);
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[j]);
           }
         }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8 pb = c_to_b(s, t);
-        const bf16x8 dsb = c_to_b(dp, t);
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const bf16x8 pb = c_to_b(s, t2);
+          const bf16x8 dsb = c_to_b(dp, t2);
+          const int tb = (2 * qh + t2) * 16 * LQ::PITCH;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 aot = *reinterpret_cast<const bf16x8 *>(ot_s + (db * 32 + ln) * TP + t * 16 + hh * 8);
-          dv[db] = mfma32(aot, pb, dv[db]);
-          const bf16x8 aqt = *reinterpret_cast<const bf16x8 *>(qt_s + (db * 32 + ln) * TP + t * 16 + hh * 8);
-          dk[db] = mfma32(aqt, dsb, dk[db]);
+          for (int db = 0; db < DB; ++db) {
+            dv[db] = mfma32(lds_tr(stage + OFF_DO, toff[db][0] + tb, toff[db][1] + tb), pb, dv[db]);
+            dk[db] = mfma32(lds_tr(stage, toff[db][0] + tb, toff[db][1] + tb), dsb, dk[db]);
+          }
         }
       }
     }
 
-    if (st + 1 < nst) store_stage(buf ^ 1);
+    if (st + 1 < nst) store_stage(smem + ((st + 1) & 1) * STAGE);
     __syncthreads();
   }
 
@@ -205,31 +202,31 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int d0 = db * 32 + 8 * c + 4 * hh;
-        bf16x2 k0 = __builtin_convertvector((f32x2){dk[db][4 * c] * sc, dk[db][4 * c + 1] * sc}, bf16x2);
-        bf16x2 k1 = __builtin_convertvector((f32x2){dk[db][4 * c + 2] * sc, dk[db][4 * c + 3] * sc}, bf16x2);
-        *reinterpret_cast<bf16x4 *>(a.dk + off + d0) = __builtin_shufflevector(k0, k1, 0, 1, 2, 3);
-        bf16x2 v0 = __builtin_convertvector((f32x2){dv[db][4 * c], dv[db][4 * c + 1]}, bf16x2);
-        bf16x2 v1 = __builtin_convertvector((f32x2){dv[db][4 * c + 2], dv[db][4 * c + 3]}, bf16x2);
-        *reinterpret_cast<bf16x4 *>(a.dv + off + d0) = __builtin_shufflevector(v0, v1, 0, 1, 2, 3);
+        *reinterpret_cast<bf16x4 *>(a.dk + off + d0) = __builtin_shufflevector(
+            cvt2(dk[db][4 * c] * sc, dk[db][4 * c + 1] * sc),
+            cvt2(dk[db][4 * c + 2] * sc, dk[db][4 * c + 3] * sc), 0, 1, 2, 3);
+        *reinterpret_cast<bf16x4 *>(a.dv + off + d0) = __builtin_shufflevector(
+            cvt2(dv[db][4 * c], dv[db][4 * c + 1]), cvt2(dv[db][4 * c + 2], dv[db][4 * c + 3]),
+            0, 1, 2, 3);
       }
   }
 }
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per forward work item (Q-tile, head group); same lane
-// ownership as the forward.  K (natural and transposed) and V (natural) tiles
-// are staged in LDS, double-buffered.  Per K-tile:
+// ownership as the forward.  K and V tiles of 64 keys are staged in LDS
+// (natural layout, double-buffered); K^T comes from the K tile by transposed
+// reads.  Each K-tile is processed as two 32-key halves:
 //   S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - D),  dQ^T += K^T dS^T
 // ---------------------------------------------------------------------------
 template <int D, int HG>
-__global__ __launch_bounds__(256, 1) void attn_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  using T = Tile64<D>;
-  constexpr int NP = T::NP, TP = T::TP;
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][64 * NP];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][64 * NP];
-  __shared__ __attribute__((aligned(16))) bf16 sKT[2][D * TP];
+  using LK = Lds<D, true>;
+  using LV = Lds<D, false>;
+  constexpr int STAGE = LK::BYTES + LV::BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ln = lane & 31, hh = lane >> 5;
@@ -263,6 +260,12 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(BwdArgs a) {
   const int4 rb = row_ok ? a.m.rowb[row] : make_int4(0, 0, 0, 0);
   const int hm = bitmap_head(a.m.bm_heads, h, a.Hq, a.G);
   const int qb = (a.m.bm_heads && row_ok) ? a.m.qblk[row] : 0;
+  int koff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    koff[db][0] = tr_off<LK>(lane, db, 0);
+    koff[db][1] = tr_off<LK>(lane, db, 1);
+  }
 
   f32x16 dq[DB];
 #pragma unroll
@@ -271,14 +274,13 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(BwdArgs a) {
 
   const uint32_t *list = a.flist + item.z;
   const int n = item.w;
-  T tk, tv;
+  Stage64<D> tk, tv;
   if (n > 0) {
     const int kt = (int)(list[0] & 0x7fffffffu);
     tk.load(kbase, ldk, kt * 64, S);
     tv.load(vbase, ldk, kt * 64, S);
-    tk.store_nat(sK[0]);
-    tk.store_trans(sKT[0]);
-    tv.store_nat(sV[0]);
+    tk.template store<LK>(smem);
+    tv.template store<LV>(smem + LK::BYTES);
   }
   __syncthreads();
 
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(BwdArgs a) {
     const uint32_t ent = list[e];
     const int kt = (int)(ent & 0x7fffffffu);
     const bool partial = (ent >> 31) != 0;
-    const int buf = e & 1;
+    char *stage = smem + (e & 1) * STAGE;
     if (e + 1 < n) {
       const int nkt = (int)(list[e + 1] & 0x7fffffffu);
       tk.load(kbase, ldk, nkt * 64, S);
@@ -302,42 +304,34 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(BwdArgs a) {
       mw[1] = (uint32_t)(sh >> 32);
     }
     if (active) {
-      const bf16 *k_s = sK[buf], *v_s = sV[buf], *kt_s = sKT[buf];
-      f32x16 s[2], dp[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = (f32x16){};
-        dp[kb] = (f32x16){};
+      for (int kh = 0; kh < 2; ++kh) {
+        f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(k_s + (kb * 32 + ln) * NP + ks * 16 + hh * 8);
-          s[kb] = mfma32(ak, qv[ks], s[kb]);
-          const bf16x8 av = *reinterpret_cast<const bf16x8 *>(v_s + (kb * 32 + ln) * NP + ks * 16 + hh * 8);
-          dp[kb] = mfma32(av, dov[ks], dp[kb]);
+          s = mfma32(lds_rows<LK>(stage, kh * 32 + ln, ks * 32 + hh * 16), qv[ks], s);
+          dp = mfma32(lds_rows<LV>(stage + LK::BYTES, kh * 32 + ln, ks * 32 + hh * 16), dov[ks], dp);
         }
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -lse2));
-          if (partial) p = keep_or(mw[kb], 8 * (r >> 2) + (r & 3), p, 0.f);
-          dp[kb][r] = p * (dp[kb][r] - Dr);
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2));
+          if (partial) p = keep_or(mw[kh], 8 * (r >> 2) + (r & 3), p, 0.f);
+          dp[r] = p * (dp[r] - Dr);
         }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8 dsb = c_to_b(dp, t);
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const bf16x8 dsb = c_to_b(dp, t2);
+          const int tb = (2 * kh + t2) * 16 * LK::PITCH;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 akt = *reinterpret_cast<const bf16x8 *>(kt_s + (db * 32 + ln) * TP + t * 16 + hh * 8);
-          dq[db] = mfma32(akt, dsb, dq[db]);
+          for (int db = 0; db < DB; ++db)
+            dq[db] = mfma32(lds_tr(stage, koff[db][0] + tb, koff[db][1] + tb), dsb, dq[db]);
         }
       }
     }
     if (e + 1 < n) {
-      tk.store_nat(sK[buf ^ 1]);
-      tk.store_trans(sKT[buf ^ 1]);
-      tv.store_nat(sV[buf ^ 1]);
+      char *next = smem + ((e + 1) & 1) * STAGE;
+      tk.template store<LK>(next);
+      tv.template store<LV>(next + LK::BYTES);
     }
     __syncthreads();
   }
@@ -350,9 +344,9 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int d0 = db * 32 + 8 * c + 4 * hh;
-        bf16x2 p0 = __builtin_convertvector((f32x2){dq[db][4 * c] * sc, dq[db][4 * c + 1] * sc}, bf16x2);
-        bf16x2 p1 = __builtin_convertvector((f32x2){dq[db][4 * c + 2] * sc, dq[db][4 * c + 3] * sc}, bf16x2);
-        *reinterpret_cast<bf16x4 *>(qrow + d0) = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+        *reinterpret_cast<bf16x4 *>(qrow + d0) = __builtin_shufflevector(
+            cvt2(dq[db][4 * c] * sc, dq[db][4 * c + 1] * sc),
+            cvt2(dq[db][4 * c + 2] * sc, dq[db][4 * c + 3] * sc), 0, 1, 2, 3);
       }
   }
 }

@@ -9,12 +9,13 @@
 // One workgroup = 4 waves = one work item: (Q-tile, group of HG query heads
 // that share a KV head).  Wave w owns 32 query rows of head h0 + w % HG; lane
 // l owns row 32*(w / HG) + l % 32, and the two lane halves split each K-tile's
-// 64 keys.  K (natural) and V (transposed) tiles of 64 keys are staged in LDS,
-// double-buffered, and shared by all heads of the item.  Per K-tile:
-//   S^T = K Q^T                  (MFMA, K from LDS, Q^T in registers)
+// 64 keys.  K and V tiles of 64 keys are staged in LDS (natural layout,
+// double-buffered) and shared by all heads of the item.  Per K-tile:
+//   S^T = K Q^T                  (MFMA; K row reads, Q^T in registers)
 //   mask (partial tiles only)    (per-lane 64-bit allowed-key word)
-//   m, l update                  (running max kept stale within the slack)
-//   O^T += V^T P^T               (MFMA, V^T from LDS, P^T from registers)
+//   m update                     (running max kept stale within the slack)
+//   P^T = exp2(S^T c - m) -> bf16, l += sum P (bf16 dot products)
+//   O^T += V^T P^T               (MFMA; V^T by transposed LDS reads)
 #include "kernels.hpp"
 
 namespace lcm {
@@ -23,10 +24,10 @@ template <int D, int HG>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int KS = D / 16;  // k-steps of QK^T
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  using T = Tile64<D>;
-  constexpr int NP = T::NP, TP = T::TP;
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][64 * NP];
-  __shared__ __attribute__((aligned(16))) bf16 sVT[2][D * TP];
+  using LK = Lds<D, false>;
+  using LV = Lds<D, true>;
+  constexpr int STAGE = LK::BYTES + LV::BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ln = lane & 31, hh = lane >> 5;
@@ -53,6 +54,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int4 rb = row_ok ? a.m.rowb[row] : make_int4(0, 0, 0, 0);
   const int hm = bitmap_head(a.m.bm_heads, h, a.Hq, a.G);
   const int qb = (a.m.bm_heads && row_ok) ? a.m.qblk[row] : 0;
+  int voff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    voff[db][0] = LK::BYTES + tr_off<LV>(lane, db, 0);
+    voff[db][1] = LK::BYTES + tr_off<LV>(lane, db, 1);
+  }
 
   f32x16 o[DB];
 #pragma unroll
@@ -62,13 +69,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 
   const uint32_t *list = a.list + item.z;
   const int n = item.w;
-  T tk, tv;
+  Stage64<D> tk, tv;
   if (n > 0) {
     const int kt = (int)(list[0] & 0x7fffffffu);
     tk.load(kbase, ldk, kt * 64, S);
     tv.load(vbase, ldk, kt * 64, S);
-    tk.store_nat(sK[0]);
-    tv.store_trans(sVT[0]);
+    tk.template store<LK>(smem);
+    tv.template store<LV>(smem + LK::BYTES);
   }
   __syncthreads();
 
@@ -76,7 +83,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     const uint32_t ent = list[e];
     const int kt = (int)(ent & 0x7fffffffu);
     const bool partial = (ent >> 31) != 0;
-    const int buf = e & 1;
+    char *stage = smem + (e & 1) * STAGE;
     if (e + 1 < n) {
       const int nkt = (int)(list[e + 1] & 0x7fffffffu);
       tk.load(kbase, ldk, nkt * 64, S);
@@ -93,17 +100,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       mhi = (uint32_t)(sh >> 32);
     }
     if (active) {
-      const bf16 *k_s = sK[buf];
-      const bf16 *vt_s = sVT[buf];
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = (f32x16){};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8 *>(k_s + (kb * 32 + ln) * NP + ks * 16 + hh * 8);
-          s[kb] = mfma32(av, qv[ks], s[kb]);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+          s[kb] = mfma32(lds_rows<LK>(stage, kb * 32 + ln, ks * 32 + hh * 16), qv[ks], s[kb]);
       }
       if (partial) {
 #pragma unroll
@@ -115,9 +118,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       }
       float mx = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * sl2);
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[0][r]), s[1][r]);
+      mx = max_halves(mx);
+      const float m_new = __builtin_fmaxf(m_run, mx * sl2);
       if (__ballot(m_new > m_run + kRescaleSlack) != 0ull) {
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
@@ -127,35 +130,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
       }
-      float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -m_run));
-          s[kb][r] = p;
-          ls += p;
-        }
-      l_run += ls;
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -m_run));
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const bf16x8 pb = c_to_b(s, t);
+        const bf16x8 pb = c_to_b(s[t >> 1], t & 1);
+        l_run = sum8(pb, l_run);
+        const int toff = t * 16 * LV::PITCH;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8 *>(vt_s + (db * 32 + ln) * TP + t * 16 + hh * 8);
-          o[db] = mfma32(av, pb, o[db]);
-        }
+        for (int db = 0; db < DB; ++db)
+          o[db] = mfma32(lds_tr(stage, voff[db][0] + toff, voff[db][1] + toff), pb, o[db]);
       }
     }
 
     if (e + 1 < n) {
-      tk.store_nat(sK[buf ^ 1]);
-      tv.store_trans(sVT[buf ^ 1]);
+      char *next = smem + ((e + 1) & 1) * STAGE;
+      tk.template store<LK>(next);
+      tv.template store<LV>(next + LK::BYTES);
     }
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     bf16 *orow = a.o + ((int64_t)b * S + row) * ldq + (int64_t)h * D;
@@ -164,13 +163,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int d0 = db * 32 + 8 * c + 4 * hh;
-        bf16x2 p0 = __builtin_convertvector((f32x2){o[db][4 * c] * inv, o[db][4 * c + 1] * inv}, bf16x2);
-        bf16x2 p1 = __builtin_convertvector((f32x2){o[db][4 * c + 2] * inv, o[db][4 * c + 3] * inv}, bf16x2);
-        *reinterpret_cast<bf16x4 *>(orow + d0) = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+        *reinterpret_cast<bf16x4 *>(orow + d0) = __builtin_shufflevector(
+            cvt2(o[db][4 * c] * inv, o[db][4 * c + 1] * inv),
+            cvt2(o[db][4 * c + 2] * inv, o[db][4 * c + 3] * inv), 0, 1, 2, 3);
       }
     if (hh == 0)
       a.lse[((int64_t)b * a.Hq + h) * S + row] =
-          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+          l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
   }
 }
 

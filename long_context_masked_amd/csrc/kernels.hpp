@@ -5,15 +5,18 @@
 //   A (32 x 16): lane l holds A[l % 32][8h .. 8h+7]
 //   B (16 x 32): lane l holds B[8h .. 8h+7][l % 32]
 //   C (32 x 32): lane l, register r holds C[8(r/4) + 4h + (r%4)][l % 32]
-// Every kernel computes transposed products (C = rows of the *other*
-// operand x columns of "its" rows) so that one lane owns one query row (or,
-// in the dK/dV pass, one key) and the softmax statistics of that row stay in
-// the lane.  A C result can then feed the next product directly as a B
+// Every kernel computes transposed products so that one lane owns one query
+// row (forward, dQ) or one key (dK/dV) and the per-row softmax statistics
+// stay in the lane.  A C result then feeds the next product directly as a B
 // operand after an fp32 -> bf16 conversion, provided the partner A operand
 // lists its k index in the order C hands it over: for the 16-wide k-step t
-// of a 64-row tile the lane half h holds rows 16t + 4h + {0..3} and
-// 16t + 8 + 4h + {0..3}.  Transposed tiles in LDS are stored in that order
-// (perm16 below) so that the partner operand is one contiguous 16-byte read.
+// of a 64-row tile, lane half h holds rows 16t + 4h + {0..3} and
+// 16t + 8 + 4h + {0..3}.  That partner operand is always a tile stored in
+// natural [row][d] layout in LDS and read transposed with
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane l receives element
+// j from the address given by lane 4j + l/4, at 16-bit offset l % 4.  Giving
+// source lane 4j + q the address of row (base + j), column (16-block + 4q)
+// hands lane l the four rows base..base+3 at column (16-block + l).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,9 +28,11 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -43,28 +48,43 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ bf16x2 cvt2(float a, float b) {
+  return __builtin_convertvector((f32x2){a, b}, bf16x2);
+}
+
 __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4,
                                         float a5, float a6, float a7) {
-  bf16x2 p0 = __builtin_convertvector((f32x2){a0, a1}, bf16x2);
-  bf16x2 p1 = __builtin_convertvector((f32x2){a2, a3}, bf16x2);
-  bf16x2 p2 = __builtin_convertvector((f32x2){a4, a5}, bf16x2);
-  bf16x2 p3 = __builtin_convertvector((f32x2){a6, a7}, bf16x2);
-  bf16x4 lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
-  bf16x4 hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  const bf16x4 lo = __builtin_shufflevector(cvt2(a0, a1), cvt2(a2, a3), 0, 1, 2, 3);
+  const bf16x4 hi = __builtin_shufflevector(cvt2(a4, a5), cvt2(a6, a7), 0, 1, 2, 3);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// The B operand for k-step t of a 64-row tile held as two C blocks c[0..1].
-__device__ __forceinline__ bf16x8 c_to_b(const f32x16 *c, int t) {
-  const f32x16 &x = c[t >> 1];
-  const int o = (t & 1) * 8;
+// The B operand of k-step t (t = 0, 1) held in one C block (registers 8t..8t+7).
+__device__ __forceinline__ bf16x8 c_to_b(const f32x16 &x, int t) {
+  const int o = t * 8;
   return pack8(x[o + 0], x[o + 1], x[o + 2], x[o + 3], x[o + 4], x[o + 5], x[o + 6], x[o + 7]);
 }
 
-// Position of row k (0..63) of a tile inside a transposed LDS tile: within
-// each 16-row group the two middle 4-row groups are swapped.
-__device__ __forceinline__ int perm16(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// Sum of the eight bf16 values of a B operand, accumulated into acc.
+__device__ __forceinline__ float sum8(bf16x8 v, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+}
+
+// max over both lane halves (lanes l and l ^ 32 hold the same row / key).
+__device__ __forceinline__ float max_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Bits [lo, hi) of a 64-bit word, clipped to [0, 64).
@@ -76,23 +96,64 @@ __device__ __forceinline__ uint64_t range64(int lo, int hi) {
   return top & ~((1ull << lo) - 1ull);
 }
 
-// Keep s where bit `bit` of `m` is set, else -inf / 0.
-__device__ __forceinline__ float keep_or(uint32_t m, int bit, float s, float other) {
-  return ((m >> bit) & 1u) ? s : other;
+// x where bit `bit` of m is set, else `other` (two VALU ops: a sign-extended
+// one-bit field extract and a bitfield insert).
+__device__ __forceinline__ float keep_or(uint32_t m, int bit, float x, float other) {
+  const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)m, bit, 1);
+  return __uint_as_float((sel & __float_as_uint(x)) | (~sel & __float_as_uint(other)));
 }
 
 // --------------------------------------------------------------------------
-// 64-row tile staging.  256 threads; thread t owns 16-byte chunk c = t % CPR
-// (elements 8c..8c+7 of d) of RPT consecutive rows starting at RPT*(t/CPR).
-// From these registers a tile can be written to LDS in natural [row][d]
-// layout (pitch D+8) and/or transposed [d][perm16(row)] layout (pitch 72).
+// LDS tiles of 64 rows x D bf16 in natural [row][d] layout.
+//   SWZ = false: row pitch 2D+16 bytes, conflict-free 16-byte row reads.
+//   SWZ = true:  row pitch 2D+64 bytes with 16-byte chunks XOR-swizzled by
+//                the row; conflict-free for row reads, transposed reads and
+//                the staging writes alike.
 // --------------------------------------------------------------------------
+template <int D, bool SWZ>
+struct Lds {
+  static constexpr int PITCH = SWZ ? 2 * D + 64 : 2 * D + 16;
+  static constexpr int BYTES = 64 * PITCH;
+  static constexpr int NCH = (2 * D / 16) < 16 ? (2 * D / 16) : 16;
+  __device__ static __forceinline__ int off(int row, int cb) {
+    return row * PITCH + (SWZ ? (cb ^ ((row & (NCH - 1)) << 4)) : cb);
+  }
+};
+
+// A operand from a natural tile: rows row..row+31 by lane, 16 elements of d
+// starting at byte cb (lane half h adds 16 bytes).
+template <class L>
+__device__ __forceinline__ bf16x8 lds_rows(const char *base, int row, int cb) {
+  return *reinterpret_cast<const bf16x8 *>(base + L::off(row, cb));
+}
+
+// Per-lane byte offsets of the transposed reads of one d-block db (two
+// halves: rows +0 and +8 of a 16-row k-step); add 16 * t * PITCH for k-step t.
+template <class L>
+__device__ __forceinline__ int tr_off(int lane, int db, int half) {
+  const int row = 8 * half + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int cb = db * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  return L::off(row, cb);
+}
+
+// A operand (m = d within a 32-block, k = 16 tile rows of k-step t in C order)
+// from a natural tile, via two transposed reads at precomputed offsets.
+__device__ __forceinline__ bf16x8 lds_tr(const char *base, int off0, int off1) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)((__attribute__((address_space(3))) char *)base + off0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)((__attribute__((address_space(3))) char *)base + off1));
+  const s16x4 lo = a, hi = b;
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 64-row tile staging through registers.  256 threads; thread t owns 16-byte
+// chunk c = t % CPR of RPT consecutive rows starting at RPT * (t / CPR):
+// global loads are coalesced along d, LDS writes are whole rows.
 template <int D>
-struct Tile64 {
-  static constexpr int CPR = D / 8;          // 16-byte chunks per row
-  static constexpr int RPT = 64 * CPR / 256; // rows per thread (4 or 2)
-  static constexpr int NP = D + 8;           // natural pitch (elements)
-  static constexpr int TP = 64 + 8;          // transposed pitch (elements)
+struct Stage64 {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPT = 64 * CPR / 256;
   uint4 r[RPT];
 
   // rows row0 + [0, 64) of a [.., ld] bf16 matrix; rows >= nrows read as 0
@@ -109,37 +170,13 @@ struct Tile64 {
     }
   }
 
-  __device__ __forceinline__ void store_nat(bf16 *s) const {
+  template <class L>
+  __device__ __forceinline__ void store(char *s) const {
     const int t = threadIdx.x;
     const int c = t % CPR, g = t / CPR;
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-      *reinterpret_cast<uint4 *>(s + (g * RPT + i) * NP + c * 8) = r[i];
-  }
-
-  __device__ __forceinline__ void store_trans(bf16 *s) const {
-    const int t = threadIdx.x;
-    const int c = t % CPR, g = t / CPR;
-    const int pos = perm16(g * RPT);  // RPT rows stay contiguous under perm16
-    const uint32_t *w[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) w[i] = reinterpret_cast<const uint32_t *>(&r[i]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) * 16;
-      uint32_t lo16[RPT];
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) lo16[i] = (w[i][e >> 1] >> sh) & 0xffffu;
-      bf16 *dst = s + (c * 8 + e) * TP + pos;
-      if constexpr (RPT == 4) {
-        uint2 v;
-        v.x = lo16[0] | (lo16[1] << 16);
-        v.y = lo16[2] | (lo16[3] << 16);
-        *reinterpret_cast<uint2 *>(dst) = v;
-      } else {
-        *reinterpret_cast<uint32_t *>(dst) = lo16[0] | (lo16[1] << 16);
-      }
-    }
+      *reinterpret_cast<uint4 *>(s + L::off(g * RPT + i, c * 16)) = r[i];
   }
 };
 
