@@ -168,8 +168,8 @@ def main():
                                  P(tt["o"].data_ptr()), P(tt["lse"].data_ptr()), sp))
             if record:
                 ev[1].record(stream)
-            L.check(lib.attn_bwd_preprocess(h, P(tt["o"].data_ptr()), P(tt["do"].data_ptr()),
-                                            P(wptr), nws, sp))
+            L.check(lib.attn_bwd_preprocess(h, P(tt["o"].data_ptr()), P(tt["lse"].data_ptr()),
+                                            P(tt["do"].data_ptr()), P(wptr), nws, sp))
             if record:
                 ev[2].record(stream)
             L.check(lib.attn_bwd_dkdv(h, P(tt["q"].data_ptr()), P(tt["k"].data_ptr()), P(tt["v"].data_ptr()),
@@ -212,7 +212,7 @@ def main():
         for key in alg:
             alg[key] += KERNEL_FLOPS_PER_PAIR[key] * d * r["nnz"] * n
         Hq = 64
-        pre_bytes += 2.0 * r["S"] * Hq * d * 2 * n + r["S"] * Hq * 4 * n
+        pre_bytes += 2.0 * r["S"] * Hq * d * 2 * n + 3.0 * r["S"] * Hq * 4 * n
         ffl, bfl = 4.0 * d * r["nnz"], 10.0 * d * r["nnz"]
         eff_fwd += ffl * n
         eff_bwd += bfl * n

@@ -165,7 +165,8 @@ typedef struct {
 
 attn_status attn_plan_get_layout(const attn_plan *plan, attn_plan_layout *out);
 
-/* Bytes of device workspace attn_bwd needs (the per-row D = rowsum(dO*O)). */
+/* Bytes of device workspace attn_bwd needs: per (b, h, row) the fp32 values
+ * LSE * log2(e) and D = rowsum(dO * O), rows padded to a multiple of 64. */
 size_t attn_bwd_workspace_bytes(const attn_plan *plan);
 
 /*
@@ -179,7 +180,8 @@ attn_status attn_fwd(const attn_plan *plan, const void *q, const void *k,
 
 /*
  * Backward: dQ, dK, dV from Q, K, V, the forward's O and LSE, and dO.
- * Three launches on `stream`: D = rowsum(dO * O) into `ws`; a KV-split pass
+ * Three launches on `stream`: D = rowsum(dO * O) and LSE * log2(e) into
+ * `ws`; a KV-split pass
  * (one workgroup per K-tile and KV head) accumulating dK and dV; a Q-split
  * pass accumulating dQ = scale * sum_j dS_ij K_j (the row/column two-axis
  * split of FlashAttention-2, "core optimisations").  dK and dV of a KV head
@@ -195,13 +197,14 @@ attn_status attn_bwd(const attn_plan *plan, const void *q, const void *k,
  * The three stages of attn_bwd, callable one at a time on the same stream
  * and in this order (attn_bwd is exactly these three calls).  They exist so
  * that callers can interleave other work between stages and time them.
- *   attn_bwd_preprocess: ws <- D = rowsum(dO * O), fp32 [B, Hq, S].
+ *   attn_bwd_preprocess: ws <- LSE * log2(e) and D = rowsum(dO * O), fp32.
  *   attn_bwd_dkdv:       dK, dV from Q, K, V, LSE, dO and D in ws.
  *   attn_bwd_dq:         dQ from Q, K, V, LSE, dO and D in ws.
  * Arguments have the meaning and requirements given for attn_bwd.
  */
-attn_status attn_bwd_preprocess(const attn_plan *plan, const void *o, const void *dout,
-                                void *ws, size_t ws_bytes, attn_stream_t stream);
+attn_status attn_bwd_preprocess(const attn_plan *plan, const void *o, const float *lse,
+                                const void *dout, void *ws, size_t ws_bytes,
+                                attn_stream_t stream);
 attn_status attn_bwd_dkdv(const attn_plan *plan, const void *q, const void *k,
                           const void *v, const float *lse, const void *dout, void *dk,
                           void *dv, const void *ws, size_t ws_bytes, attn_stream_t stream);

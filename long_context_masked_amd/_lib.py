@@ -66,7 +66,7 @@ SIGNATURES = {
     "attn_bwd_workspace_bytes": (C.c_size_t, [C.c_void_p]),
     "attn_fwd": (C.c_int, [C.c_void_p] * 5 + [C.c_void_p, C.c_void_p]),
     "attn_bwd": (C.c_int, [C.c_void_p] * 11 + [C.c_size_t, C.c_void_p]),
-    "attn_bwd_preprocess": (C.c_int, [C.c_void_p] * 4 + [C.c_size_t, C.c_void_p]),
+    "attn_bwd_preprocess": (C.c_int, [C.c_void_p] * 5 + [C.c_size_t, C.c_void_p]),
     "attn_bwd_dkdv": (C.c_int, [C.c_void_p] * 9 + [C.c_size_t, C.c_void_p]),
     "attn_bwd_dq": (C.c_int, [C.c_void_p] * 8 + [C.c_size_t, C.c_void_p]),
     "attn_plan_destroy": (None, [C.c_void_p]),

@@ -126,7 +126,8 @@ BwdArgs bwd_args(const attn_plan *p, const void *q, const void *k, const void *v
   a.o = static_cast<const bf16 *>(o);
   a.dout = static_cast<const bf16 *>(dout);
   a.lse = lse;
-  a.dws = static_cast<float *>(const_cast<void *>(ws));
+  a.ws = static_cast<float *>(const_cast<void *>(ws));
+  a.S64 = (int)((p->shape.S + 63) / 64 * 64);
   a.dq = static_cast<bf16 *>(dq);
   a.dk = static_cast<bf16 *>(dk);
   a.dv = static_cast<bf16 *>(dv);
@@ -168,15 +169,17 @@ attn_status launched(hipError_t e, const char *what) {
 
 }  // namespace
 
-extern "C" attn_status attn_bwd_preprocess(const attn_plan *p, const void *o, const void *dout,
-                                           void *ws, size_t ws_bytes, attn_stream_t stream) {
+extern "C" attn_status attn_bwd_preprocess(const attn_plan *p, const void *o, const float *lse,
+                                           const void *dout, void *ws, size_t ws_bytes,
+                                           attn_stream_t stream) {
   clear_error();
   LCM_CHECK(check_plan(p));
   LCM_CHECK(check_tensor(o, "o", 16));
+  LCM_CHECK(check_tensor(lse, "lse", 4));
   LCM_CHECK(check_tensor(dout, "dout", 16));
   LCM_CHECK(check_ws(p, ws, ws_bytes));
   if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
-  const BwdArgs a = bwd_args(p, nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr,
+  const BwdArgs a = bwd_args(p, nullptr, nullptr, nullptr, o, lse, dout, nullptr, nullptr,
                              nullptr, ws);
   (void)hipGetLastError();
   return launched(launch_bwd_pre(a, (int)p->shape.d, (int)p->shape.B,

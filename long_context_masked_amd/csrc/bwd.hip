@@ -1,4 +1,4 @@
-// Backward kernels: D = rowsum(dO * O), a KV-split pass for dK/dV and a
+// Backward kernels: a preprocess pass, a KV-split pass for dK/dV and a
 // Q-split pass for dQ.
 //
 // Method ("FlashAttention vs. RingAttention", dtcms, FlashAttention-2 "core
@@ -11,8 +11,10 @@
 //
 // With c = scale * log2(e) and lse2 = LSE * log2(e):
 //   P  = exp2(c * Q K^T - lse2)          (masked entries 0)
-//   dP = dO V^T,  dS = P * (dP - D)
+//   dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O)
 //   dV = P^T dO,  dK = scale * dS^T Q,  dQ = scale * dS K
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace lcm {
@@ -20,19 +22,32 @@ namespace lcm {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// D[b, h, s] = sum_d dO[b, s, h, d] * O[b, s, h, d] (bf16 inputs, fp32 sum).
+// Workspace rows of (b, h): lse2 at ws + 2 (b Hq + h) S64, D right after.
+__device__ __forceinline__ int64_t ws_row0(int b, int h, int Hq, int S64) {
+  return 2 * ((int64_t)b * Hq + h) * S64;
+}
+
+// ws <- {lse * log2(e), D = sum_d dO * O} per (b, h, row); rows in [S, S64)
+// get zeros.  One group of D/8 lanes per row; the grid covers B * S64 * Hq
+// rows in [b][s][h] order.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const bf16 *dout,
-                                                           float *dws, int S, int Hq,
-                                                           int64_t nrows) {
+                                                           const float *lse, float *ws, int S,
+                                                           int S64, int Hq, int64_t nrows) {
   constexpr int CPR = D / 8;
   constexpr int RPB = 256 / CPR;
   const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
   const int c = threadIdx.x % CPR;
+  const int h = (int)(r % Hq);
+  const int64_t bs = r / Hq;
+  const int b = (int)(bs / S64);
+  const int s = (int)(bs % S64);
+  const bool real = r < nrows && s < S;
   float acc = 0.f;
-  if (r < nrows) {
-    const uint4 x = *reinterpret_cast<const uint4 *>(o + r * D + c * 8);
-    const uint4 y = *reinterpret_cast<const uint4 *>(dout + r * D + c * 8);
+  if (real) {
+    const int64_t g = (((int64_t)b * S + s) * Hq + h) * D + c * 8;
+    const uint4 x = *reinterpret_cast<const uint4 *>(o + g);
+    const uint4 y = *reinterpret_cast<const uint4 *>(dout + g);
     acc = bf_lo(x.x) * bf_lo(y.x) + bf_hi(x.x) * bf_hi(y.x) + bf_lo(x.y) * bf_lo(y.y) +
           bf_hi(x.y) * bf_hi(y.y) + bf_lo(x.z) * bf_lo(y.z) + bf_hi(x.z) * bf_hi(y.z) +
           bf_lo(x.w) * bf_lo(y.w) + bf_hi(x.w) * bf_hi(y.w);
@@ -40,11 +55,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
 #pragma unroll
   for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (r < nrows && c == 0) {
-    const int64_t bs = r / Hq;
-    const int h = (int)(r % Hq);
-    const int64_t bb = bs / S;
-    const int s = (int)(bs % S);
-    dws[(bb * Hq + h) * S + s] = acc;
+    const int64_t w0 = ws_row0(b, h, Hq, S64);
+    ws[w0 + s] = real ? lse[((int64_t)b * Hq + h) * S + s] * kLog2e : 0.f;
+    ws[w0 + S64 + s] = acc;
   }
 }
 
@@ -53,9 +66,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
 // 32w .. 32w+31 of the tile (lane l: key 32w + l % 32), keeps K and V of
 // those keys as MFMA operands in registers and accumulates dK^T and dV^T.
 // For each listed Q-tile of 64 rows and each query head of the group, Q, dO,
-// LSE and D are staged in LDS (double-buffered); Q^T and dO^T come from the
-// same tiles by transposed reads.  Each 64-row tile is processed as two
-// 32-row halves:
+// lse2 and D are loaded straight into LDS (double-buffered); Q^T and dO^T
+// come from the same tiles by transposed reads.  Each 64-row tile is
+// processed as two 32-row halves:
 //   S = Q K^T, dP = dO V^T, P = exp2(S c - lse2), dS = P (dP - D)
 //   dV^T += dO^T P,  dK^T += Q^T dS
 // ---------------------------------------------------------------------------
@@ -63,10 +76,10 @@ template <int D>
 __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  using LQ = Lds<D, true>;
-  constexpr int OFF_DO = LQ::BYTES, OFF_L = 2 * LQ::BYTES, OFF_D = OFF_L + 256;
-  constexpr int STAGE = OFF_D + 256;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  using T = Tile<D>;
+  constexpr int OFF_DO = T::BYTES, OFF_L = 2 * T::BYTES, OFF_D = OFF_L + 256;
+  constexpr int STAGE = 2 * T::BYTES + 1024;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -91,11 +104,13 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   }
   const int4 cb = key_ok ? a.m.colb[key] : make_int4(0, S, 0, 0);
   const int kblk = (a.m.bm_heads && key_ok) ? a.m.kblk[key] : 0;
-  int toff[DB][2];
+  int roff[KS], toff[DB][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = row_off<D>(lane, ks);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    toff[db][0] = tr_off<LQ>(lane, db, 0);
-    toff[db][1] = tr_off<LQ>(lane, db, 1);
+    toff[db][0] = tr_off<D>(lane, db, 0);
+    toff[db][1] = tr_off<D>(lane, db, 1);
   }
 
   f32x16 dk[DB], dv[DB];
@@ -105,32 +120,28 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 
   const uint32_t *list = a.blist + item.z;
   const int nst = item.w * G;
-  Stage64<D> tq, tdo;
-  float lval = 0.f;
 
-  auto load_stage = [&](int st) {
+  // Loads of stage st into `stg`: the Q and dO tiles of head kvh*G + g and
+  // 64 rows each of lse2 and D (wave 0, lanes 0..31, 16 bytes per lane).
+  auto load_stage = [&](int st, char *stg) {
     const int e = st / G, g = st - e * G;
     const int qt = (int)(list[e] & 0x7fffffffu);
     const int h = kvh * G + g;
-    tq.load(a.q + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
-    tdo.load(a.dout + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
-    const int rr = qt * 64 + (tid & 63);
-    lval = 0.f;
-    if (tid < 128 && rr < S) {
-      const int64_t idx = ((int64_t)b * a.Hq + h) * S + rr;
-      lval = tid < 64 ? a.lse[idx] * kLog2e : a.dws[idx];
+    dma_tile<D>(stg, a.q + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
+    dma_tile<D>(stg + OFF_DO, a.dout + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
+    if (wave == 0 && lane < 32) {
+      const float *src = a.ws + ws_row0(b, h, a.Hq, a.S64) + (lane >> 4) * a.S64 + qt * 64 +
+                         (lane & 15) * 4;
+      __builtin_amdgcn_global_load_lds(
+          src,
+          (__attribute__((address_space(3))) void *)((__attribute__((address_space(3))) char *)stg +
+                                                      OFF_L),
+          16, 0, 0);
     }
   };
-  auto store_stage = [&](char *stg) {
-    tq.template store<LQ>(stg);
-    tdo.template store<LQ>(stg + OFF_DO);
-    if (tid < 128) reinterpret_cast<float *>(stg + OFF_L)[tid] = lval;  // lse2 then D
-  };
 
-  if (nst > 0) {
-    load_stage(0);
-    store_stage(smem);
-  }
+  if (nst > 0) load_stage(0, smem);
+  dma_wait();
   __syncthreads();
 
   for (int st = 0; st < nst; ++st) {
@@ -140,8 +151,10 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     const bool partial = (ent >> 31) != 0;
     const int h = kvh * G + g;
     char *stage = smem + (st & 1) * STAGE;
-    if (st + 1 < nst) load_stage(st + 1);
+    // the other buffer was last read before the previous barrier
+    if (st + 1 < nst) load_stage(st + 1, smem + ((st + 1) & 1) * STAGE);
 
+    // rows of this tile visible to the lane's key (all ones on full tiles)
     uint32_t mw[2] = {0xffffffffu, 0xffffffffu};
     bool active = true;
     if (partial) {
@@ -155,13 +168,20 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     if (active) {
       const float *sl = reinterpret_cast<const float *>(stage + OFF_L);
       const float *sd = reinterpret_cast<const float *>(stage + OFF_D);
+      const uint32_t sbase = lds_addr(stage);
+      uint32_t sa[DB][2];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        sa[db][0] = sbase + toff[db][0];
+        sa[db][1] = sbase + toff[db][1];
+      }
 #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
         f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s = mfma32(lds_rows<LQ>(stage, qh * 32 + ln, ks * 32 + hh * 16), kv[ks], s);
-          dp = mfma32(lds_rows<LQ>(stage + OFF_DO, qh * 32 + ln, ks * 32 + hh * 16), vv[ks], dp);
+          s = mfma32(lds_rows(stage, roff[ks] + qh * 32 * T::ROWB), kv[ks], s);
+          dp = mfma32(lds_rows(stage + OFF_DO, roff[ks] + qh * 32 * T::ROWB), vv[ks], dp);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -170,27 +190,44 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int r = 4 * c + j;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[j]));
-            if (partial) p = keep_or(mw[qh], 8 * c + j, p, 0.f);
+            const float p = keep_or(mw[qh], 8 * c + j,
+                                    __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[j])), 0.f);
             s[r] = p;
             dp[r] = p * (dp[r] - d4[j]);
           }
         }
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const bf16x8 pb = c_to_b(s, t2);
-          const bf16x8 dsb = c_to_b(dp, t2);
-          const int tb = (2 * qh + t2) * 16 * LQ::PITCH;
+        // dV^T += dO^T P and dK^T += Q^T dS, one 16-row step at a time; the
+        // transposed operands of a step are read while P and dS are converted.
+        auto step = [&](auto tc) {
+          constexpr int t = decltype(tc)::value;  // 16-row step within the tile
+          constexpr int toff = t * 16 * T::ROWB;
+          s16x4 x[4 * DB];
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            dv[db] = mfma32(lds_tr(stage + OFF_DO, toff[db][0] + tb, toff[db][1] + tb), pb, dv[db]);
-            dk[db] = mfma32(lds_tr(stage, toff[db][0] + tb, toff[db][1] + tb), dsb, dk[db]);
+            x[4 * db + 0] = tr_issue<toff + OFF_DO>(sa[db][0]);
+            x[4 * db + 1] = tr_issue<toff + OFF_DO>(sa[db][1]);
+            x[4 * db + 2] = tr_issue<toff>(sa[db][0]);
+            x[4 * db + 3] = tr_issue<toff>(sa[db][1]);
           }
+          const bf16x8 pb = c_to_b(s, t & 1);
+          const bf16x8 dsb = c_to_b(dp, t & 1);
+          tr_wait(x);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dv[db] = mfma32(tr_pair(x[4 * db], x[4 * db + 1]), pb, dv[db]);
+            dk[db] = mfma32(tr_pair(x[4 * db + 2], x[4 * db + 3]), dsb, dk[db]);
+          }
+        };
+        if (qh == 0) {
+          step(std::integral_constant<int, 0>{});
+          step(std::integral_constant<int, 1>{});
+        } else {
+          step(std::integral_constant<int, 2>{});
+          step(std::integral_constant<int, 3>{});
         }
       }
     }
-
-    if (st + 1 < nst) store_stage(smem + ((st + 1) & 1) * STAGE);
+    dma_wait();
     __syncthreads();
   }
 
@@ -214,19 +251,18 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per forward work item (Q-tile, head group); same lane
-// ownership as the forward.  K and V tiles of 64 keys are staged in LDS
-// (natural layout, double-buffered); K^T comes from the K tile by transposed
-// reads.  Each K-tile is processed as two 32-key halves:
+// ownership as the forward.  K and V tiles of 64 keys are loaded straight
+// into LDS (natural layout, double-buffered); K^T comes from the K tile by
+// transposed reads.  Each K-tile is processed as two 32-key halves:
 //   S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - D),  dQ^T += K^T dS^T
 // ---------------------------------------------------------------------------
 template <int D, int HG>
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  using LK = Lds<D, true>;
-  using LV = Lds<D, false>;
-  constexpr int STAGE = LK::BYTES + LV::BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  using T = Tile<D>;
+  constexpr int STAGE = 2 * T::BYTES;  // K tile, then V tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ln = lane & 31, hh = lane >> 5;
@@ -253,18 +289,20 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
   }
   float lse2 = 0.f, Dr = 0.f;
   if (row_ok) {
-    const int64_t idx = ((int64_t)b * a.Hq + h) * S + row;
-    lse2 = a.lse[idx] * kLog2e;
-    Dr = a.dws[idx];
+    const int64_t w0 = ws_row0(b, h, a.Hq, a.S64);
+    lse2 = a.ws[w0 + row];
+    Dr = a.ws[w0 + a.S64 + row];
   }
   const int4 rb = row_ok ? a.m.rowb[row] : make_int4(0, 0, 0, 0);
   const int hm = bitmap_head(a.m.bm_heads, h, a.Hq, a.G);
   const int qb = (a.m.bm_heads && row_ok) ? a.m.qblk[row] : 0;
-  int koff[DB][2];
+  int roff[KS], koff[DB][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = row_off<D>(lane, ks);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    koff[db][0] = tr_off<LK>(lane, db, 0);
-    koff[db][1] = tr_off<LK>(lane, db, 1);
+    koff[db][0] = tr_off<D>(lane, db, 0);
+    koff[db][1] = tr_off<D>(lane, db, 1);
   }
 
   f32x16 dq[DB];
@@ -274,14 +312,12 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
 
   const uint32_t *list = a.flist + item.z;
   const int n = item.w;
-  Stage64<D> tk, tv;
   if (n > 0) {
     const int kt = (int)(list[0] & 0x7fffffffu);
-    tk.load(kbase, ldk, kt * 64, S);
-    tv.load(vbase, ldk, kt * 64, S);
-    tk.template store<LK>(smem);
-    tv.template store<LV>(smem + LK::BYTES);
+    dma_tile<D>(smem, kbase, ldk, kt * 64, S);
+    dma_tile<D>(smem + T::BYTES, vbase, ldk, kt * 64, S);
   }
+  dma_wait();
   __syncthreads();
 
   for (int e = 0; e < n; ++e) {
@@ -291,8 +327,9 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
     char *stage = smem + (e & 1) * STAGE;
     if (e + 1 < n) {
       const int nkt = (int)(list[e + 1] & 0x7fffffffu);
-      tk.load(kbase, ldk, nkt * 64, S);
-      tv.load(vbase, ldk, nkt * 64, S);
+      char *next = smem + ((e + 1) & 1) * STAGE;
+      dma_tile<D>(next, kbase, ldk, nkt * 64, S);
+      dma_tile<D>(next + T::BYTES, vbase, ldk, nkt * 64, S);
     }
     uint32_t mw[2] = {0xffffffffu, 0xffffffffu};
     bool active = true;
@@ -304,35 +341,52 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
       mw[1] = (uint32_t)(sh >> 32);
     }
     if (active) {
+      const uint32_t sbase = lds_addr(stage);
+      uint32_t ka[DB][2];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        ka[db][0] = sbase + koff[db][0];
+        ka[db][1] = sbase + koff[db][1];
+      }
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s = mfma32(lds_rows<LK>(stage, kh * 32 + ln, ks * 32 + hh * 16), qv[ks], s);
-          dp = mfma32(lds_rows<LV>(stage + LK::BYTES, kh * 32 + ln, ks * 32 + hh * 16), dov[ks], dp);
+          s = mfma32(lds_rows(stage, roff[ks] + kh * 32 * T::ROWB), qv[ks], s);
+          dp = mfma32(lds_rows(stage + T::BYTES, roff[ks] + kh * 32 * T::ROWB), dov[ks], dp);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2));
-          if (partial) p = keep_or(mw[kh], 8 * (r >> 2) + (r & 3), p, 0.f);
+          const float p = keep_or(mw[kh], 8 * (r >> 2) + (r & 3),
+                                  __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2)), 0.f);
           dp[r] = p * (dp[r] - Dr);
         }
+        // dQ^T += K^T dS^T, one 16-key step at a time.
+        auto step = [&](auto tc) {
+          constexpr int t = decltype(tc)::value;  // 16-key step within the tile
+          constexpr int toff = t * 16 * T::ROWB;
+          s16x4 x[2 * DB];
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const bf16x8 dsb = c_to_b(dp, t2);
-          const int tb = (2 * kh + t2) * 16 * LK::PITCH;
+          for (int db = 0; db < DB; ++db) {
+            x[2 * db] = tr_issue<toff>(ka[db][0]);
+            x[2 * db + 1] = tr_issue<toff>(ka[db][1]);
+          }
+          const bf16x8 dsb = c_to_b(dp, t & 1);
+          tr_wait(x);
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-            dq[db] = mfma32(lds_tr(stage, koff[db][0] + tb, koff[db][1] + tb), dsb, dq[db]);
+          for (int db = 0; db < DB; ++db) dq[db] = mfma32(tr_pair(x[2 * db], x[2 * db + 1]), dsb, dq[db]);
+        };
+        if (kh == 0) {
+          step(std::integral_constant<int, 0>{});
+          step(std::integral_constant<int, 1>{});
+        } else {
+          step(std::integral_constant<int, 2>{});
+          step(std::integral_constant<int, 3>{});
         }
       }
     }
-    if (e + 1 < n) {
-      char *next = smem + ((e + 1) & 1) * STAGE;
-      tk.template store<LK>(next);
-      tv.template store<LV>(next + LK::BYTES);
-    }
+    dma_wait();
     __syncthreads();
   }
 
@@ -352,11 +406,15 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
 }
 
 hipError_t launch_bwd_pre(const BwdArgs &a, int d, int B, hipStream_t st) {
-  const int64_t nrows = (int64_t)B * a.S * a.Hq;
+  const int64_t nrows = (int64_t)B * a.S64 * a.Hq;
   const int rpb = 256 / (d / 8);
   const dim3 grid((unsigned)((nrows + rpb - 1) / rpb)), block(256);
-  if (d == 128) hipLaunchKernelGGL((attn_bwd_pre_kernel<128>), grid, block, 0, st, a.o, a.dout, a.dws, a.S, a.Hq, nrows);
-  else if (d == 64) hipLaunchKernelGGL((attn_bwd_pre_kernel<64>), grid, block, 0, st, a.o, a.dout, a.dws, a.S, a.Hq, nrows);
+  if (d == 128)
+    hipLaunchKernelGGL((attn_bwd_pre_kernel<128>), grid, block, 0, st, a.o, a.dout, a.lse, a.ws,
+                       a.S, a.S64, a.Hq, nrows);
+  else if (d == 64)
+    hipLaunchKernelGGL((attn_bwd_pre_kernel<64>), grid, block, 0, st, a.o, a.dout, a.lse, a.ws,
+                       a.S, a.S64, a.Hq, nrows);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -9,13 +9,15 @@
 // One workgroup = 4 waves = one work item: (Q-tile, group of HG query heads
 // that share a KV head).  Wave w owns 32 query rows of head h0 + w % HG; lane
 // l owns row 32*(w / HG) + l % 32, and the two lane halves split each K-tile's
-// 64 keys.  K and V tiles of 64 keys are staged in LDS (natural layout,
-// double-buffered) and shared by all heads of the item.  Per K-tile:
+// 64 keys.  K and V tiles of 64 keys are loaded straight into LDS (natural
+// layout, double-buffered) and shared by all heads of the item.  Per K-tile:
 //   S^T = K Q^T                  (MFMA; K row reads, Q^T in registers)
 //   mask (partial tiles only)    (per-lane 64-bit allowed-key word)
 //   m update                     (running max kept stale within the slack)
 //   P^T = exp2(S^T c - m) -> bf16, l += sum P (bf16 dot products)
 //   O^T += V^T P^T               (MFMA; V^T by transposed LDS reads)
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace lcm {
@@ -24,10 +26,9 @@ template <int D, int HG>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int KS = D / 16;  // k-steps of QK^T
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  using LK = Lds<D, false>;
-  using LV = Lds<D, true>;
-  constexpr int STAGE = LK::BYTES + LV::BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  using T = Tile<D>;
+  constexpr int STAGE = 2 * T::BYTES;  // K tile, then V tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ln = lane & 31, hh = lane >> 5;
@@ -54,11 +55,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int4 rb = row_ok ? a.m.rowb[row] : make_int4(0, 0, 0, 0);
   const int hm = bitmap_head(a.m.bm_heads, h, a.Hq, a.G);
   const int qb = (a.m.bm_heads && row_ok) ? a.m.qblk[row] : 0;
-  int voff[DB][2];
+  int koff[KS], voff[DB][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = row_off<D>(lane, ks);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    voff[db][0] = LK::BYTES + tr_off<LV>(lane, db, 0);
-    voff[db][1] = LK::BYTES + tr_off<LV>(lane, db, 1);
+    voff[db][0] = T::BYTES + tr_off<D>(lane, db, 0);
+    voff[db][1] = T::BYTES + tr_off<D>(lane, db, 1);
   }
 
   f32x16 o[DB];
@@ -69,14 +72,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 
   const uint32_t *list = a.list + item.z;
   const int n = item.w;
-  Stage64<D> tk, tv;
   if (n > 0) {
     const int kt = (int)(list[0] & 0x7fffffffu);
-    tk.load(kbase, ldk, kt * 64, S);
-    tv.load(vbase, ldk, kt * 64, S);
-    tk.template store<LK>(smem);
-    tv.template store<LV>(smem + LK::BYTES);
+    dma_tile<D>(smem, kbase, ldk, kt * 64, S);
+    dma_tile<D>(smem + T::BYTES, vbase, ldk, kt * 64, S);
   }
+  dma_wait();
   __syncthreads();
 
   for (int e = 0; e < n; ++e) {
@@ -85,9 +86,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     const bool partial = (ent >> 31) != 0;
     char *stage = smem + (e & 1) * STAGE;
     if (e + 1 < n) {
+      // the other buffer was last read before the previous barrier
       const int nkt = (int)(list[e + 1] & 0x7fffffffu);
-      tk.load(kbase, ldk, nkt * 64, S);
-      tv.load(vbase, ldk, nkt * 64, S);
+      char *next = smem + ((e + 1) & 1) * STAGE;
+      dma_tile<D>(next, kbase, ldk, nkt * 64, S);
+      dma_tile<D>(next + T::BYTES, vbase, ldk, nkt * 64, S);
     }
 
     uint32_t mlo = 0xffffffffu, mhi = 0xffffffffu;
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
         s[kb] = (f32x16){};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          s[kb] = mfma32(lds_rows<LK>(stage, kb * 32 + ln, ks * 32 + hh * 16), qv[ks], s[kb]);
+          s[kb] = mfma32(lds_rows(stage, koff[ks] + kb * 32 * T::ROWB), qv[ks], s[kb]);
       }
       if (partial) {
 #pragma unroll
@@ -135,22 +138,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -m_run));
+      // O^T += V^T P^T, one 16-key step at a time; the V^T operands of a step
+      // are read (transposed) while its P^T operand is converted.
+      const uint32_t sbase = lds_addr(stage);
+      uint32_t va[DB][2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int db = 0; db < DB; ++db) {
+        va[db][0] = sbase + voff[db][0];
+        va[db][1] = sbase + voff[db][1];
+      }
+      auto pv_step = [&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int toff = t * 16 * T::ROWB;
+        s16x4 x[2 * DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          x[2 * db] = tr_issue<toff>(va[db][0]);
+          x[2 * db + 1] = tr_issue<toff>(va[db][1]);
+        }
         const bf16x8 pb = c_to_b(s[t >> 1], t & 1);
         l_run = sum8(pb, l_run);
-        const int toff = t * 16 * LV::PITCH;
+        tr_wait(x);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          o[db] = mfma32(lds_tr(stage, voff[db][0] + toff, voff[db][1] + toff), pb, o[db]);
-      }
+        for (int db = 0; db < DB; ++db) o[db] = mfma32(tr_pair(x[2 * db], x[2 * db + 1]), pb, o[db]);
+      };
+      pv_step(std::integral_constant<int, 0>{});
+      pv_step(std::integral_constant<int, 1>{});
+      pv_step(std::integral_constant<int, 2>{});
+      pv_step(std::integral_constant<int, 3>{});
     }
 
-    if (e + 1 < n) {
-      char *next = smem + ((e + 1) & 1) * STAGE;
-      tk.template store<LK>(next);
-      tv.template store<LV>(next + LK::BYTES);
-    }
+    dma_wait();
     __syncthreads();
   }
 

@@ -104,81 +104,118 @@ __device__ __forceinline__ float keep_or(uint32_t m, int bit, float x, float oth
 }
 
 // --------------------------------------------------------------------------
-// LDS tiles of 64 rows x D bf16 in natural [row][d] layout.
-//   SWZ = false: row pitch 2D+16 bytes, conflict-free 16-byte row reads.
-//   SWZ = true:  row pitch 2D+64 bytes with 16-byte chunks XOR-swizzled by
-//                the row; conflict-free for row reads, transposed reads and
-//                the staging writes alike.
+// LDS tiles of 64 rows x D bf16 in natural [row][d] layout, rows unpadded
+// (2D bytes) and 16-byte chunks XOR-swizzled by the row, so that 16-byte row
+// reads (MFMA A operands), transposed reads and whole-row writes are all free
+// of bank conflicts (d = 128; d = 64 keeps a two-way conflict on one kind).
+// Tiles are filled by direct global -> LDS loads: one wave instruction writes
+// 1 KiB of consecutive LDS bytes, lane L at byte 16 L, and each lane fetches
+// the global chunk that the swizzle places at its LDS position.
 // --------------------------------------------------------------------------
-template <int D, bool SWZ>
-struct Lds {
-  static constexpr int PITCH = SWZ ? 2 * D + 64 : 2 * D + 16;
-  static constexpr int BYTES = 64 * PITCH;
-  static constexpr int NCH = (2 * D / 16) < 16 ? (2 * D / 16) : 16;
+template <int D>
+struct Tile {
+  static constexpr int ROWB = 2 * D;            // bytes per row
+  static constexpr int BYTES = 64 * ROWB;
+  static constexpr int RPK = 1024 / ROWB;       // rows per 1 KiB load instruction
+  static constexpr int LPR = 64 / RPK;          // lanes per row in one instruction
+  static constexpr int NI = BYTES / 1024 / 4;   // load instructions per wave (4 waves)
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return ((r & 3) << 1) | ((r >> 2) & 1);
+  }
   __device__ static __forceinline__ int off(int row, int cb) {
-    return row * PITCH + (SWZ ? (cb ^ ((row & (NCH - 1)) << 4)) : cb);
+    return row * ROWB + (cb ^ (swz(row) << 4));
   }
 };
 
-// A operand from a natural tile: rows row..row+31 by lane, 16 elements of d
-// starting at byte cb (lane half h adds 16 bytes).
-template <class L>
-__device__ __forceinline__ bf16x8 lds_rows(const char *base, int row, int cb) {
-  return *reinterpret_cast<const bf16x8 *>(base + L::off(row, cb));
+// Issue the loads of rows row0 + [0, 64) of a [.., ld] bf16 matrix into the
+// LDS tile at `dst`.  Rows >= nrows repeat row nrows - 1 (finite values; the
+// kernels mask them).  Completion: s_waitcnt vmcnt(0) then a barrier.
+template <int D>
+__device__ __forceinline__ void dma_tile(char *dst, const bf16 *base, int64_t ld, int row0,
+                                         int nrows) {
+  using T = Tile<D>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < T::NI; ++i) {
+    const int blk = wave * T::NI + i;
+    const int row = blk * T::RPK + lane / T::LPR;
+    const int c = (lane % T::LPR) ^ T::swz(row);
+    int grow = row0 + row;
+    grow = grow < nrows ? grow : nrows - 1;
+    __builtin_amdgcn_global_load_lds(base + (int64_t)grow * ld + c * 8,
+                                     (__attribute__((address_space(3))) void *)(
+                                         (__attribute__((address_space(3))) char *)dst + blk * 1024),
+                                     16, 0, 0);
+  }
+}
+
+// Wait for this wave's outstanding global -> LDS loads (and other vector
+// memory operations); a barrier must follow before other waves read.
+__device__ __forceinline__ void dma_wait() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Byte offset, inside a tile, of this lane's 16-byte row read for k-step ks
+// (rows 32 rb + l % 32 add rb * 32 * ROWB, which leaves the swizzle alone).
+template <int D>
+__device__ __forceinline__ int row_off(int lane, int ks) {
+  return Tile<D>::off(lane & 31, ks * 32 + (lane >> 5) * 16);
+}
+
+__device__ __forceinline__ bf16x8 lds_rows(const char *base, int off) {
+  return *reinterpret_cast<const bf16x8 *>(base + off);
 }
 
 // Per-lane byte offsets of the transposed reads of one d-block db (two
-// halves: rows +0 and +8 of a 16-row k-step); add 16 * t * PITCH for k-step t.
-template <class L>
+// halves: rows +0 and +8 of a 16-row k-step); add 16 * t * ROWB for step t.
+template <int D>
 __device__ __forceinline__ int tr_off(int lane, int db, int half) {
   const int row = 8 * half + 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int cb = db * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-  return L::off(row, cb);
+  return Tile<D>::off(row, cb);
 }
 
-// A operand (m = d within a 32-block, k = 16 tile rows of k-step t in C order)
-// from a natural tile, via two transposed reads at precomputed offsets.
-__device__ __forceinline__ bf16x8 lds_tr(const char *base, int off0, int off1) {
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4 *)((__attribute__((address_space(3))) char *)base + off0));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4 *)((__attribute__((address_space(3))) char *)base + off1));
-  const s16x4 lo = a, hi = b;
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// Transposed LDS reads are issued as inline assembly and completed by an
+// explicit wait.  The compiler cannot tell which LDS bytes its own transposed
+// read builtin touches, so it waits for every outstanding global -> LDS load
+// before each such read, which would serialise the next tile's prefetch with
+// the current tile's products.  The tiles read here were completed by
+// dma_wait() and a barrier, so no wait on the prefetch is needed.
+// tr_issue<OFF>(addr): one ds_read_b64_tr_b16 at LDS byte addr + OFF; the
+// result is valid only after tr_wait() names it.
+template <int OFF>
+__device__ __forceinline__ s16x4 tr_issue(uint32_t addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// Wait for all outstanding LDS reads; the listed registers are tied to the
+// wait so that no use of them can be scheduled before it.
+template <int N>
+__device__ __forceinline__ void tr_wait(s16x4 (&x)[N]) {
+  static_assert(N == 4 || N == 8 || N == 16, "tr_wait: 4, 8 or 16 operands");
+  if constexpr (N == 4)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+  else if constexpr (N == 8)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
+                   "+v"(x[6]), "+v"(x[7]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
+                   "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]),
+                   "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
+}
+
+// The A operand formed by two transposed reads (rows +0 and +8 of a k-step).
+__device__ __forceinline__ bf16x8 tr_pair(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
-
-// 64-row tile staging through registers.  256 threads; thread t owns 16-byte
-// chunk c = t % CPR of RPT consecutive rows starting at RPT * (t / CPR):
-// global loads are coalesced along d, LDS writes are whole rows.
-template <int D>
-struct Stage64 {
-  static constexpr int CPR = D / 8;
-  static constexpr int RPT = 64 * CPR / 256;
-  uint4 r[RPT];
-
-  // rows row0 + [0, 64) of a [.., ld] bf16 matrix; rows >= nrows read as 0
-  __device__ __forceinline__ void load(const bf16 *base, int64_t ld, int row0, int nrows) {
-    const int t = threadIdx.x;
-    const int c = t % CPR, g = t / CPR;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int row = row0 + g * RPT + i;
-      if (row < nrows)
-        r[i] = *reinterpret_cast<const uint4 *>(base + (int64_t)row * ld + c * 8);
-      else
-        r[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-
-  template <class L>
-  __device__ __forceinline__ void store(char *s) const {
-    const int t = threadIdx.x;
-    const int c = t % CPR, g = t / CPR;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-      *reinterpret_cast<uint4 *>(s + L::off(g * RPT + i, c * 16)) = r[i];
-  }
-};
 
 // --------------------------------------------------------------------------
 // Kernel arguments (device pointers into caller buffers and the plan blob).
@@ -203,10 +240,13 @@ struct FwdArgs {
   MaskArgs m;
 };
 
+// Backward workspace: per (b, h), S64 = S rounded up to 64 rows of
+// lse * log2(e), then S64 rows of D = rowsum(dO * O); pad rows hold 0.
 struct BwdArgs {
   const bf16 *q, *k, *v, *o, *dout;
   const float *lse;
-  float *dws;  // D = rowsum(dO * O), [B, Hq, S]
+  float *ws;
+  int S64;
   bf16 *dq, *dk, *dv;
   int S, Hq, Hkv, G;
   float scale, sl2;

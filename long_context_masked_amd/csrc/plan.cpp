@@ -583,9 +583,11 @@ extern "C" attn_status attn_plan_get_layout(const attn_plan *plan, attn_plan_lay
   return ATTN_OK;
 }
 
+// Two fp32 values (LSE * log2 e and D) per (b, h, row), rows padded to 64.
 extern "C" size_t attn_bwd_workspace_bytes(const attn_plan *plan) {
   if (!plan) return 0;
-  return (size_t)((plan->shape.B * plan->shape.Hq * plan->shape.S * 4 + 255) & ~int64_t(255));
+  const int64_t s64 = (plan->shape.S + 63) / 64 * 64;
+  return (size_t)((plan->shape.B * plan->shape.Hq * s64 * 8 + 255) & ~int64_t(255));
 }
 
 extern "C" void attn_plan_destroy(attn_plan *plan) { delete plan; }
