@@ -145,6 +145,10 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   __syncthreads();
 
   for (int st = 0; st < nst; ++st) {
+#pragma unroll
+    for (int i = 0; i < DB; ++i) { in_agpr(dk[i]); in_agpr(dv[i]); }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) { in_agpr(kv[ks]); in_agpr(vv[ks]); }
     const int e = st / G, g = st - e * G;
     const uint32_t ent = list[e];
     const int qt = (int)(ent & 0x7fffffffu);
@@ -177,12 +181,23 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
+        // S = Q K^T and dP = dO V^T; the Q and dO row reads run two k-steps
+        // ahead of the products that consume them.
         f32x16 s = (f32x16){}, dp = (f32x16){};
+        bf16x8 aq[KS], ao[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s = mfma32(lds_rows(stage, roff[ks] + qh * 32 * T::ROWB), kv[ks], s);
-          dp = mfma32(lds_rows(stage + OFF_DO, roff[ks] + qh * 32 * T::ROWB), vv[ks], dp);
+          aq[ks] = lds_rows(stage, roff[ks] + qh * 32 * T::ROWB);
+          ao[ks] = lds_rows(stage + OFF_DO, roff[ks] + qh * 32 * T::ROWB);
         }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s = mfma32(aq[ks], kv[ks], s);
+          dp = mfma32(ao[ks], vv[ks], dp);
+        }
+        pipeline_reads_mfma<KS>();
+        in_vgpr(s);
+        in_vgpr(dp);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sl + qh * 32 + 8 * c + 4 * hh);

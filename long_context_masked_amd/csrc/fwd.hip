@@ -103,14 +103,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       mhi = (uint32_t)(sh >> 32);
     }
     if (active) {
+      // S^T = K Q^T for the two 32-key blocks; the K row reads run two
+      // k-steps ahead of the products that consume them.
       f32x16 s[2];
+      bf16x8 ak[2][KS];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = (f32x16){};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[kb] = mfma32(lds_rows(stage, koff[ks] + kb * 32 * T::ROWB), qv[ks], s[kb]);
+      for (int ks = 0; ks < KS; ++ks) {
+        ak[0][ks] = lds_rows(stage, koff[ks]);
+        ak[1][ks] = lds_rows(stage, koff[ks] + 32 * T::ROWB);
       }
+      s[0] = (f32x16){};
+      s[1] = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s[0] = mfma32(ak[0][ks], qv[ks], s[0]);
+        s[1] = mfma32(ak[1][ks], qv[ks], s[1]);
+      }
+      pipeline_reads_mfma<KS>();
       if (partial) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

@@ -212,6 +212,30 @@ __device__ __forceinline__ void tr_wait(s16x4 (&x)[N]) {
                    "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
 }
 
+// Register-class hints (no instructions): keep a value in accumulation
+// registers (AGPRs, readable by MFMA as operands and accumulators) or in
+// vector registers (VGPRs, where VALU instructions can use it).  They steer
+// the allocator away from shuttling values between the two files.
+template <class X>
+__device__ __forceinline__ void in_agpr(X &x) { asm volatile("" : "+a"(x)); }
+template <class X>
+__device__ __forceinline__ void in_vgpr(X &x) { asm volatile("" : "+v"(x)); }
+
+// Scheduling pattern for a block of 2*KS LDS row reads feeding 2*KS MFMAs
+// (two independent accumulation chains): four reads first, then pairs of
+// products each followed by the next pair of reads, so that LDS latency is
+// covered by MFMA work instead of a wait before every pair.
+template <int KS>
+__device__ __forceinline__ void pipeline_reads_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+#pragma unroll
+  for (int i = 0; i < KS - 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
 // The A operand formed by two transposed reads (rows +0 and +8 of a k-step).
 __device__ __forceinline__ bf16x8 tr_pair(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
