@@ -186,3 +186,36 @@ def output_rows(q, k, v, spec, h, rows, scale=None):
         o[r] = p[0] @ v[0, :, kv, :]
         lse[r] = l[0]
     return o, lse
+
+
+def grad_rows(q, k, v, do, spec, h, rows, scale=None, o_for_d="exact"):
+    """dQ, O and LSE of query head ``h`` for an arbitrary set of rows only
+    (batch 0).  Every quantity a row's dQ needs is local to the row: its
+    probabilities p_ij, D_i = dO_i . O_i and dP_ij = dO_i . v_j.  Returns
+    dq [len(rows), d], o [len(rows), d], lse [len(rows)] and the quadratic
+    magnitudes m_dq, m_o of the two products (see ``backward``)."""
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    hm = masks.mask_head(spec, h, Hq, Hkv)
+    kv = h // G
+    kk = k[0, :, kv, :]
+    vv = v[0, :, kv, :]
+    out = {n: np.zeros((len(rows), d)) for n in ("dq", "o", "m_dq", "m_o")}
+    out["lse"] = np.zeros(len(rows))
+    for r, i in enumerate(rows):
+        s = (kk @ q[0, i, h, :]) * scale
+        p, l = _probs(s[None, :], masks.allowed(spec, i, i + 1, hm))
+        p = p[0]
+        oi = p @ vv
+        od = oi if o_for_d == "exact" else round_bf16(oi)
+        Di = float(do[0, i, h, :] @ od)
+        dp = vv @ do[0, i, h, :]
+        ds = p * (dp - Di)
+        out["dq"][r] = (ds @ kk) * scale
+        out["o"][r] = oi
+        out["lse"][r] = l[0]
+        out["m_dq"][r] = np.sqrt((ds * ds) @ (kk * kk)) * scale
+        out["m_o"][r] = np.sqrt((p * p) @ (vv * vv))
+    return out

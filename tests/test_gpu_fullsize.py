@@ -1,0 +1,152 @@
+"""GPU parity at the workloads' full sizes, in the benchmark's launch
+configuration (B=1, GQA 64:8, d=128).
+
+At these sizes the fp64 oracle cannot run whole tensors, so the tests check:
+* sampled rows of O, LSE and dQ, which the oracle computes one row at a time
+  (everything a row's dQ needs is local to the row), against the same gate as
+  the small cases;
+* every row's mask coverage with Q = 0: all allowed keys then get the same
+  weight, so exp(LSE_i) must equal the number of allowed keys n_i (counted
+  from the oracle's predicate) and O_i the mean of the allowed v_j;
+* the identity sum_j dV_j = sum over query rows of the group of dO_i, which
+  holds at any size because every probability row sums to one;
+* uniform V: O = v, dQ = dK = 0.
+"""
+import numpy as np
+import pytest
+
+import synthetic as syn
+from oracle import attention as ora
+from oracle import masks as om
+
+from gpu_util import f64, gate, to_dev, to_f64
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import long_context_masked_amd as lcm  # noqa: E402
+
+HQ, HKV, D = 64, 8, 128
+_INPUTS = {}
+
+
+def inputs(S):
+    if S not in _INPUTS:
+        x = syn.attention_inputs(1, S, HQ, HKV, D, seed=0)
+        _INPUTS[S] = (x, {n: to_dev(x[n], torch) for n in x})
+    return _INPUTS[S]
+
+
+class Lazy64:
+    """Array view that widens bf16 bits to float64 only where indexed."""
+
+    def __init__(self, bits):
+        self.bits = bits
+        self.shape = bits.shape
+
+    def __getitem__(self, idx):
+        return f64(self.bits[idx])
+
+
+def _cases():
+    out = []
+    for label, spec in syn.config_mask_specs("dense", 49152):
+        out.append(("dense48K_" + label, spec))
+    for label, spec in syn.config_mask_specs("document"):
+        out.append(("doc64K_" + label, spec))
+    for label, spec in syn.config_mask_specs("hetero"):
+        out.append(("hetero32K_" + label, spec))
+    for label, spec in syn.config_mask_specs("sparse", 32768, Hq=HQ, Hkv=HKV):
+        out.append(("sparse32K_" + label, spec))
+    return out
+
+
+CASES = _cases()
+IDS = [c[0] for c in CASES]
+
+
+def _rows(S, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, S // 3, S // 2 + 7, S - 65, S - 2, S - 1]
+    return sorted(set(fixed + rng.integers(0, S, 7).tolist()))
+
+
+@pytest.mark.parametrize("label,spec", CASES, ids=IDS)
+def test_sampled_rows(label, spec):
+    S = spec["S"]
+    x, t = inputs(S)
+    plan = lcm.Plan(1, S, HQ, HKV, D, spec)
+    o, lse = lcm.fwd(plan, t["q"], t["k"], t["v"])
+    dq, dk, dv = lcm.bwd(plan, t["q"], t["k"], t["v"], o, lse, t["do"])
+    torch.cuda.synchronize()
+    rows = _rows(S, 1)
+    lz = {n: Lazy64(x[n]) for n in ("q", "k", "v", "do")}
+    got = {"o": [], "dq": [], "lse": []}
+    ref = {"o": [], "dq": [], "lse": [], "m_o": [], "m_dq": []}
+    for h in (0, 7, 33, 63):
+        r = ora.grad_rows(lz["q"], lz["k"], lz["v"], lz["do"], spec, h, rows, o_for_d="bf16")
+        for n in ref:
+            ref[n].append(r[n])
+        got["o"].append(to_f64(o[0, rows, h]))
+        got["dq"].append(to_f64(dq[0, rows, h]))
+        got["lse"].append(lse[0, h, rows].cpu().numpy().astype(np.float64))
+    g = {n: np.stack(v) for n, v in got.items()}
+    rf = {n: np.stack(v) for n, v in ref.items()}
+    gate("O", g["o"], rf["o"], rf["m_o"])
+    gate("dQ", g["dq"], rf["dq"], rf["m_dq"])
+    assert np.abs(g["lse"] - rf["lse"]).max() <= 5e-3
+    # sum_j dV_j = sum of dO over the rows of the group (every row has a key)
+    dvs = dv[0].to(torch.float64).sum(dim=0)          # [Hkv, d]
+    dos = t["do"][0].to(torch.float64).sum(dim=0).reshape(HKV, HQ // HKV, D).sum(dim=1)
+    err = (dvs - dos).abs().max().item()
+    assert err <= 1e-2 * np.sqrt(S * HQ / HKV), err
+    assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+@pytest.mark.parametrize("label,spec", CASES, ids=IDS)
+def test_mask_coverage_every_row(label, spec):
+    """Q = 0: exp(LSE_i) = n_i for every row and head; O_i = mean of allowed v_j."""
+    S = spec["S"]
+    x, t = inputs(S)
+    plan = lcm.Plan(1, S, HQ, HKV, D, spec)
+    q0 = torch.zeros_like(t["q"])
+    o, lse = lcm.fwd(plan, q0, t["k"], t["v"])
+    torch.cuda.synchronize()
+    nh = spec["bitmap"]["bits"].shape[0] if "bitmap" in spec else 1
+    G = HQ // HKV
+    vbits = x["v"]
+    for hm in range(nh):
+        counts = np.zeros(S, dtype=np.int64)
+        for i0 in range(0, S, 2048):
+            counts[i0:i0 + 2048] = om.allowed(spec, i0, min(S, i0 + 2048), hm).sum(axis=1)
+        heads = [h for h in range(HQ) if om.mask_head(spec, h, HQ, HKV) == hm]
+        n_gpu = torch.exp(lse[0, heads].to(torch.float64)).cpu().numpy()
+        assert (np.rint(n_gpu) == counts[None, :]).all(), label
+        assert np.abs(n_gpu / counts[None, :] - 1).max() < 1e-4
+        # O_i = mean of the allowed v_j on sampled rows of the first head
+        h = heads[0]
+        rows = _rows(S, 2)
+        vv = f64(vbits[0, :, h // G, :])
+        a = np.stack([om.allowed(spec, i, i + 1, hm)[0] for i in rows])
+        want = (a @ vv) / a.sum(axis=1, keepdims=True)
+        gate("O(Q=0)", to_f64(o[0, rows, h]), want)
+
+
+@pytest.mark.parametrize("label,spec", [c for c in CASES if c[0].startswith(("dense48K_causal", "hetero32K_shared", "sparse32K_var"))],
+                         ids=[c[0] for c in CASES if c[0].startswith(("dense48K_causal", "hetero32K_shared", "sparse32K_var"))])
+def test_uniform_v_closed_form(label, spec):
+    """v_j = v for every key: O = v, and dQ = dK = 0 up to rounding."""
+    S = spec["S"]
+    x, t = inputs(S)
+    plan = lcm.Plan(1, S, HQ, HKV, D, spec)
+    v1 = t["v"][:, :1].expand_as(t["v"]).contiguous()
+    o, lse = lcm.fwd(plan, t["q"], t["k"], v1)
+    dq, dk, dv = lcm.bwd(plan, t["q"], t["k"], v1, o, lse, t["do"])
+    torch.cuda.synchronize()
+    want = v1[0, 0].repeat_interleave(HQ // HKV, dim=0).to(torch.float32)  # [Hq, d]
+    assert (o[0].to(torch.float32) - want[None]).abs().max().item() <= 2.0 ** -7 * want.abs().max().item()
+    assert dq.abs().max().item() <= 1e-3
+    assert dk.abs().max().item() <= 1e-3

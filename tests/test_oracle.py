@@ -376,3 +376,22 @@ def test_o_for_d_bf16_is_exact_when_o_is_representable():
     e = ora.backward(x["q"], x["k"], x["v"], x["do"], spec)
     assert np.abs(c["dq"] - e["dq"]).max() > 0
     np.testing.assert_array_equal(c["dv"], e["dv"])
+
+
+def test_grad_rows_matches_backward():
+    """The per-row oracle path agrees with the whole-tensor backward."""
+    S, Hq, Hkv, d = 80, 4, 2, 6
+    x = _inputs(S, Hq, Hkv, d, seed=14)
+    offs, bits = syn.variable_block_bitmap(S, 5, 20, Hkv, 0.5, seed=15)
+    for spec in (syn.spec_causal(S), syn.spec_shared_question(10, [30, 40]),
+                 syn.with_bitmap(syn.spec_full(S), offs, offs, bits)):
+        for o_for_d in ("exact", "bf16"):
+            g = ora.backward(x["q"], x["k"], x["v"], x["do"], spec, o_for_d=o_for_d, magnitudes=True)
+            rows = [0, 1, 37, 79]
+            for h in (0, 3):
+                r = ora.grad_rows(x["q"], x["k"], x["v"], x["do"], spec, h, rows, o_for_d=o_for_d)
+                np.testing.assert_allclose(r["dq"], g["dq"][0, rows, h], atol=1e-13)
+                np.testing.assert_allclose(r["o"], g["o"][0, rows, h], atol=1e-14)
+                np.testing.assert_allclose(r["lse"], g["lse"][0, h, rows], atol=1e-14)
+                np.testing.assert_allclose(r["m_dq"], g["m_dq"][0, rows, h], atol=1e-13)
+                np.testing.assert_allclose(r["m_o"], g["m_o"][0, rows, h], atol=1e-14)
