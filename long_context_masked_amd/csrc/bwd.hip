@@ -120,6 +120,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 
   const uint32_t *list = a.blist + item.z;
   const int nst = item.w * G;
+  TileDma<D> dma;
+  dma.init(ldq);
 
   // Loads of stage st into `stg`: the Q and dO tiles of head kvh*G + g and
   // 64 rows each of lse2 and D (wave 0, lanes 0..31, 16 bytes per lane).
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     const int e = st / G, g = st - e * G;
     const int qt = (int)(list[e] & 0x7fffffffu);
     const int h = kvh * G + g;
-    dma_tile<D>(stg, a.q + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
-    dma_tile<D>(stg + OFF_DO, a.dout + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
+    dma.load(stg, a.q + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
+    dma.load(stg + OFF_DO, a.dout + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
     if (wave == 0 && lane < 32) {
       const float *src = a.ws + ws_row0(b, h, a.Hq, a.S64) + (lane >> 4) * a.S64 + qt * 64 +
                          (lane & 15) * 4;
@@ -198,6 +200,10 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
         pipeline_reads_mfma<KS>();
         in_vgpr(s);
         in_vgpr(dp);
+        if (partial) {  // masked scores -> -inf, so that P = 0 there
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = keep_or(mw[qh], 8 * (r >> 2) + (r & 3), s[r], kNegInf);
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sl + qh * 32 + 8 * c + 4 * hh);
@@ -205,8 +211,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int r = 4 * c + j;
-            const float p = keep_or(mw[qh], 8 * c + j,
-                                    __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[j])), 0.f);
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[j]));
             s[r] = p;
             dp[r] = p * (dp[r] - d4[j]);
           }
@@ -327,10 +332,12 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
 
   const uint32_t *list = a.flist + item.z;
   const int n = item.w;
+  TileDma<D> dma;
+  dma.init(ldk);
   if (n > 0) {
     const int kt = (int)(list[0] & 0x7fffffffu);
-    dma_tile<D>(smem, kbase, ldk, kt * 64, S);
-    dma_tile<D>(smem + T::BYTES, vbase, ldk, kt * 64, S);
+    dma.load(smem, kbase, ldk, kt * 64, S);
+    dma.load(smem + T::BYTES, vbase, ldk, kt * 64, S);
   }
   dma_wait();
   __syncthreads();
@@ -343,8 +350,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
     if (e + 1 < n) {
       const int nkt = (int)(list[e + 1] & 0x7fffffffu);
       char *next = smem + ((e + 1) & 1) * STAGE;
-      dma_tile<D>(next, kbase, ldk, nkt * 64, S);
-      dma_tile<D>(next + T::BYTES, vbase, ldk, nkt * 64, S);
+      dma.load(next, kbase, ldk, nkt * 64, S);
+      dma.load(next + T::BYTES, vbase, ldk, nkt * 64, S);
     }
     uint32_t mw[2] = {0xffffffffu, 0xffffffffu};
     bool active = true;
@@ -371,10 +378,13 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
           s = mfma32(lds_rows(stage, roff[ks] + kh * 32 * T::ROWB), qv[ks], s);
           dp = mfma32(lds_rows(stage + T::BYTES, roff[ks] + kh * 32 * T::ROWB), dov[ks], dp);
         }
+        if (partial) {  // masked scores -> -inf, so that P = 0 there
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = keep_or(mw[kh], 8 * (r >> 2) + (r & 3), s[r], kNegInf);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = keep_or(mw[kh], 8 * (r >> 2) + (r & 3),
-                                  __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2)), 0.f);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2));
           dp[r] = p * (dp[r] - Dr);
         }
         // dQ^T += K^T dS^T, one 16-key step at a time.
@@ -419,6 +429,19 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
       }
   }
 }
+
+// Every variant is instantiated explicitly: implicit instantiation from the
+// launchers alone has left some host-side launch stubs unemitted.
+template __global__ void attn_bwd_pre_kernel<128>(const bf16 *, const bf16 *, const float *,
+                                                  float *, int, int, int, int64_t);
+template __global__ void attn_bwd_pre_kernel<64>(const bf16 *, const bf16 *, const float *,
+                                                 float *, int, int, int, int64_t);
+template __global__ void attn_dkdv_kernel<128>(BwdArgs);
+template __global__ void attn_dkdv_kernel<64>(BwdArgs);
+template __global__ void attn_dq_kernel<128, 2>(BwdArgs);
+template __global__ void attn_dq_kernel<128, 1>(BwdArgs);
+template __global__ void attn_dq_kernel<64, 2>(BwdArgs);
+template __global__ void attn_dq_kernel<64, 1>(BwdArgs);
 
 hipError_t launch_bwd_pre(const BwdArgs &a, int d, int B, hipStream_t st) {
   const int64_t nrows = (int64_t)B * a.S64 * a.Hq;

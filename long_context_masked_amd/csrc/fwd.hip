@@ -72,10 +72,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 
   const uint32_t *list = a.list + item.z;
   const int n = item.w;
+  TileDma<D> dma;
+  dma.init(ldk);
   if (n > 0) {
     const int kt = (int)(list[0] & 0x7fffffffu);
-    dma_tile<D>(smem, kbase, ldk, kt * 64, S);
-    dma_tile<D>(smem + T::BYTES, vbase, ldk, kt * 64, S);
+    dma.load(smem, kbase, ldk, kt * 64, S);
+    dma.load(smem + T::BYTES, vbase, ldk, kt * 64, S);
   }
   dma_wait();
   __syncthreads();
@@ -89,8 +91,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       // the other buffer was last read before the previous barrier
       const int nkt = (int)(list[e + 1] & 0x7fffffffu);
       char *next = smem + ((e + 1) & 1) * STAGE;
-      dma_tile<D>(next, kbase, ldk, nkt * 64, S);
-      dma_tile<D>(next + T::BYTES, vbase, ldk, nkt * 64, S);
+      dma.load(next, kbase, ldk, nkt * 64, S);
+      dma.load(next + T::BYTES, vbase, ldk, nkt * 64, S);
     }
 
     uint32_t mlo = 0xffffffffu, mhi = 0xffffffffu;
@@ -199,6 +201,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
           l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
   }
 }
+
+// Every variant is instantiated explicitly: implicit instantiation from the
+// launcher alone has left some host-side launch stubs unemitted.
+template __global__ void attn_fwd_kernel<128, 2>(FwdArgs);
+template __global__ void attn_fwd_kernel<128, 1>(FwdArgs);
+template __global__ void attn_fwd_kernel<64, 2>(FwdArgs);
+template __global__ void attn_fwd_kernel<64, 1>(FwdArgs);
 
 hipError_t launch_fwd(const FwdArgs &a, int d, int HG, int n_items, int B, hipStream_t st) {
   const dim3 grid((unsigned)n_items, (unsigned)B), block(256);

@@ -150,6 +150,47 @@ __device__ __forceinline__ void dma_tile(char *dst, const bf16 *base, int64_t ld
   }
 }
 
+// dma_tile with the per-lane addressing hoisted out of the loop: `off` holds
+// the byte offset, from the tile's first row, of the global chunk that each
+// of the lane's NI load instructions fetches, and the wave index is made
+// uniform so that each load takes a scalar base plus a 32-bit lane offset.
+// Tiles that extend past nrows (the ragged last tile) use dma_tile instead.
+template <int D>
+struct TileDma {
+  uint32_t off[Tile<D>::NI];
+  int lds0;  // byte offset of this wave's first 1 KiB block in the tile
+
+  __device__ __forceinline__ void init(int64_t ld) {
+    using T = Tile<D>;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < T::NI; ++i) {
+      const int row = (wave * T::NI + i) * T::RPK + lane / T::LPR;
+      const int c = (lane % T::LPR) ^ T::swz(row);
+      off[i] = (uint32_t)(row * ld * 2 + c * 16);
+    }
+    lds0 = wave * T::NI * 1024;
+  }
+
+  __device__ __forceinline__ void load(char *dst, const bf16 *base, int64_t ld, int row0,
+                                       int nrows) const {
+    using T = Tile<D>;
+    if (row0 + 64 <= nrows) {
+      const char *g = reinterpret_cast<const char *>(base + (int64_t)row0 * ld);
+#pragma unroll
+      for (int i = 0; i < T::NI; ++i)
+        __builtin_amdgcn_global_load_lds(
+            g + off[i],
+            (__attribute__((address_space(3))) void *)(
+                (__attribute__((address_space(3))) char *)dst + lds0 + i * 1024),
+            16, 0, 0);
+    } else {
+      dma_tile<D>(dst, base, ld, row0, nrows);
+    }
+  }
+};
+
 // Wait for this wave's outstanding global -> LDS loads (and other vector
 // memory operations); a barrier must follow before other waves read.
 __device__ __forceinline__ void dma_wait() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
