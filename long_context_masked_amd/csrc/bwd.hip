@@ -65,24 +65,44 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
 // dK / dV: one workgroup per (K-tile of 128 keys, KV head).  Wave w owns keys
 // 32w .. 32w+31 of the tile (lane l: key 32w + l % 32), keeps K and V of
 // those keys as MFMA operands in registers and accumulates dK^T and dV^T.
-// For each listed Q-tile of 64 rows and each query head of the group, Q, dO,
-// lse2 and D are loaded straight into LDS (double-buffered); Q^T and dO^T
-// come from the same tiles by transposed reads.  Each 64-row tile is
-// processed as two 32-row halves:
-//   S = Q K^T, dP = dO V^T, P = exp2(S c - lse2), dS = P (dP - D)
-//   dV^T += dO^T P,  dK^T += Q^T dS
+// For each listed Q-tile of 64 rows and each query head of the group (one
+// stage), Q, dO, lse2 and D are loaded straight into LDS; Q^T and dO^T come
+// from the same tiles by transposed reads.  Each stage is two 32-row units,
+// and each unit u takes three steps:
+//   A(u): S = Q K^T, dP = dO V^T                          (MFMA)
+//   B(u): mask, P = exp2(S c - lse2), dS = P (dP - D)     (VALU)
+//   C(u): dV^T += dO^T P, dK^T += Q^T dS                   (MFMA)
+// One wave runs per SIMD, so the exponentials only overlap the products if
+// the wave's own instruction stream alternates them: a wave stalls at an
+// MFMA while the matrix pipe is busy with the previous one, but VALU work
+// issued between two MFMAs runs while the first is in the pipe.  The steps of
+// neighbouring units are therefore software-pipelined, and each phase is
+// written as a fixed sequence of chunks (two MFMAs plus a slice of B's VALU
+// work) fenced against reordering:
+//   phase 1:  A(st, 1)     with B(st, 0)           (exponentials)
+//   phase 2:  C(st, 0)     with B(st, 1) rows 0-15 (AGPR reads, mask) and
+//                               rows 0-7 (exponentials)
+//   phase 3a: A(st + 1, 0) with B(st, 1) rows 8-15 (exponentials)
+//   phase 3b: C(st, 1)     with B(st + 1, 0)       (AGPR reads, mask)
+// ("rows" are the 16 accumulator registers of a unit.)  Phase 3 reads the
+// next stage's tiles, so stages rotate through three LDS buffers: the
+// barrier before phase 3 publishes stage st + 1 and frees the buffer of
+// stage st - 1, which then receives stage st + 2.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
+  constexpr int KS = D / 16;    // k-steps of A (two MFMAs each: S and dP)
+  constexpr int DB = D / 32;    // 32-row blocks of dK^T / dV^T
+  constexpr int NC = 2 * DB;    // chunks of C (two MFMAs each: dV and dK)
   using T = Tile<D>;
   constexpr int OFF_DO = T::BYTES, OFF_L = 2 * T::BYTES, OFF_D = OFF_L + 256;
   constexpr int STAGE = 2 * T::BYTES + 1024;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr int NBUF = 3;
+  static_assert(16 % KS == 0 && 8 % KS == 0 && 16 % NC == 0 && 8 % NC == 0, "chunking");
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int ln = lane & 31, hh = lane >> 5;
   const int4 item = a.bitems[blockIdx.x];
   const int b = blockIdx.y;
@@ -118,137 +138,277 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   for (int i = 0; i < DB; ++i) { dk[i] = (f32x16){}; dv[i] = (f32x16){}; }
   const float sl2 = a.sl2;
 
-  const uint32_t *list = a.blist + item.z;
+  const auto *list = as_const(a.blist + item.z);
   const int nst = item.w * G;
   TileDma<D> dma;
   dma.init(ldq);
 
-  // Loads of stage st into `stg`: the Q and dO tiles of head kvh*G + g and
-  // 64 rows each of lse2 and D (wave 0, lanes 0..31, 16 bytes per lane).
+  // Loads of stage st into `stg`: the Q and dO tiles of head kvh*G + g, and
+  // 64 rows each of lse2 and D (lanes 0..7 of every wave, 16 bytes each), so
+  // that every wave issues the same number of loads per stage.
   auto load_stage = [&](int st, char *stg) {
     const int e = st / G, g = st - e * G;
     const int qt = (int)(list[e] & 0x7fffffffu);
     const int h = kvh * G + g;
     dma.load(stg, a.q + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
     dma.load(stg + OFF_DO, a.dout + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
-    if (wave == 0 && lane < 32) {
-      const float *src = a.ws + ws_row0(b, h, a.Hq, a.S64) + (lane >> 4) * a.S64 + qt * 64 +
-                         (lane & 15) * 4;
+    if (lane < 8) {
+      const int q = wave * 8 + lane;
+      const float *src =
+          a.ws + ws_row0(b, h, a.Hq, a.S64) + (q >> 4) * a.S64 + qt * 64 + (q & 15) * 4;
       __builtin_amdgcn_global_load_lds(
           src,
           (__attribute__((address_space(3))) void *)((__attribute__((address_space(3))) char *)stg +
-                                                      OFF_L),
+                                                      OFF_L + wave * 128),
           16, 0, 0);
     }
   };
 
-  if (nst > 0) load_stage(0, smem);
-  dma_wait();
-  __syncthreads();
+  // Allowed-row words of the lane's key for the two units of stage st (all
+  // ones unless the tile is partial).
+  auto stage_mask = [&](int st, uint32_t (&mw)[2]) {
+    const int e = st / G, g = st - e * G;
+    const uint32_t ent = list[e];
+    mw[0] = 0xffffffffu;
+    mw[1] = 0xffffffffu;
+    if (ent >> 31) {
+      const int qt = (int)(ent & 0x7fffffffu);
+      const int hm = bitmap_head(a.m.bm_heads, kvh * G + g, a.Hq, G);
+      const uint64_t mk = key_ok ? col_mask(a.m, cb, kblk, hm, qt * 64, S) : 0ull;
+      const uint64_t sh = mk >> (4 * hh);
+      mw[0] = (uint32_t)sh;
+      mw[1] = (uint32_t)(sh >> 32);
+    }
+  };
 
+  // The row operands of k-step ks of unit qh of `buf`.
+  auto rows_q = [&](const char *buf, int qh, int ks) { return lds_rows(buf, roff[ks] + qh * 32 * T::ROWB); };
+  auto rows_o = [&](const char *buf, int qh, int ks) {
+    return lds_rows(buf + OFF_DO, roff[ks] + qh * 32 * T::ROWB);
+  };
+
+  // Transposed operands of C for k-step TT of unit QH of the current stage.
+  uint32_t sa[DB][2];
+  auto issue_tr = [&](auto qhc, auto ttc, s16x4(&x)[4 * DB]) {
+    constexpr int OFF = (2 * decltype(qhc)::value + decltype(ttc)::value) * 16 * T::ROWB;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      x[4 * db + 0] = tr_issue<OFF + OFF_DO>(sa[db][0]);
+      x[4 * db + 1] = tr_issue<OFF + OFF_DO>(sa[db][1]);
+      x[4 * db + 2] = tr_issue<OFF>(sa[db][0]);
+      x[4 * db + 3] = tr_issue<OFF>(sa[db][1]);
+    }
+  };
+  // One chunk of C: block db of k-step x.
+  auto c_chunk = [&](const s16x4(&x)[4 * DB], int db, bf16x8 pb, bf16x8 dsb) {
+    dv[db] = mfma32(tr_pair(x[4 * db], x[4 * db + 1]), pb, dv[db]);
+    dk[db] = mfma32(tr_pair(x[4 * db + 2], x[4 * db + 3]), dsb, dk[db]);
+  };
+
+  // B pieces on accumulator register r of a unit.
+  auto b_read = [&](f32x16 &s, f32x16 &dp, const f32x16 &sa_, const f32x16 &dpa, int r) {
+    float x = sa_[r], y = dpa[r];
+    in_vgpr(x);
+    in_vgpr(y);
+    s[r] = x;
+    dp[r] = y;
+  };
+  // (Each result is pinned where it is computed: the values are consumed
+  // phases later, and without the pins the compiler sinks the arithmetic
+  // next to its uses, undoing the interleave.)
+  auto b_mask = [&](f32x16 &s, uint32_t mw, int r) {
+    float x = keep_or(mw, 8 * (r >> 2) + (r & 3), s[r], kNegInf);
+    in_vgpr(x);
+    s[r] = x;
+  };
+  auto b_exp = [&](f32x16 &s, f32x16 &dp, int r, float l, float d) {
+    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l));
+    float ds = p * (dp[r] - d);
+    in_vgpr(p);
+    in_vgpr(ds);
+    s[r] = p;
+    dp[r] = ds;
+  };
+  auto b_pack = [&](const f32x16 &s, const f32x16 &dp, int t, bf16x8 &pb, bf16x8 &dsb) {
+    pb = c_to_b(s, t);
+    dsb = c_to_b(dp, t);
+    in_vgpr(pb);
+    in_vgpr(dsb);
+  };
+
+  f32x16 s0, dp0;  // unit (st, 0): S and dP in VGPRs, masked
+  uint32_t mwc[2], mwn[2];
+  if (nst > 0) {
+    load_stage(0, smem);
+    if (nst > 1) load_stage(1, smem + STAGE);
+    stage_mask(0, mwc);
+    dma_wait();
+    __syncthreads();
+    f32x16 sa0 = (f32x16){}, dpa0 = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      sa0 = mfma32(rows_q(smem, 0, ks), kv[ks], sa0);
+      dpa0 = mfma32(rows_o(smem, 0, ks), vv[ks], dpa0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      b_read(s0, dp0, sa0, dpa0, r);
+      b_mask(s0, mwc[0], r);
+    }
+  }
+
+  int cur = 0;  // buffer of stage st
   for (int st = 0; st < nst; ++st) {
 #pragma unroll
     for (int i = 0; i < DB; ++i) { in_agpr(dk[i]); in_agpr(dv[i]); }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) { in_agpr(kv[ks]); in_agpr(vv[ks]); }
-    const int e = st / G, g = st - e * G;
-    const uint32_t ent = list[e];
-    const int qt = (int)(ent & 0x7fffffffu);
-    const bool partial = (ent >> 31) != 0;
-    const int h = kvh * G + g;
-    char *stage = smem + (st & 1) * STAGE;
-    // the other buffer was last read before the previous barrier
-    if (st + 1 < nst) load_stage(st + 1, smem + ((st + 1) & 1) * STAGE);
-
-    // rows of this tile visible to the lane's key (all ones on full tiles)
-    uint32_t mw[2] = {0xffffffffu, 0xffffffffu};
-    bool active = true;
-    if (partial) {
-      const int hm = bitmap_head(a.m.bm_heads, h, a.Hq, G);
-      const uint64_t mk = key_ok ? col_mask(a.m, cb, kblk, hm, qt * 64, S) : 0ull;
-      active = __ballot(mk != 0ull) != 0ull;
-      const uint64_t sh = mk >> (4 * hh);
-      mw[0] = (uint32_t)sh;
-      mw[1] = (uint32_t)(sh >> 32);
+    const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
+    const int fre = nxt == NBUF - 1 ? 0 : nxt + 1;  // buffer of stage st - 1 = st + 2
+    const char *buf = smem + cur * STAGE;
+    const char *nbuf = smem + nxt * STAGE;
+    if (st + 1 < nst) {
+      stage_mask(st + 1, mwn);
+    } else {
+      mwn[0] = 0xffffffffu;
+      mwn[1] = 0xffffffffu;
     }
-    if (active) {
-      const float *sl = reinterpret_cast<const float *>(stage + OFF_L);
-      const float *sd = reinterpret_cast<const float *>(stage + OFF_D);
-      const uint32_t sbase = lds_addr(stage);
-      uint32_t sa[DB][2];
+    const uint32_t sbase = lds_addr(buf);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        sa[db][0] = sbase + toff[db][0];
-        sa[db][1] = sbase + toff[db][1];
+    for (int db = 0; db < DB; ++db) {
+      sa[db][0] = sbase + toff[db][0];
+      sa[db][1] = sbase + toff[db][1];
+    }
+    const float *sl = reinterpret_cast<const float *>(buf + OFF_L) + 4 * hh;
+    const float *sd = reinterpret_cast<const float *>(buf + OFF_D) + 4 * hh;
+    f32x4 l0[4], d0[4], l1[4], d1[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      l0[c] = *reinterpret_cast<const f32x4 *>(sl + 8 * c);
+      d0[c] = *reinterpret_cast<const f32x4 *>(sd + 8 * c);
+    }
+    bf16x8 aq[KS], ao[KS];
+    aq[0] = rows_q(buf, 1, 0);
+    ao[0] = rows_o(buf, 1, 0);
+    aq[1] = rows_q(buf, 1, 1);
+    ao[1] = rows_o(buf, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase 1: A(st, 1) with the exponentials of B(st, 0)
+    f32x16 sa1 = (f32x16){}, dpa1 = (f32x16){};
+    bf16x8 pb0[2], dsb0[2];
+    s16x4 xa[4 * DB], xb[4 * DB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 2 < KS) {
+        aq[ks + 2] = rows_q(buf, 1, ks + 2);
+        ao[ks + 2] = rows_o(buf, 1, ks + 2);
       }
-#pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {
-        // S = Q K^T and dP = dO V^T; the Q and dO row reads run two k-steps
-        // ahead of the products that consume them.
-        f32x16 s = (f32x16){}, dp = (f32x16){};
-        bf16x8 aq[KS], ao[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          aq[ks] = lds_rows(stage, roff[ks] + qh * 32 * T::ROWB);
-          ao[ks] = lds_rows(stage + OFF_DO, roff[ks] + qh * 32 * T::ROWB);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s = mfma32(aq[ks], kv[ks], s);
-          dp = mfma32(ao[ks], vv[ks], dp);
-        }
-        pipeline_reads_mfma<KS>();
-        in_vgpr(s);
-        in_vgpr(dp);
-        if (partial) {  // masked scores -> -inf, so that P = 0 there
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] = keep_or(mw[qh], 8 * (r >> 2) + (r & 3), s[r], kNegInf);
-        }
+      if (ks == KS / 2) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sl + qh * 32 + 8 * c + 4 * hh);
-          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sd + qh * 32 + 8 * c + 4 * hh);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * c + j;
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[j]));
-            s[r] = p;
-            dp[r] = p * (dp[r] - d4[j]);
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS, one 16-row step at a time; the
-        // transposed operands of a step are read while P and dS are converted.
-        auto step = [&](auto tc) {
-          constexpr int t = decltype(tc)::value;  // 16-row step within the tile
-          constexpr int toff = t * 16 * T::ROWB;
-          s16x4 x[4 * DB];
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            x[4 * db + 0] = tr_issue<toff + OFF_DO>(sa[db][0]);
-            x[4 * db + 1] = tr_issue<toff + OFF_DO>(sa[db][1]);
-            x[4 * db + 2] = tr_issue<toff>(sa[db][0]);
-            x[4 * db + 3] = tr_issue<toff>(sa[db][1]);
-          }
-          const bf16x8 pb = c_to_b(s, t & 1);
-          const bf16x8 dsb = c_to_b(dp, t & 1);
-          tr_wait(x);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            dv[db] = mfma32(tr_pair(x[4 * db], x[4 * db + 1]), pb, dv[db]);
-            dk[db] = mfma32(tr_pair(x[4 * db + 2], x[4 * db + 3]), dsb, dk[db]);
-          }
-        };
-        if (qh == 0) {
-          step(std::integral_constant<int, 0>{});
-          step(std::integral_constant<int, 1>{});
-        } else {
-          step(std::integral_constant<int, 2>{});
-          step(std::integral_constant<int, 3>{});
+          l1[c] = *reinterpret_cast<const f32x4 *>(sl + 32 + 8 * c);
+          d1[c] = *reinterpret_cast<const f32x4 *>(sd + 32 + 8 * c);
         }
       }
+      sa1 = mfma32(aq[ks], kv[ks], sa1);
+      dpa1 = mfma32(ao[ks], vv[ks], dpa1);
+#pragma unroll
+      for (int i = 0; i < 16 / KS; ++i) {
+        const int r = ks * (16 / KS) + i;
+        b_exp(s0, dp0, r, l0[r >> 2][r & 3], d0[r >> 2][r & 3]);
+      }
+      if ((ks + 1) * (16 / KS) == 8) b_pack(s0, dp0, 0, pb0[0], dsb0[0]);
+      if (ks == KS - 1) {
+        b_pack(s0, dp0, 1, pb0[1], dsb0[1]);
+        issue_tr(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, xa);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+
+    // ---- phase 2: C(st, 0) with B(st, 1): AGPR reads and mask of all rows,
+    // exponentials of rows 0-7 (the mask word is all ones on full stages:
+    // a select costs less than splitting the chunk sequence by a branch)
+    f32x16 s1, dp1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int tt = c / DB, db = c % DB;
+      if (c == 0) {
+        tr_wait(xa);
+        issue_tr(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, xb);
+      }
+      if (c == DB) tr_wait(xb);
+      if (tt == 0) c_chunk(xa, db, pb0[0], dsb0[0]);
+      else c_chunk(xb, db, pb0[1], dsb0[1]);
+#pragma unroll
+      for (int i = 0; i < 16 / NC; ++i) {
+        const int r = c * (16 / NC) + i;
+        b_read(s1, dp1, sa1, dpa1, r);
+        b_mask(s1, mwc[1], r);
+      }
+#pragma unroll
+      for (int i = 0; i < 8 / NC; ++i) {
+        const int r = c * (8 / NC) + i;
+        b_exp(s1, dp1, r, l1[r >> 2][r & 3], d1[r >> 2][r & 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bf16x8 pb1[2], dsb1[2];
+    b_pack(s1, dp1, 0, pb1[0], dsb1[0]);
+
+    // stage st + 1 is in LDS for every wave, and stage st - 1's buffer is free
     dma_wait();
     __syncthreads();
+    if (st + 2 < nst) load_stage(st + 2, smem + fre * STAGE);
+    aq[0] = rows_q(nbuf, 0, 0);
+    ao[0] = rows_o(nbuf, 0, 0);
+    aq[1] = rows_q(nbuf, 0, 1);
+    ao[1] = rows_o(nbuf, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase 3a: A(st + 1, 0) with the exponentials of B(st, 1) rows 8-15
+    // (after the last stage A reads a stale buffer and is discarded)
+    f32x16 sa0 = (f32x16){}, dpa0 = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 2 < KS) {
+        aq[ks + 2] = rows_q(nbuf, 0, ks + 2);
+        ao[ks + 2] = rows_o(nbuf, 0, ks + 2);
+      }
+      sa0 = mfma32(aq[ks], kv[ks], sa0);
+      dpa0 = mfma32(ao[ks], vv[ks], dpa0);
+#pragma unroll
+      for (int i = 0; i < 8 / KS; ++i) {
+        const int r = 8 + ks * (8 / KS) + i;
+        b_exp(s1, dp1, r, l1[r >> 2][r & 3], d1[r >> 2][r & 3]);
+      }
+      if (ks == KS - 2) issue_tr(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, xa);
+      if (ks == KS - 1) b_pack(s1, dp1, 1, pb1[1], dsb1[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- phase 3b: C(st, 1) with B(st + 1, 0): AGPR reads and mask
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int tt = c / DB, db = c % DB;
+      if (c == 0) {
+        tr_wait(xa);
+        issue_tr(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, xb);
+      }
+      if (c == DB) tr_wait(xb);
+      if (tt == 0) c_chunk(xa, db, pb1[0], dsb1[0]);
+      else c_chunk(xb, db, pb1[1], dsb1[1]);
+#pragma unroll
+      for (int i = 0; i < 16 / NC; ++i) {
+        const int r = c * (16 / NC) + i;
+        b_read(s0, dp0, sa0, dpa0, r);
+        b_mask(s0, mwn[0], r);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mwc[0] = mwn[0];
+    mwc[1] = mwn[1];
+    cur = nxt;
   }
 
   if (key_ok) {

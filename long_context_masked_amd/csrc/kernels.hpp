@@ -277,6 +277,30 @@ __device__ __forceinline__ void pipeline_reads_mfma() {
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
+// Interleave pattern for a block that pairs NM MFMAs with VALU work of an
+// independent softmax step: NDS0 DS reads first, then each MFMA followed by
+// NV VALU instructions and, for the first NDS1 MFMAs, one more DS read.
+// Issuing VALU between MFMAs is what lets the two run concurrently: a wave
+// stalls at an MFMA while the matrix pipe is still busy with the previous one.
+template <int NDS0, int NM, int NV, int NDS1>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NDS0, 0);  // DS read
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+    if (i < NDS1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+// Uniform read-only data (work lists, items) read through the constant
+// address space is fetched with scalar loads, which complete on their own
+// counter instead of queueing behind in-flight global -> LDS tile loads.
+template <class X>
+__device__ __forceinline__ const __attribute__((address_space(4))) X *as_const(const X *p) {
+  return (const __attribute__((address_space(4))) X *)p;
+}
+
 // The A operand formed by two transposed reads (rows +0 and +8 of a k-step).
 __device__ __forceinline__ bf16x8 tr_pair(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
