@@ -17,6 +17,8 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +30,17 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 METRIC = "effective masked-attention TFLOP/s fwd+bwd (fraction of bf16 MFMA peak)"
+
+# HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
+# this script (FETCH_SIZE, then WRITE_SIZE) with --copy-calibration-mib: the
+# counters of a plain device copy of known size in the same process give the
+# scale from counter units to bytes.  --summarize-traffic turns the two
+# counter files into TRAFFIC_FILE, tagged with a hash of the kernel's sources;
+# the figure is reported only while the sources still hash the same.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dkdv_dense.json")
+TRAFFIC_SOURCES = ["long_context_masked_amd/csrc/bwd.hip", "long_context_masked_amd/csrc/kernels.hpp"]
+TRAFFIC_KERNEL = "attn_dkdv_kernel"
+COPY_KERNEL_HINT = "copy"
 
 # Algorithmic work per allowed (i, j) pair per query head, in units of d
 # flops, of each kernel: forward = Q K^T + P V; dK/dV pass = Q K^T, dO V^T,
@@ -100,6 +113,65 @@ def cpu_baseline(seconds_cap=30.0):
                       f"masks {done}: {secs:.1f} s, effective flops as for the GPU"}
 
 
+def sources_sha256():
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _counter_rows(path, counter):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], int(r.get("Dispatch_Id", 0) or 0),
+                             float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_traffic(fetch_csv, write_csv, copy_mib, workload_desc, commands):
+    """Average HBM bytes per launch of the dominant kernel, from the two
+    counter files (values in KiB per dispatch), each scaled by what the same
+    counter reads for the calibration copy (copy_mib MiB read, copy_mib MiB
+    written)."""
+    out = {"kernel": TRAFFIC_KERNEL, "workload": workload_desc, "copy_mib": copy_mib,
+           "commands": commands, "source_sha256": sources_sha256(), "sources": TRAFFIC_SOURCES}
+    known = copy_mib * 1024.0  # KiB
+    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = _counter_rows(path, counter)
+        agg = {}
+        for kname, did, val in rows:   # sum over counter instances of a dispatch
+            agg.setdefault((kname, did), 0.0)
+            agg[(kname, did)] += val
+        copies = [v for (k, _), v in agg.items() if COPY_KERNEL_HINT in k.lower() and "attn" not in k]
+        kern = [v for (k, _), v in agg.items() if TRAFFIC_KERNEL in k]
+        if not copies or not kern:
+            raise SystemExit(f"{path}: no calibration copy or no {TRAFFIC_KERNEL} dispatches")
+        copy_kib = max(copies)
+        factor = known / copy_kib
+        mean_kib = sum(kern) / len(kern)
+        out[name] = {"counter": counter, "copy_kib": round(copy_kib, 1), "factor": round(factor, 4),
+                     "kernel_dispatches": len(kern), "kernel_mean_kib_raw": round(mean_kib, 1),
+                     "bytes_per_launch": round(mean_kib * factor * 1024.0)}
+    out["bytes_per_launch"] = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
+    return out
+
+
+def traffic_for(desc):
+    """Bytes per launch of the dominant kernel if the stored counters were
+    taken on this workload with the current kernel sources, else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != sources_sha256() or t.get("workload") != desc:
+        return None
+    return t.get("bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,7 +180,21 @@ def main():
     ap.add_argument("--workload", default="dense", choices=["dense", "document", "hetero", "sparse"])
     ap.add_argument("--seqs", default="1024,8192,16384,49152")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size before warmup (counter scale)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic file from two counter runs and exit (no GPU)")
+    ap.add_argument("--traffic-commands", default="", help="commands recorded in the traffic file")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        seqs = [int(s) for s in args.seqs.split(",") if s]
+        _, desc = workload(args.workload, seqs)
+        t = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
+                              args.copy_calibration_mib, desc, args.traffic_commands)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -184,6 +270,16 @@ def main():
                 ev[4].record(stream)
                 r.setdefault("events", []).append(ev)
 
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.copy_calibration_mib} MiB done")
+        del src, dst
+
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         one_step(False)
@@ -249,7 +345,8 @@ def main():
         "kernel_ms_per_launch": {k: round(kern[k] / launches[k] * 1e3, 4) for k in kern},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for(desc) if dom == "dkdv" else None},
         "plan_build_s": round(plan_secs, 3),
         "detail": detail,
     }

@@ -118,7 +118,8 @@ struct Tile {
   static constexpr int BYTES = 64 * ROWB;
   static constexpr int RPK = 1024 / ROWB;       // rows per 1 KiB load instruction
   static constexpr int LPR = 64 / RPK;          // lanes per row in one instruction
-  static constexpr int NI = BYTES / 1024 / 4;   // load instructions per wave (4 waves)
+  template <int NW>
+  static constexpr int NI = BYTES / 1024 / NW;  // load instructions per wave (NW waves)
   __device__ static __forceinline__ int swz(int r) {
     if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
     else return ((r & 3) << 1) | ((r >> 2) & 1);
@@ -129,16 +130,18 @@ struct Tile {
 };
 
 // Issue the loads of rows row0 + [0, 64) of a [.., ld] bf16 matrix into the
-// LDS tile at `dst`.  Rows >= nrows repeat row nrows - 1 (finite values; the
-// kernels mask them).  Completion: s_waitcnt vmcnt(0) then a barrier.
-template <int D>
+// LDS tile at `dst`, shared by the NW waves of the workgroup.  Rows >= nrows
+// repeat row nrows - 1 (finite values; the kernels mask them).  Completion:
+// s_waitcnt vmcnt(0) then a barrier.
+template <int D, int NW = 4>
 __device__ __forceinline__ void dma_tile(char *dst, const bf16 *base, int64_t ld, int row0,
                                          int nrows) {
   using T = Tile<D>;
+  constexpr int NI = T::template NI<NW>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < T::NI; ++i) {
-    const int blk = wave * T::NI + i;
+  for (int i = 0; i < NI; ++i) {
+    const int blk = wave * NI + i;
     const int row = blk * T::RPK + lane / T::LPR;
     const int c = (lane % T::LPR) ^ T::swz(row);
     int grow = row0 + row;
@@ -155,9 +158,10 @@ __device__ __forceinline__ void dma_tile(char *dst, const bf16 *base, int64_t ld
 // of the lane's NI load instructions fetches, and the wave index is made
 // uniform so that each load takes a scalar base plus a 32-bit lane offset.
 // Tiles that extend past nrows (the ragged last tile) use dma_tile instead.
-template <int D>
+template <int D, int NW = 4>
 struct TileDma {
-  uint32_t off[Tile<D>::NI];
+  static constexpr int NI = Tile<D>::template NI<NW>;
+  uint32_t off[NI];
   int lds0;  // byte offset of this wave's first 1 KiB block in the tile
 
   __device__ __forceinline__ void init(int64_t ld) {
@@ -165,12 +169,12 @@ struct TileDma {
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < T::NI; ++i) {
-      const int row = (wave * T::NI + i) * T::RPK + lane / T::LPR;
+    for (int i = 0; i < NI; ++i) {
+      const int row = (wave * NI + i) * T::RPK + lane / T::LPR;
       const int c = (lane % T::LPR) ^ T::swz(row);
       off[i] = (uint32_t)(row * ld * 2 + c * 16);
     }
-    lds0 = wave * T::NI * 1024;
+    lds0 = wave * NI * 1024;
   }
 
   __device__ __forceinline__ void load(char *dst, const bf16 *base, int64_t ld, int row0,
@@ -179,14 +183,14 @@ struct TileDma {
     if (row0 + 64 <= nrows) {
       const char *g = reinterpret_cast<const char *>(base + (int64_t)row0 * ld);
 #pragma unroll
-      for (int i = 0; i < T::NI; ++i)
+      for (int i = 0; i < NI; ++i)
         __builtin_amdgcn_global_load_lds(
             g + off[i],
             (__attribute__((address_space(3))) void *)(
                 (__attribute__((address_space(3))) char *)dst + lds0 + i * 1024),
             16, 0, 0);
     } else {
-      dma_tile<D>(dst, base, ld, row0, nrows);
+      dma_tile<D, NW>(dst, base, ld, row0, nrows);
     }
   }
 };

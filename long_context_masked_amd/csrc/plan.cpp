@@ -289,6 +289,41 @@ int64_t nnz_with_bitmap(int64_t S, const std::vector<Run> &rb, const Bitmap &bm,
 
 struct Item { int32_t tile, head, off, len; double cost; };
 
+// Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin in
+// launch order, so item b runs on XCD b % 8.  Items of one KV head stream
+// the same K/V (forward, dQ) or Q/dO (dK/dV) tiles; giving each XCD the items
+// of as few KV heads as possible lets its L2 serve those tiles to all of its
+// workgroups.  v is in longest-first order.  When Hkv is a multiple of 8,
+// XCD x takes the heads h with h % 8 == x; when Hkv divides 8, each head's
+// items go to the least-loaded of the XCDs congruent to it modulo Hkv (the
+// longest-processing-time rule within that set).  Otherwise the order is
+// left as it is.  Each XCD's share stays in longest-first order.
+constexpr int kXcds = 8;
+void xcd_interleave(std::vector<Item> &v, int64_t Hkv, int64_t heads_per_kv) {
+  const bool by_mod = Hkv % kXcds == 0;
+  const bool spread = kXcds % Hkv == 0;
+  if (!by_mod && !spread) return;
+  std::vector<std::vector<Item>> q(kXcds);
+  std::vector<double> load(kXcds, 0.0);
+  for (const Item &x : v) {
+    const int64_t kvh = x.head / heads_per_kv;
+    int64_t slot = kvh % kXcds;
+    if (!by_mod) {
+      for (int64_t c = kvh; c < kXcds; c += Hkv)
+        if (load[(size_t)c] < load[(size_t)slot]) slot = c;
+    }
+    q[(size_t)slot].push_back(x);
+    load[(size_t)slot] += x.cost;
+  }
+  v.clear();
+  for (size_t i = 0;; ++i) {
+    bool any = false;
+    for (int x = 0; x < kXcds; ++x)
+      if (i < q[x].size()) { v.push_back(q[x][i]); any = true; }
+    if (!any) break;
+  }
+}
+
 }  // namespace
 }  // namespace lcm
 
@@ -416,6 +451,11 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
         npart += part;
         bwd_list.push_back((uint32_t)I | (part ? kPartialBit : 0u));
       }
+      // Descending Q-tile order: the items of a K-tile band that run at once
+      // then all start from the last Q-tiles (which every lower-triangular or
+      // banded mask shares) and move down together, so the Q/dO tiles they
+      // stream are fetched once per L2.
+      std::reverse(bwd_list.begin() + bwd_off[slot], bwd_list.end());
       bwd_len[slot] = (int32_t)(bwd_list.size() - bwd_off[slot]);
       bwd_npart[slot] = npart;
     }
@@ -456,6 +496,8 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   auto by_cost = [](const Item &a, const Item &b) { return a.cost > b.cost; };
   std::stable_sort(fi.begin(), fi.end(), by_cost);
   std::stable_sort(bi.begin(), bi.end(), by_cost);
+  xcd_interleave(fi, sh.Hkv, G);  // forward items carry their first query head
+  xcd_interleave(bi, sh.Hkv, 1);  // dK/dV items carry their KV head
 
   // blob layout
   Layout &L = p->lay;

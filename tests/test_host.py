@@ -170,9 +170,13 @@ def _lpt_makespan(costs, m):
 
 @pytest.mark.parametrize("family", ["causal", "causal_document", "block64_50"])
 def test_schedule_is_longest_first(family):
-    """Items are issued longest first, which bounds the list-scheduling
-    makespan by Graham's LPT bound 4/3 * max(total/m, largest item)."""
+    """Workgroups are dealt to the 8 XCDs round-robin, so item b runs on XCD
+    b % 8.  Each XCD's share holds the items of its KV heads (head h % 8, or
+    h % Hkv when Hkv divides 8) in longest-first order, which bounds each
+    XCD's list-scheduling makespan by Graham's LPT bound 4/3 * max(total/m,
+    largest item); the shares are balanced to within a few percent."""
     S, Hq, Hkv = 4096, 16, 2
+    G = Hq // Hkv
     if family == "causal":
         spec = syn.spec_causal(S)
     elif family == "causal_document":
@@ -182,17 +186,25 @@ def test_schedule_is_longest_first(family):
         spec = syn.with_bitmap(syn.spec_full(S), offs, offs, bits)
     p = lcm.Plan(1, S, Hq, Hkv, 128, spec)
     lay = p.layout()
-    for items, lst in ((lay["fwd_items"], lay["fwd_list"]), (lay["bwd_items"], lay["bwd_list"])):
-        costs = []
-        for _, _, off, n in items:
+    for kind, items, lst in (("fwd", lay["fwd_items"], lay["fwd_list"]),
+                             ("bwd", lay["bwd_items"], lay["bwd_list"])):
+        costs, kvh = [], []
+        for _, head, off, n in items:
             e = lst[off:off + n]
             npart = int((e >> 31).sum())
             costs.append((n - npart) + 1.25 * npart)
-        costs = np.array(costs)
-        assert (np.diff(costs) <= 1e-9).all(), "items not in non-increasing cost order"
-        for m in (64, 256, 512):
-            bound = 4.0 / 3.0 * max(costs.sum() / m, costs.max())
-            assert _lpt_makespan(costs, m) <= bound + 1e-9
+            kvh.append(head // G if kind == "fwd" else head)
+        costs, kvh = np.array(costs), np.array(kvh)
+        xcd = np.arange(len(costs)) % 8
+        assert (kvh == xcd % Hkv).all(), "items not grouped by KV head per XCD"
+        totals = np.array([costs[x::8].sum() for x in range(8)])
+        assert totals.max() <= 1.05 * totals.mean()
+        for x in range(8):
+            share = costs[x::8]
+            assert (np.diff(share) <= 1e-9).all(), "XCD share not in non-increasing cost order"
+            for m in (8, 32, 64):
+                bound = 4.0 / 3.0 * max(share.sum() / m, share.max())
+                assert _lpt_makespan(share, m) <= bound + 1e-9
 
 
 def _status(fn):
