@@ -70,8 +70,11 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
 // from the same tiles by transposed reads.  Each stage is two 32-row units,
 // and each unit u takes three steps:
 //   A(u): S = Q K^T, dP = dO V^T                          (MFMA)
-//   B(u): mask, P = exp2(S c - lse2), dS = P (dP - D)     (VALU)
+//   B(u): P = exp2(S c - lse2), dS = P (dP - D)           (VALU)
 //   C(u): dV^T += dO^T P, dK^T += Q^T dS                   (MFMA)
+// Masking costs nothing on stages without masked entries: on a partial
+// stage the accumulation of S starts at -inf on the masked entries (and at
+// 0 elsewhere), so that their P is 0.
 // One wave runs per SIMD, so the exponentials only overlap the products if
 // the wave's own instruction stream alternates them: a wave stalls at an
 // MFMA while the matrix pipe is busy with the previous one, but VALU work
@@ -80,10 +83,10 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
 // written as a fixed sequence of chunks (two MFMAs plus a slice of B's VALU
 // work) fenced against reordering:
 //   phase 1:  A(st, 1)     with B(st, 0)           (exponentials)
-//   phase 2:  C(st, 0)     with B(st, 1) rows 0-15 (AGPR reads, mask) and
+//   phase 2:  C(st, 0)     with B(st, 1) rows 0-15 (AGPR reads) and
 //                               rows 0-7 (exponentials)
 //   phase 3a: A(st + 1, 0) with B(st, 1) rows 8-15 (exponentials)
-//   phase 3b: C(st, 1)     with B(st + 1, 0)       (AGPR reads, mask)
+//   phase 3b: C(st, 1)     with B(st + 1, 0)       (AGPR reads)
 // ("rows" are the 16 accumulator registers of a unit.)  Phase 3 reads the
 // next stage's tiles, so stages rotate through three LDS buffers: the
 // barrier before phase 3 publishes stage st + 1 and frees the buffer of
@@ -165,13 +168,14 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   };
 
   // Allowed-row words of the lane's key for the two units of stage st (all
-  // ones unless the tile is partial).
-  auto stage_mask = [&](int st, uint32_t (&mw)[2]) {
+  // ones unless the tile is partial); returns whether it is partial.
+  auto stage_mask = [&](int st, uint32_t (&mw)[2]) -> bool {
     const int e = st / G, g = st - e * G;
     const uint32_t ent = list[e];
     mw[0] = 0xffffffffu;
     mw[1] = 0xffffffffu;
-    if (ent >> 31) {
+    const bool part = (ent >> 31) != 0;
+    if (part) {
       const int qt = (int)(ent & 0x7fffffffu);
       const int hm = bitmap_head(a.m.bm_heads, kvh * G + g, a.Hq, G);
       const uint64_t mk = key_ok ? col_mask(a.m, cb, kblk, hm, qt * 64, S) : 0ull;
@@ -179,6 +183,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       mw[0] = (uint32_t)sh;
       mw[1] = (uint32_t)(sh >> 32);
     }
+    return part;
   };
 
   // The row operands of k-step ks of unit qh of `buf`.
@@ -216,11 +221,6 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   // (Each result is pinned where it is computed: the values are consumed
   // phases later, and without the pins the compiler sinks the arithmetic
   // next to its uses, undoing the interleave.)
-  auto b_mask = [&](f32x16 &s, uint32_t mw, int r) {
-    float x = keep_or(mw, 8 * (r >> 2) + (r & 3), s[r], kNegInf);
-    in_vgpr(x);
-    s[r] = x;
-  };
   auto b_exp = [&](f32x16 &s, f32x16 &dp, int r, float l, float d) {
     float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l));
     float ds = p * (dp[r] - d);
@@ -236,25 +236,37 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     in_vgpr(dsb);
   };
 
-  f32x16 s0, dp0;  // unit (st, 0): S and dP in VGPRs, masked
+  // First k-step of S of a unit: the accumulation starts at 0, or, when the
+  // stage is partial, at -inf on the masked entries, so that their P is 0.
+  // The branch keeps the bias (and its accumulator writes) off full stages.
+  auto s_first = [&](bf16x8 aq0, bool part, uint32_t mw) -> f32x16 {
+    if (part) {
+      __asm__ volatile("");
+      f32x16 bias;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bias[r] = keep_or(mw, 8 * (r >> 2) + (r & 3), 0.f, kNegInf);
+      return mfma32(aq0, kv[0], bias);
+    }
+    return mfma32(aq0, kv[0], (f32x16){});
+  };
+
+  f32x16 s0, dp0;  // unit (st, 0): S and dP in VGPRs
   uint32_t mwc[2], mwn[2];
+  bool pc = false, pn = false;  // stages st and st + 1 are partial
   if (nst > 0) {
     load_stage(0, smem);
     if (nst > 1) load_stage(1, smem + STAGE);
-    stage_mask(0, mwc);
+    pc = stage_mask(0, mwc);
     dma_wait();
     __syncthreads();
-    f32x16 sa0 = (f32x16){}, dpa0 = (f32x16){};
+    f32x16 sa0 = s_first(rows_q(smem, 0, 0), pc, mwc[0]), dpa0 = (f32x16){};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      sa0 = mfma32(rows_q(smem, 0, ks), kv[ks], sa0);
+      if (ks > 0) sa0 = mfma32(rows_q(smem, 0, ks), kv[ks], sa0);
       dpa0 = mfma32(rows_o(smem, 0, ks), vv[ks], dpa0);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      b_read(s0, dp0, sa0, dpa0, r);
-      b_mask(s0, mwc[0], r);
-    }
+    for (int r = 0; r < 16; ++r) b_read(s0, dp0, sa0, dpa0, r);
   }
 
   int cur = 0;  // buffer of stage st
@@ -268,8 +280,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     const char *buf = smem + cur * STAGE;
     const char *nbuf = smem + nxt * STAGE;
     if (st + 1 < nst) {
-      stage_mask(st + 1, mwn);
+      pn = stage_mask(st + 1, mwn);
     } else {
+      pn = false;
       mwn[0] = 0xffffffffu;
       mwn[1] = 0xffffffffu;
     }
@@ -295,7 +308,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- phase 1: A(st, 1) with the exponentials of B(st, 0)
-    f32x16 sa1 = (f32x16){}, dpa1 = (f32x16){};
+    f32x16 sa1 = s_first(aq[0], pc, mwc[1]), dpa1 = (f32x16){};
     bf16x8 pb0[2], dsb0[2];
     s16x4 xa[4 * DB], xb[4 * DB];
 #pragma unroll
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
           d1[c] = *reinterpret_cast<const f32x4 *>(sd + 32 + 8 * c);
         }
       }
-      sa1 = mfma32(aq[ks], kv[ks], sa1);
+      if (ks > 0) sa1 = mfma32(aq[ks], kv[ks], sa1);
       dpa1 = mfma32(ao[ks], vv[ks], dpa1);
 #pragma unroll
       for (int i = 0; i < 16 / KS; ++i) {
@@ -326,9 +339,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- phase 2: C(st, 0) with B(st, 1): AGPR reads and mask of all rows,
-    // exponentials of rows 0-7 (the mask word is all ones on full stages:
-    // a select costs less than splitting the chunk sequence by a branch)
+    // ---- phase 2: C(st, 0) with B(st, 1): AGPR reads of all rows,
+    // exponentials of rows 0-7
     f32x16 s1, dp1;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -344,7 +356,6 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       for (int i = 0; i < 16 / NC; ++i) {
         const int r = c * (16 / NC) + i;
         b_read(s1, dp1, sa1, dpa1, r);
-        b_mask(s1, mwc[1], r);
       }
 #pragma unroll
       for (int i = 0; i < 8 / NC; ++i) {
@@ -368,14 +379,14 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 
     // ---- phase 3a: A(st + 1, 0) with the exponentials of B(st, 1) rows 8-15
     // (after the last stage A reads a stale buffer and is discarded)
-    f32x16 sa0 = (f32x16){}, dpa0 = (f32x16){};
+    f32x16 sa0 = s_first(aq[0], pn, mwn[0]), dpa0 = (f32x16){};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 2 < KS) {
         aq[ks + 2] = rows_q(nbuf, 0, ks + 2);
         ao[ks + 2] = rows_o(nbuf, 0, ks + 2);
       }
-      sa0 = mfma32(aq[ks], kv[ks], sa0);
+      if (ks > 0) sa0 = mfma32(aq[ks], kv[ks], sa0);
       dpa0 = mfma32(ao[ks], vv[ks], dpa0);
 #pragma unroll
       for (int i = 0; i < 8 / KS; ++i) {
@@ -387,7 +398,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- phase 3b: C(st, 1) with B(st + 1, 0): AGPR reads and mask
+    // ---- phase 3b: C(st, 1) with B(st + 1, 0): AGPR reads
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int tt = c / DB, db = c % DB;
@@ -402,12 +413,12 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       for (int i = 0; i < 16 / NC; ++i) {
         const int r = c * (16 / NC) + i;
         b_read(s0, dp0, sa0, dpa0, r);
-        b_mask(s0, mwn[0], r);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     mwc[0] = mwn[0];
     mwc[1] = mwn[1];
+    pc = pn;
     cur = nxt;
   }
 
