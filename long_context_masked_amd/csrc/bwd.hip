@@ -455,7 +455,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
   constexpr int STAGE = 2 * T::BYTES;  // K tile, then V tile
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int ln = lane & 31, hh = lane >> 5;
   const int4 item = a.fitems[blockIdx.x];
   const int b = blockIdx.y;
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
   for (int i = 0; i < DB; ++i) dq[i] = (f32x16){};
   const float sl2 = a.sl2;
 
-  const uint32_t *list = a.flist + item.z;
+  const auto *list = as_const(a.flist + item.z);
   const int n = item.w;
   TileDma<D> dma;
   dma.init(ldk);

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int STAGE = 2 * T::BYTES;  // K tile, then V tile
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int ln = lane & 31, hh = lane >> 5;
   const int4 item = a.items[blockIdx.x];
   const int b = blockIdx.y;
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   float m_run = kMinit, l_run = 0.f;
   const float sl2 = a.sl2;
 
-  const uint32_t *list = a.list + item.z;
+  const auto *list = as_const(a.list + item.z);
   const int n = item.w;
   TileDma<D> dma;
   dma.init(ldk);
@@ -82,15 +82,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   dma_wait();
   __syncthreads();
 
-  for (int e = 0; e < n; ++e) {
+  // One K-tile, read from buffer BUF (tiles alternate between the two
+  // buffers; with BUF a constant the buffer offset folds into the LDS
+  // instructions' immediate offsets).
+  auto tile = [&](int e, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const uint32_t ent = list[e];
     const int kt = (int)(ent & 0x7fffffffu);
     const bool partial = (ent >> 31) != 0;
-    char *stage = smem + (e & 1) * STAGE;
+    char *stage = smem + BUF * STAGE;
     if (e + 1 < n) {
       // the other buffer was last read before the previous barrier
       const int nkt = (int)(list[e + 1] & 0x7fffffffu);
-      char *next = smem + ((e + 1) & 1) * STAGE;
+      char *next = smem + (1 - BUF) * STAGE;
       dma.load(next, kbase, ldk, nkt * 64, S);
       dma.load(next + T::BYTES, vbase, ldk, nkt * 64, S);
     }
@@ -181,7 +185,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 
     dma_wait();
     __syncthreads();
+  };
+  int e = 0;
+  for (; e + 1 < n; e += 2) {
+    tile(e, std::integral_constant<int, 0>{});
+    tile(e + 1, std::integral_constant<int, 1>{});
   }
+  if (e < n) tile(e, std::integral_constant<int, 0>{});
 
   const float l_tot = sum_halves(l_run);
   if (row_ok) {
