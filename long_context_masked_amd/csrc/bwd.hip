@@ -513,14 +513,25 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
   dma_wait();
   __syncthreads();
 
-  for (int e = 0; e < n; ++e) {
+  // One K-tile, read from buffer BUF (tiles alternate between the two
+  // buffers; with BUF a constant the buffer offset folds into the LDS
+  // instructions' immediate offsets).
+  const uint32_t sbase = lds_addr(smem);
+  uint32_t ka[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    ka[db][0] = sbase + koff[db][0];
+    ka[db][1] = sbase + koff[db][1];
+  }
+  auto tile = [&](int e, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const uint32_t ent = list[e];
     const int kt = (int)(ent & 0x7fffffffu);
     const bool partial = (ent >> 31) != 0;
-    char *stage = smem + (e & 1) * STAGE;
+    char *stage = smem + BUF * STAGE;
     if (e + 1 < n) {
       const int nkt = (int)(list[e + 1] & 0x7fffffffu);
-      char *next = smem + ((e + 1) & 1) * STAGE;
+      char *next = smem + (1 - BUF) * STAGE;
       dma.load(next, kbase, ldk, nkt * 64, S);
       dma.load(next + T::BYTES, vbase, ldk, nkt * 64, S);
     }
@@ -534,13 +545,6 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
       mw[1] = (uint32_t)(sh >> 32);
     }
     if (active) {
-      const uint32_t sbase = lds_addr(stage);
-      uint32_t ka[DB][2];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        ka[db][0] = sbase + koff[db][0];
-        ka[db][1] = sbase + koff[db][1];
-      }
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         f32x16 s = (f32x16){}, dp = (f32x16){};
@@ -561,7 +565,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
         // dQ^T += K^T dS^T, one 16-key step at a time.
         auto step = [&](auto tc) {
           constexpr int t = decltype(tc)::value;  // 16-key step within the tile
-          constexpr int toff = t * 16 * T::ROWB;
+          constexpr int toff = BUF * STAGE + t * 16 * T::ROWB;
           s16x4 x[2 * DB];
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
@@ -584,7 +588,13 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
     }
     dma_wait();
     __syncthreads();
+  };
+  int e = 0;
+  for (; e + 1 < n; e += 2) {
+    tile(e, std::integral_constant<int, 0>{});
+    tile(e + 1, std::integral_constant<int, 1>{});
   }
+  if (e < n) tile(e, std::integral_constant<int, 0>{});
 
   if (row_ok) {
     bf16 *qrow = a.dq + ((int64_t)b * S + row) * ldq + (int64_t)h * D;
