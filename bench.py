@@ -56,6 +56,7 @@ def workload(name, seqs):
     import synthetic as syn
     out = []
     if name == "dense":
+        seqs = seqs or [1024, 8192, 16384, 49152]
         for S in seqs:
             for label, spec in syn.config_mask_specs("dense", S):
                 out.append((f"S{S // 1024}K_{label}", S, 64, 8, spec))
@@ -178,7 +179,9 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="dense", choices=["dense", "document", "hetero", "sparse"])
-    ap.add_argument("--seqs", default="1024,8192,16384,49152")
+    ap.add_argument("--seqs", default=None,
+                    help="comma-separated sequence lengths (dense: default 1024,8192,16384,49152; "
+                         "sparse: first value, default 32768; ignored by document and hetero)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size before warmup (counter scale)")
@@ -187,7 +190,7 @@ def main():
     ap.add_argument("--traffic-commands", default="", help="commands recorded in the traffic file")
     args = ap.parse_args()
     if args.summarize_traffic:
-        seqs = [int(s) for s in args.seqs.split(",") if s]
+        seqs = [int(x) for x in args.seqs.split(",") if x] if args.seqs else []
         _, desc = workload(args.workload, seqs)
         t = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
                               args.copy_calibration_mib, desc, args.traffic_commands)
@@ -207,7 +210,7 @@ def main():
     import synthetic as syn
 
     dev = torch.device("cuda:0")
-    seqs = [int(s) for s in args.seqs.split(",") if s]
+    seqs = [int(x) for x in args.seqs.split(",") if x] if args.seqs else []
     cases, desc = workload(args.workload, seqs)
     d = 128
 
