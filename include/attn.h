@@ -161,12 +161,24 @@ typedef struct {
   int64_t off_bwd_items, n_bwd_items;   /* int32 [n][4]: tile, kvh, off, len */
   int64_t off_bwd_list, n_bwd_list;     /* uint32 [n]                      */
   int64_t off_bits, off_qblk, off_kblk, off_qoffs, off_koffs; /* -1 if none */
+  /* int32 [n_bwd_items], parallel to the dK/dV items: the partial slot of an
+   * item that is one chunk of a split (K-tile, KV head), or -1 when the item
+   * writes dK/dV itself.  The chunks of a split item list consecutive runs
+   * of its Q-tiles, in slot order. */
+  int64_t off_bwd_slot;
+  /* int32 [n][4]: K-tile, KV head, first slot, number of chunks, for each
+   * dK/dV item split into chunks whose partial results are summed. */
+  int64_t off_bwd_reduce, n_bwd_reduce;
+  int64_t n_slots;                      /* partial slots per batch entry    */
 } attn_plan_layout;
 
 attn_status attn_plan_get_layout(const attn_plan *plan, attn_plan_layout *out);
 
 /* Bytes of device workspace attn_bwd needs: per (b, h, row) the fp32 values
- * LSE * log2(e) and D = rowsum(dO * O), rows padded to a multiple of 64. */
+ * LSE * log2(e) and D = rowsum(dO * O), rows padded to a multiple of 64,
+ * then, when the plan split long dK/dV work items into chunks (small S, or
+ * key columns seen by every row), fp32 partial dK and dV of 128 keys per
+ * chunk slot and batch entry. */
 size_t attn_bwd_workspace_bytes(const attn_plan *plan);
 
 /*

@@ -90,6 +90,9 @@ class Plan:
             "fwd_list": raw[lay.off_fwd_list:lay.off_fwd_list + 4 * lay.n_fwd_list].view(np.uint32),
             "bwd_items": i32(lay.off_bwd_items, 4 * lay.n_bwd_items).reshape(-1, 4),
             "bwd_list": raw[lay.off_bwd_list:lay.off_bwd_list + 4 * lay.n_bwd_list].view(np.uint32),
+            "bwd_slot": i32(lay.off_bwd_slot, lay.n_bwd_items),
+            "bwd_reduce": i32(lay.off_bwd_reduce, 4 * lay.n_bwd_reduce).reshape(-1, 4),
+            "n_slots": int(lay.n_slots),
         }
         return out
 

@@ -15,6 +15,8 @@ hipError_t launch_dq(const BwdArgs &a, int d, int HG, int B, hipStream_t st);
 
 using namespace lcm;
 
+static_assert(kDkdvKeys == kBwdKeyTile, "dK/dV tile width of the kernels and the plan");
+
 namespace {
 
 template <typename T>
@@ -141,8 +143,15 @@ BwdArgs bwd_args(const attn_plan *p, const void *q, const void *k, const void *v
   a.flist = sect<uint32_t>(p, p->lay.fwd_list);
   a.bitems = sect<int4>(p, p->lay.bwd_items);
   a.blist = sect<uint32_t>(p, p->lay.bwd_list);
+  a.bslot = sect<int>(p, p->lay.bwd_slot);
+  a.breduce = sect<int4>(p, p->lay.bwd_reduce);
+  a.part = ws ? reinterpret_cast<float *>(static_cast<char *>(const_cast<void *>(ws)) +
+                                          ws_stats_bytes(p))
+              : nullptr;
   a.n_fitems = (int)p->lay.n_fwd_items;
   a.n_bitems = (int)p->lay.n_bwd_items;
+  a.n_breduce = (int)p->lay.n_bwd_reduce;
+  a.n_slots = (int)p->lay.n_slots;
   a.m = mask_args(p);
   return a;
 }

@@ -108,6 +108,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int ln = lane & 31, hh = lane >> 5;
   const int4 item = a.bitems[blockIdx.x];
+  const int slot = *as_const(a.bslot + blockIdx.x);  // >= 0: one chunk of a split item
   const int b = blockIdx.y;
   const int S = a.S, G = a.G;
   const int kvh = item.y;
@@ -422,7 +423,22 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     cur = nxt;
   }
 
-  if (key_ok) {
+  if (slot >= 0) {
+    // a chunk of a split item: unscaled fp32 partial sums into its slot
+    float *pk = a.part + (((int64_t)b * a.n_slots + slot) * 2) * kDkdvKeys * D +
+                (int64_t)(wave * 32 + ln) * D;
+    float *pv = pk + (int64_t)kDkdvKeys * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d0 = db * 32 + 8 * c + 4 * hh;
+        *reinterpret_cast<f32x4 *>(pk + d0) =
+            (f32x4){dk[db][4 * c], dk[db][4 * c + 1], dk[db][4 * c + 2], dk[db][4 * c + 3]};
+        *reinterpret_cast<f32x4 *>(pv + d0) =
+            (f32x4){dv[db][4 * c], dv[db][4 * c + 1], dv[db][4 * c + 2], dv[db][4 * c + 3]};
+      }
+  } else if (key_ok) {
     const int64_t off = ((int64_t)b * S + key) * ldk + (int64_t)kvh * D;
     const float sc = a.scale;
 #pragma unroll
@@ -439,6 +455,36 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       }
   }
 }
+
+// ---------------------------------------------------------------------------
+// Sum of the partial dK/dV of each split dK/dV item, over its chunks in slot
+// order (so the result does not depend on scheduling), then dK * scale and
+// both to bf16.  One workgroup per (split item, batch entry); a thread sums
+// four consecutive values of one key at a time.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_dkdv_reduce_kernel(BwdArgs a) {
+  const int4 r = a.breduce[blockIdx.x];  // K-tile, KV head, first slot, chunks
+  const int b = blockIdx.y;
+  const int64_t ldk = (int64_t)a.Hkv * D;
+  constexpr int PER = kDkdvKeys * D / 4;  // float4 groups per output (dK or dV)
+  const float *base = a.part + ((int64_t)b * a.n_slots + r.z) * 2 * kDkdvKeys * D;
+  for (int i = threadIdx.x; i < 2 * PER; i += blockDim.x) {
+    const int which = i / PER, j = i - which * PER;
+    const int kl = j / (D / 4), d0 = (j - kl * (D / 4)) * 4;
+    const int key = r.x * kDkdvKeys + kl;
+    if (key >= a.S) continue;
+    const float *src = base + (int64_t)which * kDkdvKeys * D + (int64_t)kl * D + d0;
+    f32x4 acc = *reinterpret_cast<const f32x4 *>(src);
+    for (int c = 1; c < r.w; ++c)
+      acc += *reinterpret_cast<const f32x4 *>(src + (int64_t)c * 2 * kDkdvKeys * D);
+    if (which == 0) acc *= a.scale;
+    bf16 *dst = (which == 0 ? a.dk : a.dv) + ((int64_t)b * a.S + key) * ldk + (int64_t)r.y * D + d0;
+    *reinterpret_cast<bf16x4 *>(dst) =
+        __builtin_shufflevector(cvt2(acc[0], acc[1]), cvt2(acc[2], acc[3]), 0, 1, 2, 3);
+  }
+}
+
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per forward work item (Q-tile, head group); same lane
@@ -619,6 +665,8 @@ template __global__ void attn_bwd_pre_kernel<64>(const bf16 *, const bf16 *, con
                                                  float *, int, int, int, int64_t);
 template __global__ void attn_dkdv_kernel<128>(BwdArgs);
 template __global__ void attn_dkdv_kernel<64>(BwdArgs);
+template __global__ void attn_dkdv_reduce_kernel<128>(BwdArgs);
+template __global__ void attn_dkdv_reduce_kernel<64>(BwdArgs);
 template __global__ void attn_dq_kernel<128, 2>(BwdArgs);
 template __global__ void attn_dq_kernel<128, 1>(BwdArgs);
 template __global__ void attn_dq_kernel<64, 2>(BwdArgs);
@@ -643,6 +691,11 @@ hipError_t launch_dkdv(const BwdArgs &a, int d, int B, hipStream_t st) {
   if (d == 128) hipLaunchKernelGGL((attn_dkdv_kernel<128>), grid, block, 0, st, a);
   else if (d == 64) hipLaunchKernelGGL((attn_dkdv_kernel<64>), grid, block, 0, st, a);
   else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_breduce == 0) return e;
+  const dim3 rgrid((unsigned)a.n_breduce, (unsigned)B);
+  if (d == 128) hipLaunchKernelGGL((attn_dkdv_reduce_kernel<128>), rgrid, block, 0, st, a);
+  else hipLaunchKernelGGL((attn_dkdv_reduce_kernel<64>), rgrid, block, 0, st, a);
   return hipGetLastError();
 }
 

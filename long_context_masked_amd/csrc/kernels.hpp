@@ -43,6 +43,7 @@ constexpr float kNegInf = -__builtin_inff();
 // O / l is unchanged (all terms of a row share the same stale maximum).
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kMinit = -1.0e30f;  // finite start value of the running max
+constexpr int kDkdvKeys = 128;      // keys per dK/dV workgroup (4 waves x 32)
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -347,7 +348,10 @@ struct BwdArgs {
   const uint32_t *flist;
   const int4 *bitems;  // KV-split items (dK/dV pass)
   const uint32_t *blist;
-  int n_fitems, n_bitems;
+  const int *bslot;     // per dK/dV item: partial slot, -1 when not split
+  const int4 *breduce;  // per split item: K-tile, KV head, first slot, chunks
+  float *part;          // partial dK/dV: [B][n_slots][2][128 keys][d] fp32
+  int n_fitems, n_bitems, n_breduce, n_slots;
   MaskArgs m;
 };
 

@@ -21,6 +21,7 @@
 //     dQ) and per-K-tile (dK/dV) lists of non-empty tiles;
 //  6. order work items longest first and lay everything out in one blob.
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -496,8 +497,63 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   auto by_cost = [](const Item &a, const Item &b) { return a.cost > b.cost; };
   std::stable_sort(fi.begin(), fi.end(), by_cost);
   std::stable_sort(bi.begin(), bi.end(), by_cost);
-  xcd_interleave(fi, sh.Hkv, G);  // forward items carry their first query head
-  xcd_interleave(bi, sh.Hkv, 1);  // dK/dV items carry their KV head
+
+  // Step 7: split dK/dV items that cost more than the launch's share per
+  // workgroup (total / kSplitTarget) into up to kSplitMax chunks, each a run
+  // of consecutive listed Q-tiles (all query heads of the group), so that no
+  // single workgroup outlasts the rest (small S, or key columns that every
+  // row sees).  A chunk is an item of its own over a slice of the item's
+  // list, and gets a partial-result slot; slots follow list order.
+  std::vector<int32_t> slot_of;
+  std::vector<std::array<int32_t, 4>> reduce;
+  {
+    double total = 0.0;
+    for (const Item &x : bi) total += x.cost;
+    const double share = total * (double)sh.B / kSplitTarget;
+    std::vector<Item> split;
+    std::vector<int32_t> sl;
+    int32_t slots = 0;
+    for (const Item &x : bi) {
+      int32_t n = 1;
+      if (x.cost * (double)sh.B > share && x.len > 1)
+        n = (int32_t)std::min<double>({(double)kSplitMax, (double)x.len,
+                                       std::ceil(x.cost * (double)sh.B / share)});
+      if (n <= 1) {
+        split.push_back(x);
+        sl.push_back(-1);
+        continue;
+      }
+      reduce.push_back({x.tile, x.head, slots, n});
+      for (int32_t c = 0; c < n; ++c) {
+        const int32_t a0 = (int32_t)((int64_t)c * x.len / n), a1 = (int32_t)((int64_t)(c + 1) * x.len / n);
+        int32_t np = 0;
+        for (int32_t e = a0; e < a1; ++e) np += (bwd_list[(size_t)x.off + e] & kPartialBit) != 0;
+        const int32_t len = a1 - a0;
+        split.push_back({x.tile, x.head, x.off + a0, len, G * ((len - np) + kPartCost * np) + kItemCost});
+        sl.push_back(slots + c);
+      }
+      slots += n;
+    }
+    // longest first again, chunks included; the slot follows its item
+    std::vector<size_t> idx(split.size());
+    for (size_t i = 0; i < idx.size(); ++i) idx[i] = i;
+    std::stable_sort(idx.begin(), idx.end(),
+                     [&](size_t a, size_t b) { return split[a].cost > split[b].cost; });
+    bi.clear();
+    for (size_t i : idx) {
+      Item y = split[i];
+      y.off = (int32_t)i;  // carried through the interleave; replaced below
+      bi.push_back(y);
+    }
+    p->n_slots = slots;
+    xcd_interleave(fi, sh.Hkv, G);  // forward items carry their first query head
+    xcd_interleave(bi, sh.Hkv, 1);  // dK/dV items carry their KV head
+    for (Item &y : bi) {
+      const size_t i = (size_t)y.off;
+      y.off = split[i].off;
+      slot_of.push_back(sl[i]);
+    }
+  }
 
   // blob layout
   Layout &L = p->lay;
@@ -513,6 +569,10 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   L.bwd_items = sect(L.n_bwd_items * 16);
   L.n_bwd_list = (int64_t)bwd_list.size();
   L.bwd_list = sect(std::max<int64_t>(1, L.n_bwd_list) * 4);
+  L.bwd_slot = sect(std::max<int64_t>(1, L.n_bwd_items) * 4);
+  L.n_bwd_reduce = (int64_t)reduce.size();
+  L.bwd_reduce = sect(std::max<int64_t>(1, L.n_bwd_reduce) * 16);
+  L.n_slots = p->n_slots;
   if (has_bm) {
     L.bits = sect((int64_t)bm.bits.size());
     L.qblk = sect(S * 4);
@@ -547,6 +607,10 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   for (const Item &x : bi) {
     *it++ = x.tile; *it++ = x.head; *it++ = x.off; *it++ = x.len;
   }
+  if (!slot_of.empty()) std::memcpy(blob + L.bwd_slot, slot_of.data(), slot_of.size() * 4);
+  it = reinterpret_cast<int32_t *>(blob + L.bwd_reduce);
+  for (const auto &r : reduce)
+    for (int t = 0; t < 4; ++t) *it++ = r[t];
   for (int64_t kvh = 0; kvh < sh.Hkv; ++kvh) {
     const int hm = hm_of(kvh * G);
     for (int64_t kt = 0; kt < nBK; ++kt) {
@@ -622,14 +686,17 @@ extern "C" attn_status attn_plan_get_layout(const attn_plan *plan, attn_plan_lay
   out->off_bwd_list = L.bwd_list; out->n_bwd_list = L.n_bwd_list;
   out->off_bits = L.bits; out->off_qblk = L.qblk; out->off_kblk = L.kblk;
   out->off_qoffs = L.qoffs; out->off_koffs = L.koffs;
+  out->off_bwd_slot = L.bwd_slot;
+  out->off_bwd_reduce = L.bwd_reduce; out->n_bwd_reduce = L.n_bwd_reduce;
+  out->n_slots = L.n_slots;
   return ATTN_OK;
 }
 
-// Two fp32 values (LSE * log2 e and D) per (b, h, row), rows padded to 64.
+// Two fp32 values (LSE * log2 e and D) per (b, h, row), rows padded to 64,
+// then the partial results of split dK/dV items.
 extern "C" size_t attn_bwd_workspace_bytes(const attn_plan *plan) {
   if (!plan) return 0;
-  const int64_t s64 = (plan->shape.S + 63) / 64 * 64;
-  return (size_t)((plan->shape.B * plan->shape.Hq * s64 * 8 + 255) & ~int64_t(255));
+  return (size_t)(lcm::ws_stats_bytes(plan) + lcm::ws_partial_bytes(plan));
 }
 
 extern "C" void attn_plan_destroy(attn_plan *plan) { delete plan; }

@@ -24,15 +24,25 @@ constexpr uint32_t kPartialBit = 0x80000000u;
 struct Layout {
   int64_t rowb = -1, colb = -1;
   int64_t fwd_items = -1, fwd_list = -1, bwd_items = -1, bwd_list = -1;
+  int64_t bwd_slot = -1, bwd_reduce = -1;
   int64_t bits = -1, qblk = -1, kblk = -1, qoffs = -1, koffs = -1;
   int64_t n_fwd_items = 0, n_fwd_list = 0, n_bwd_items = 0, n_bwd_list = 0;
+  int64_t n_bwd_reduce = 0, n_slots = 0;
   int64_t total = 0;
 };
+
+// dK/dV items whose work exceeds the share of one workgroup are split into
+// chunks, each a run of the item's listed Q-tiles; a chunk writes fp32
+// partial dK/dV into a slot of the caller's workspace and a reduce pass sums
+// the chunks of each split item in a fixed order.
+constexpr int kSplitTarget = 256;  // dK/dV workgroups resident at once (one per CU)
+constexpr int kSplitMax = 16;      // chunks per item at most
 
 }  // namespace lcm
 
 struct attn_plan {
   attn_shape shape{};
+  int32_t n_slots = 0;  // partial-result slots of split dK/dV items
   float scale = 0.f;
   int G = 1;            // query heads per KV head
   int HG = 1;           // query heads per forward / dQ workgroup
@@ -47,6 +57,16 @@ struct attn_plan {
 };
 
 namespace lcm {
+// Backward workspace: lse2 and D per (b, h, row), rows padded to 64, then
+// the fp32 partial dK/dV of split items, [B][slot][dK, dV][128 keys][d].
+inline int64_t ws_stats_bytes(const attn_plan *p) {
+  const int64_t s64 = (p->shape.S + 63) / 64 * 64;
+  return (p->shape.B * p->shape.Hq * s64 * 8 + 255) & ~int64_t(255);
+}
+inline int64_t ws_partial_bytes(const attn_plan *p) {
+  return p->shape.B * (int64_t)p->n_slots * 2 * kBwdKeyTile * p->shape.d * 4;
+}
+
 // Thread-local last error (defined in plan.cpp).
 attn_status fail(attn_status s, const char *fmt, ...);
 void clear_error();
