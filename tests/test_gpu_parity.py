@@ -127,6 +127,23 @@ def test_forward_is_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_backward_is_deterministic_with_split_items():
+    """The partial dK/dV of split items are summed in a fixed order, so two
+    backward passes give identical bits (S = 1K splits every dK/dV item)."""
+    S = 1024
+    spec = syn.spec_causal(S)
+    plan = lcm.Plan(1, S, 8, 2, 128, spec)
+    assert plan.layout()["n_slots"] > 0
+    x = syn.attention_inputs(1, S, 8, 2, 128, 0)
+    q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
+    o, lse = lcm.fwd(plan, q, k, v)
+    g1 = lcm.bwd(plan, q, k, v, o, lse, do)
+    g2 = lcm.bwd(plan, q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
 def test_forced_device_error_leaves_outputs_untouched(monkeypatch):
     S = 128
     plan = lcm.Plan(1, S, 2, 1, 64, syn.spec_causal(S))

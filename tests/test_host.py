@@ -244,6 +244,31 @@ def test_schedule_is_longest_first(family):
                 assert _lpt_makespan(share, m) <= bound + 1e-9
 
 
+@pytest.mark.parametrize("label,spec,S,splits", [
+    ("full1K", syn.spec_full(1024), 1024, True),
+    ("causal1K", syn.spec_causal(1024), 1024, True),
+    ("global_sliding32K", syn.spec_global_sliding(32768, 64, 2048), 32768, True),
+    ("full16K", syn.spec_full(16384), 16384, False),
+    ("causal16K", syn.spec_causal(16384), 16384, False),
+])
+def test_dkdv_split_where_items_outlast_the_launch(label, spec, S, splits):
+    """dK/dV items longer than the launch's share per resident workgroup
+    (total / 256) are cut into at most 16 chunks; the rest stay whole.  At
+    S = 1K the 64 items of GQA 64:8 cannot fill 256 CUs, and under global
+    sliding the global key columns are seen by every row; uniform masks at
+    16K have 1024 items of equal cost."""
+    p = lcm.Plan(1, S, 64, 8, 128, spec)
+    lay = p.layout()
+    assert (lay["n_slots"] > 0) == splits
+    red = lay["bwd_reduce"]
+    assert (red[:, 3] >= 2).all() and (red[:, 3] <= 16).all()
+    assert int(red[:, 3].sum()) == lay["n_slots"]
+    assert p.workspace_bytes() >= lay["n_slots"] * 2 * 128 * 128 * 4
+    if splits:  # chunks bring the longest workgroup near the launch's share
+        cost = lay["bwd_items"][:, 3].astype(float)  # listed Q-tiles per item
+        assert cost.max() <= max(2.0 * cost.sum() / 256, 1.0)
+
+
 def _status(fn):
     try:
         fn()
