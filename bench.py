@@ -72,10 +72,14 @@ def workload(name, seqs):
             out.append((label, spec["S"], 64, 8, spec))
         desc = "heterogeneous masks: B=1, S=32K, GQA 64:8, d=128: PREFIX LM CAUSAL, SHARED QUESTION, GLOBAL SLIDING, CAUSAL BLOCKWISE, fwd+bwd"
     elif name == "sparse":
-        S = seqs[0] if seqs else 32768
-        for label, spec in syn.config_mask_specs("sparse", S, Hq=64, Hkv=8):
-            out.append((label, S, 64, 8, spec))
-        desc = f"block-sparse masks: B=1, S={S // 1024}K, GQA 64:8, d=128, 50% density, uniform 64/128 and variable blocks, fwd+bwd"
+        seqs = seqs or [32768, 131072]
+        for S in seqs:
+            for Hkv, heads in ((8, "gqa"), (64, "mha")):
+                for label, spec in syn.config_mask_specs("sparse", S, Hq=64, Hkv=Hkv):
+                    out.append((f"S{S // 1024}K_{heads}_{label}", S, 64, Hkv, spec))
+        desc = ("block-sparse masks: B=1, d=128, S in {" + ", ".join(f"{s // 1024}K" for s in seqs)
+                + "} x {GQA 64:8, MHA 64:64}, bitmap per KV head at 50% density, uniform 64/128 and "
+                  "variable blocks, fwd+bwd")
     else:
         raise SystemExit(f"unknown workload {name}")
     return out, desc
@@ -181,7 +185,7 @@ def main():
     ap.add_argument("--workload", default="dense", choices=["dense", "document", "hetero", "sparse"])
     ap.add_argument("--seqs", default=None,
                     help="comma-separated sequence lengths (dense: default 1024,8192,16384,49152; "
-                         "sparse: first value, default 32768; ignored by document and hetero)")
+                         "sparse: default 32768,131072; ignored by document and hetero)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size before warmup (counter scale)")
@@ -221,11 +225,12 @@ def main():
     runs = []
     plan_secs = 0.0
     for label, S, Hq, Hkv, spec in cases:
-        if S not in tensors:
-            log(f"inputs S={S}")
+        if (S, Hkv) not in tensors:
+            log(f"inputs S={S} Hkv={Hkv}")
             x = syn.attention_inputs(1, S, Hq, Hkv, d, seed=0)
             q, k, v, do = t(x["q"]), t(x["k"]), t(x["v"]), t(x["do"])
-            tensors[S] = dict(q=q, k=k, v=v, do=do, o=torch.empty_like(q),
+            del x
+            tensors[(S, Hkv)] = dict(q=q, k=k, v=v, do=do, o=torch.empty_like(q),
                               lse=torch.empty((1, Hq, S), dtype=torch.float32, device=dev),
                               dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
         t0 = time.perf_counter()
@@ -233,7 +238,7 @@ def main():
         plan_secs += time.perf_counter() - t0
         plan.bind(dev)
         ws = torch.empty(plan.workspace_bytes() + 256, dtype=torch.uint8, device=dev)
-        runs.append(dict(label=label, S=S, plan=plan, ws=ws, nnz=plan.stats["nnz_total"]))
+        runs.append(dict(label=label, S=S, Hkv=Hkv, plan=plan, ws=ws, nnz=plan.stats["nnz_total"]))
         log(f"plan {label}: nnz {plan.stats['nnz_total']:.4g}, fwd partial tiles "
             f"{plan.stats['fwd_tiles_partial']}, full {plan.stats['fwd_tiles_full']}")
 
@@ -245,7 +250,7 @@ def main():
 
     def one_step(record):
         for r in runs:
-            tt = tensors[r["S"]]
+            tt = tensors[(r["S"], r["Hkv"])]
             h = r["plan"].handle
             wptr = r["ws"].data_ptr()
             wptr += (-wptr) % 256

@@ -1,5 +1,6 @@
 """GPU parity at the workloads' full sizes, in the benchmark's launch
-configuration (B=1, GQA 64:8, d=128).
+configuration (B=1, d=128, GQA 64:8; the block-sparse masks also under MHA
+64:64 and at S = 128K).
 
 At these sizes the fp64 oracle cannot run whole tensors, so the tests check:
 * sampled rows of O, LSE and dQ, which the oracle computes one row at a time
@@ -7,7 +8,9 @@ At these sizes the fp64 oracle cannot run whole tensors, so the tests check:
   the small cases;
 * every row's mask coverage with Q = 0: all allowed keys then get the same
   weight, so exp(LSE_i) must equal the number of allowed keys n_i (counted
-  from the oracle's predicate) and O_i the mean of the allowed v_j;
+  from the oracle's predicate) and O_i the mean of the allowed v_j (beyond
+  S = 64K on sampled blocks of rows, and with more than 8 bitmap heads on
+  two of them, to keep the oracle's count within a minute);
 * the identity sum_j dV_j = sum over query rows of the group of dO_i, which
   holds at any size because every probability row sums to one;
 * uniform V: O = v, dQ = dK = 0.
@@ -29,15 +32,15 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import long_context_masked_amd as lcm  # noqa: E402
 
-HQ, HKV, D = 64, 8, 128
+HQ, D = 64, 128
 _INPUTS = {}
 
 
-def inputs(S):
-    if S not in _INPUTS:
-        x = syn.attention_inputs(1, S, HQ, HKV, D, seed=0)
-        _INPUTS[S] = (x, {n: to_dev(x[n], torch) for n in x})
-    return _INPUTS[S]
+def inputs(S, Hkv):
+    if (S, Hkv) not in _INPUTS:
+        x = syn.attention_inputs(1, S, HQ, Hkv, D, seed=0)
+        _INPUTS[(S, Hkv)] = (x, {n: to_dev(x[n], torch) for n in x})
+    return _INPUTS[(S, Hkv)]
 
 
 class Lazy64:
@@ -54,13 +57,20 @@ class Lazy64:
 def _cases():
     out = []
     for label, spec in syn.config_mask_specs("dense", 49152):
-        out.append(("dense48K_" + label, spec))
+        out.append(("dense48K_" + label, spec, 8))
     for label, spec in syn.config_mask_specs("document"):
-        out.append(("doc64K_" + label, spec))
+        out.append(("doc64K_" + label, spec, 8))
     for label, spec in syn.config_mask_specs("hetero"):
-        out.append(("hetero32K_" + label, spec))
-    for label, spec in syn.config_mask_specs("sparse", 32768, Hq=HQ, Hkv=HKV):
-        out.append(("sparse32K_" + label, spec))
+        out.append(("hetero32K_" + label, spec, 8))
+    for label, spec in syn.config_mask_specs("sparse", 32768, Hq=HQ, Hkv=8):
+        out.append(("sparse32K_" + label, spec, 8))
+    for label, spec in syn.config_mask_specs("sparse", 32768, Hq=HQ, Hkv=64):
+        out.append(("sparse32K_mha_" + label, spec, 64))
+    for label, spec in syn.config_mask_specs("sparse", 131072, Hq=HQ, Hkv=8):
+        out.append(("sparse128K_" + label, spec, 8))
+    # one 128K MHA mask: its plan alone lists about 10^8 tiles per direction
+    offs, bits = syn.uniform_block_bitmap(131072, 128, 64, 0.5, 0)
+    out.append(("sparse128K_mha_block128_50", syn.with_bitmap(syn.spec_full(131072), offs, offs, bits), 64))
     return out
 
 
@@ -74,11 +84,11 @@ def _rows(S, seed):
     return sorted(set(fixed + rng.integers(0, S, 7).tolist()))
 
 
-@pytest.mark.parametrize("label,spec", CASES, ids=IDS)
-def test_sampled_rows(label, spec):
+@pytest.mark.parametrize("label,spec,Hkv", CASES, ids=IDS)
+def test_sampled_rows(label, spec, Hkv):
     S = spec["S"]
-    x, t = inputs(S)
-    plan = lcm.Plan(1, S, HQ, HKV, D, spec)
+    x, t = inputs(S, Hkv)
+    plan = lcm.Plan(1, S, HQ, Hkv, D, spec)
     o, lse = lcm.fwd(plan, t["q"], t["k"], t["v"])
     dq, dk, dv = lcm.bwd(plan, t["q"], t["k"], t["v"], o, lse, t["do"])
     torch.cuda.synchronize()
@@ -100,30 +110,34 @@ def test_sampled_rows(label, spec):
     assert np.abs(g["lse"] - rf["lse"]).max() <= 5e-3
     # sum_j dV_j = sum of dO over the rows of the group (every row has a key)
     dvs = dv[0].to(torch.float64).sum(dim=0)          # [Hkv, d]
-    dos = t["do"][0].to(torch.float64).sum(dim=0).reshape(HKV, HQ // HKV, D).sum(dim=1)
+    dos = t["do"][0].to(torch.float64).sum(dim=0).reshape(Hkv, HQ // Hkv, D).sum(dim=1)
     err = (dvs - dos).abs().max().item()
-    assert err <= 1e-2 * np.sqrt(S * HQ / HKV), err
+    assert err <= 1e-2 * np.sqrt(S * HQ / Hkv), err
     assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
 
 
-@pytest.mark.parametrize("label,spec", CASES, ids=IDS)
-def test_mask_coverage_every_row(label, spec):
-    """Q = 0: exp(LSE_i) = n_i for every row and head; O_i = mean of allowed v_j."""
+@pytest.mark.parametrize("label,spec,Hkv", CASES, ids=IDS)
+def test_mask_coverage_every_row(label, spec, Hkv):
+    """Q = 0: exp(LSE_i) = n_i for every row and head (beyond S = 64K on
+    sampled row blocks; with more than 8 bitmap heads on the first and last);
+    O_i = mean of allowed v_j."""
     S = spec["S"]
-    x, t = inputs(S)
-    plan = lcm.Plan(1, S, HQ, HKV, D, spec)
+    x, t = inputs(S, Hkv)
+    plan = lcm.Plan(1, S, HQ, Hkv, D, spec)
     q0 = torch.zeros_like(t["q"])
     o, lse = lcm.fwd(plan, q0, t["k"], t["v"])
     torch.cuda.synchronize()
     nh = spec["bitmap"]["bits"].shape[0] if "bitmap" in spec else 1
-    G = HQ // HKV
+    G = HQ // Hkv
     vbits = x["v"]
-    for hm in range(nh):
-        counts = np.zeros(S, dtype=np.int64)
-        for i0 in range(0, S, 2048):
-            counts[i0:i0 + 2048] = om.allowed(spec, i0, min(S, i0 + 2048), hm).sum(axis=1)
-        heads = [h for h in range(HQ) if om.mask_head(spec, h, HQ, HKV) == hm]
-        n_gpu = torch.exp(lse[0, heads].to(torch.float64)).cpu().numpy()
+    # the oracle counts about 2.5e8 (row, key) pairs per second
+    blocks = list(range(0, S, 2048)) if S <= 65536 else [0, S // 2 - 1024, S - 2048]
+    hms = range(nh) if nh <= 8 else [0, nh - 1]
+    for hm in hms:
+        rows = np.concatenate([np.arange(i0, min(S, i0 + 2048)) for i0 in blocks])
+        counts = np.concatenate([om.allowed(spec, i0, min(S, i0 + 2048), hm).sum(axis=1) for i0 in blocks])
+        heads = [h for h in range(HQ) if om.mask_head(spec, h, HQ, Hkv) == hm]
+        n_gpu = torch.exp(lse[0, heads][:, rows].to(torch.float64)).cpu().numpy()
         assert (np.rint(n_gpu) == counts[None, :]).all(), label
         assert np.abs(n_gpu / counts[None, :] - 1).max() < 1e-4
         # O_i = mean of the allowed v_j on sampled rows of the first head
@@ -135,18 +149,21 @@ def test_mask_coverage_every_row(label, spec):
         gate("O(Q=0)", to_f64(o[0, rows, h]), want)
 
 
-@pytest.mark.parametrize("label,spec", [c for c in CASES if c[0].startswith(("dense48K_causal", "hetero32K_shared", "sparse32K_var"))],
-                         ids=[c[0] for c in CASES if c[0].startswith(("dense48K_causal", "hetero32K_shared", "sparse32K_var"))])
-def test_uniform_v_closed_form(label, spec):
+_UNIFORM = [c for c in CASES if c[0].startswith(("dense48K_causal", "hetero32K_shared", "sparse32K_var",
+                                                   "sparse128K_block64"))]
+
+
+@pytest.mark.parametrize("label,spec,Hkv", _UNIFORM, ids=[c[0] for c in _UNIFORM])
+def test_uniform_v_closed_form(label, spec, Hkv):
     """v_j = v for every key: O = v, and dQ = dK = 0 up to rounding."""
     S = spec["S"]
-    x, t = inputs(S)
-    plan = lcm.Plan(1, S, HQ, HKV, D, spec)
+    x, t = inputs(S, Hkv)
+    plan = lcm.Plan(1, S, HQ, Hkv, D, spec)
     v1 = t["v"][:, :1].expand_as(t["v"]).contiguous()
     o, lse = lcm.fwd(plan, t["q"], t["k"], v1)
     dq, dk, dv = lcm.bwd(plan, t["q"], t["k"], v1, o, lse, t["do"])
     torch.cuda.synchronize()
-    want = v1[0, 0].repeat_interleave(HQ // HKV, dim=0).to(torch.float32)  # [Hq, d]
+    want = v1[0, 0].repeat_interleave(HQ // Hkv, dim=0).to(torch.float32)  # [Hq, d]
     assert (o[0].to(torch.float32) - want[None]).abs().max().item() <= 2.0 ** -7 * want.abs().max().item()
     assert dq.abs().max().item() <= 1e-3
     assert dk.abs().max().item() <= 1e-3
