@@ -10,12 +10,22 @@
 // that share a KV head).  Wave w owns 32 query rows of head h0 + w % HG; lane
 // l owns row 32*(w / HG) + l % 32, and the two lane halves split each K-tile's
 // 64 keys.  K and V tiles of 64 keys are loaded straight into LDS (natural
-// layout, double-buffered) and shared by all heads of the item.  Per K-tile:
-//   S^T = K Q^T                  (MFMA; K row reads, Q^T in registers)
-//   mask (partial tiles only)    (per-lane 64-bit allowed-key word)
+// layout) and shared by all heads of the item.  Per K-tile t:
+//   S^T = K Q^T                  (MFMA; K row reads, Q^T in registers;
+//                                 masked entries start the sum at -inf)
 //   m update                     (running max kept stale within the slack)
 //   P^T = exp2(S^T c - m) -> bf16, l += sum P (bf16 dot products)
 //   O^T += V^T P^T               (MFMA; V^T by transposed LDS reads)
+// The steps of neighbouring tiles are software-pipelined so that every run
+// of products has independent VALU work between its MFMAs (a wave stalls at
+// an MFMA while the matrix pipe is busy with the previous one, but VALU
+// work issued between two MFMAs runs meanwhile):
+//   phase A:  S^T(t + 1)     with the exponentials of key block 0 of tile t
+//   phase B:  O^T += V^T(t)  with the exponentials of key block 1 of tile t
+//             P^T(t)         and the maximum of S^T(t + 1)
+// K tiles are read one tile ahead of V tiles, so each has its own ring of two
+// LDS slots; the loads for K(t + 3) and V(t + 2) are issued after the
+// barrier that ends tile t and complete by the barrier that ends tile t + 1.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -24,11 +34,13 @@ namespace lcm {
 
 template <int D, int HG>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
-  constexpr int KS = D / 16;  // k-steps of QK^T
-  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  constexpr int KS = D / 16;   // k-steps of QK^T
+  constexpr int DB = D / 32;   // 32-row blocks of O^T
+  constexpr int NCB = 2 * DB;  // chunks of two MFMAs in phase B (4 P^T steps)
   using T = Tile<D>;
-  constexpr int STAGE = 2 * T::BYTES;  // K tile, then V tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr int VOFF = 2 * T::BYTES;  // K slots 0 and 1, then V slots 0 and 1
+  static_assert(16 % KS == 0 && 16 % DB == 0, "chunking");
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T::BYTES];
 
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int ln = lane & 31, hh = lane >> 5;
@@ -55,13 +67,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int4 rb = row_ok ? a.m.rowb[row] : make_int4(0, 0, 0, 0);
   const int hm = bitmap_head(a.m.bm_heads, h, a.Hq, a.G);
   const int qb = (a.m.bm_heads && row_ok) ? a.m.qblk[row] : 0;
-  int koff[KS], voff[DB][2];
+  // K row reads use byte offsets from a slot; transposed V reads use LDS
+  // addresses in V slot 0 (slot 1 adds a constant to the instruction)
+  int koff[KS];
+  uint32_t va[DB][2];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) koff[ks] = row_off<D>(lane, ks);
+  {
+    const uint32_t v0 = lds_addr(smem + VOFF);
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    voff[db][0] = T::BYTES + tr_off<D>(lane, db, 0);
-    voff[db][1] = T::BYTES + tr_off<D>(lane, db, 1);
+    for (int db = 0; db < DB; ++db) {
+      va[db][0] = v0 + tr_off<D>(lane, db, 0);
+      va[db][1] = v0 + tr_off<D>(lane, db, 1);
+    }
   }
 
   f32x16 o[DB];
@@ -74,124 +92,214 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int n = item.w;
   TileDma<D> dma;
   dma.init(ldk);
-  if (n > 0) {
-    const int kt = (int)(list[0] & 0x7fffffffu);
-    dma.load(smem, kbase, ldk, kt * 64, S);
-    dma.load(smem + T::BYTES, vbase, ldk, kt * 64, S);
-  }
-  dma_wait();
-  __syncthreads();
-
-  // One K-tile, read from buffer BUF (tiles alternate between the two
-  // buffers; with BUF a constant the buffer offset folds into the LDS
-  // instructions' immediate offsets).
-  auto tile = [&](int e, auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
+  auto load_k = [&](int e, int slot) {
+    dma.load(smem + slot * T::BYTES, kbase, ldk, (int)(list[e] & 0x7fffffffu) * 64, S);
+  };
+  auto load_v = [&](int e, int slot) {
+    dma.load(smem + VOFF + slot * T::BYTES, vbase, ldk, (int)(list[e] & 0x7fffffffu) * 64, S);
+  };
+  // Allowed-key words of the lane's row for the two key blocks of tile e
+  // (all ones unless the tile is partial); returns whether it is partial.
+  auto tile_mask = [&](int e, uint32_t (&mw)[2]) -> bool {
     const uint32_t ent = list[e];
-    const int kt = (int)(ent & 0x7fffffffu);
-    const bool partial = (ent >> 31) != 0;
-    char *stage = smem + BUF * STAGE;
-    if (e + 1 < n) {
-      // the other buffer was last read before the previous barrier
-      const int nkt = (int)(list[e + 1] & 0x7fffffffu);
-      char *next = smem + (1 - BUF) * STAGE;
-      dma.load(next, kbase, ldk, nkt * 64, S);
-      dma.load(next + T::BYTES, vbase, ldk, nkt * 64, S);
-    }
-
-    uint32_t mlo = 0xffffffffu, mhi = 0xffffffffu;
-    bool active = true;
-    if (partial) {
-      const uint64_t mk = row_ok ? row_mask(a.m, rb, qb, hm, kt * 64, S) : 0ull;
-      active = __ballot(mk != 0ull) != 0ull;
+    mw[0] = 0xffffffffu;
+    mw[1] = 0xffffffffu;
+    const bool part = (ent >> 31) != 0;
+    if (part) {
+      const uint64_t mk = row_ok ? row_mask(a.m, rb, qb, hm, (int)(ent & 0x7fffffffu) * 64, S) : 0ull;
       const uint64_t sh = mk >> (4 * hh);
-      mlo = (uint32_t)sh;
-      mhi = (uint32_t)(sh >> 32);
+      mw[0] = (uint32_t)sh;
+      mw[1] = (uint32_t)(sh >> 32);
     }
-    if (active) {
-      // S^T = K Q^T for the two 32-key blocks; the K row reads run two
-      // k-steps ahead of the products that consume them.
-      f32x16 s[2];
-      bf16x8 ak[2][KS];
+    return part;
+  };
+  // First k-step of S^T for one key block: the sum starts at 0, or, on a
+  // partial tile, at -inf on the masked entries (whose P is then 0).  The
+  // branch keeps the bias off full tiles.
+  auto s_first = [&](bf16x8 ak0, bool part, uint32_t mw) -> f32x16 {
+    if (part) {
+      __asm__ volatile("");
+      f32x16 bias;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        ak[0][ks] = lds_rows(stage, koff[ks]);
-        ak[1][ks] = lds_rows(stage, koff[ks] + 32 * T::ROWB);
-      }
-      s[0] = (f32x16){};
-      s[1] = (f32x16){};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s[0] = mfma32(ak[0][ks], qv[ks], s[0]);
-        s[1] = mfma32(ak[1][ks], qv[ks], s[1]);
-      }
-      pipeline_reads_mfma<KS>();
-      if (partial) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int bit = 8 * (r >> 2) + (r & 3);
-          s[0][r] = keep_or(mlo, bit, s[0][r], kNegInf);
-          s[1][r] = keep_or(mhi, bit, s[1][r], kNegInf);
-        }
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[0][r]), s[1][r]);
-      mx = max_halves(mx);
-      const float m_new = __builtin_fmaxf(m_run, mx * sl2);
-      if (__ballot(m_new > m_run + kRescaleSlack) != 0ull) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -m_run));
-      // O^T += V^T P^T, one 16-key step at a time; the V^T operands of a step
-      // are read (transposed) while its P^T operand is converted.
-      const uint32_t sbase = lds_addr(stage);
-      uint32_t va[DB][2];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        va[db][0] = sbase + voff[db][0];
-        va[db][1] = sbase + voff[db][1];
-      }
-      auto pv_step = [&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        constexpr int toff = t * 16 * T::ROWB;
-        s16x4 x[2 * DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          x[2 * db] = tr_issue<toff>(va[db][0]);
-          x[2 * db + 1] = tr_issue<toff>(va[db][1]);
-        }
-        const bf16x8 pb = c_to_b(s[t >> 1], t & 1);
-        l_run = sum8(pb, l_run);
-        tr_wait(x);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = mfma32(tr_pair(x[2 * db], x[2 * db + 1]), pb, o[db]);
-      };
-      pv_step(std::integral_constant<int, 0>{});
-      pv_step(std::integral_constant<int, 1>{});
-      pv_step(std::integral_constant<int, 2>{});
-      pv_step(std::integral_constant<int, 3>{});
+      for (int r = 0; r < 16; ++r) bias[r] = keep_or(mw, 8 * (r >> 2) + (r & 3), 0.f, kNegInf);
+      return mfma32(ak0, qv[0], bias);
     }
+    return mfma32(ak0, qv[0], (f32x16){});
+  };
+  // P of accumulator register r of key block kb, pinned where it is
+  // computed (the compiler would otherwise sink it next to its use and undo
+  // the interleave).
+  auto p_exp = [&](f32x16 &s, int r) {
+    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -m_run));
+    in_vgpr(p);
+    s[r] = p;
+  };
+  auto p_pack = [&](const f32x16 &s, int t, bf16x8 &pb) {
+    pb = c_to_b(s, t);
+    in_vgpr(pb);
+    l_run = sum8(pb, l_run);
+  };
+  // Running max after S^T of a new tile (rescaling O only past the slack).
+  auto m_update = [&](float mx) {
+    const float m_new = __builtin_fmaxf(m_run, max_halves(mx) * sl2);
+    if (__ballot(m_new > m_run + kRescaleSlack) != 0ull) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
+  };
 
+  // Prologue: K(0), V(0), K(1) in; S^T(0) and its max; then K(2), V(1) out.
+  f32x16 sc[2];  // S^T of the current tile, then its P (exponentiated in place)
+  if (n > 0) {
+    load_k(0, 0);
+    load_v(0, 0);
+    if (n > 1) load_k(1, 1);
+    uint32_t mw[2];
+    const bool part = tile_mask(0, mw);
     dma_wait();
     __syncthreads();
-  };
-  int e = 0;
-  for (; e + 1 < n; e += 2) {
-    tile(e, std::integral_constant<int, 0>{});
-    tile(e + 1, std::integral_constant<int, 1>{});
+    bf16x8 ak[2][KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      ak[0][ks] = lds_rows(smem, koff[ks]);
+      ak[1][ks] = lds_rows(smem, koff[ks] + 32 * T::ROWB);
+    }
+    sc[0] = s_first(ak[0][0], part, mw[0]);
+    sc[1] = s_first(ak[1][0], part, mw[1]);
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) {
+      sc[0] = mfma32(ak[0][ks], qv[ks], sc[0]);
+      sc[1] = mfma32(ak[1][ks], qv[ks], sc[1]);
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[0][r]), sc[1][r]);
+    m_update(mx);
+    __syncthreads();  // every wave is done with K slot 0
+    if (n > 2) load_k(2, 0);
+    if (n > 1) load_v(1, 1);
   }
-  if (e < n) tile(e, std::integral_constant<int, 0>{});
+
+  // Tile t, read from K slot 1 - P (for t + 1) and V slot P; P = t % 2 is a
+  // constant so that slot offsets fold into the LDS instructions.
+  auto tile = [&](int t, auto pc, auto nc) {
+    constexpr int P = decltype(pc)::value;
+    constexpr bool NEXT = decltype(nc)::value;  // tile t + 1 exists
+    const char *kslot = smem + (1 - P) * T::BYTES;
+    uint32_t mw[2] = {0xffffffffu, 0xffffffffu};
+    bool pn = false;
+    if constexpr (NEXT) pn = tile_mask(t + 1, mw);
+    bf16x8 ak[2][KS];
+    if constexpr (NEXT) {
+      ak[0][0] = lds_rows(kslot, koff[0]);
+      ak[1][0] = lds_rows(kslot, koff[0] + 32 * T::ROWB);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase A: S^T(t + 1) with the exponentials of key block 0 of tile t
+    f32x16 sn[2];
+    bf16x8 pb[4];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (NEXT) {
+        if (ks + 1 < KS) {
+          ak[0][ks + 1] = lds_rows(kslot, koff[ks + 1]);
+          ak[1][ks + 1] = lds_rows(kslot, koff[ks + 1] + 32 * T::ROWB);
+        }
+        if (ks == 0) {
+          sn[0] = s_first(ak[0][0], pn, mw[0]);
+          sn[1] = s_first(ak[1][0], pn, mw[1]);
+        } else {
+          sn[0] = mfma32(ak[0][ks], qv[ks], sn[0]);
+          sn[1] = mfma32(ak[1][ks], qv[ks], sn[1]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16 / KS; ++i) p_exp(sc[0], ks * (16 / KS) + i);
+      if ((ks + 1) * (16 / KS) == 8) p_pack(sc[0], 0, pb[0]);
+      if (ks == KS - 1) p_pack(sc[0], 1, pb[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- phase B: O^T += V^T P^T(t), 16 keys per step, with the
+    // exponentials of key block 1 (steps 0 and 1) and the max of S^T(t + 1)
+    auto issue = [&](auto stc, s16x4(&x)[2 * DB]) {
+      constexpr int toff = P * T::BYTES + decltype(stc)::value * 16 * T::ROWB;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        x[2 * db] = tr_issue<toff>(va[db][0]);
+        x[2 * db + 1] = tr_issue<toff>(va[db][1]);
+      }
+    };
+    s16x4 xa[2 * DB], xb[2 * DB];
+    float mx = kNegInf;
+    issue(std::integral_constant<int, 0>{}, xa);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      const int st = c / (DB / 2);         // P^T step (16 keys)
+      const int d0 = (c % (DB / 2)) * 2;   // first of the chunk's two O^T blocks
+      if (c % (DB / 2) == 0) {
+        if (st % 2 == 0) {
+          tr_wait(xa);
+          if (st == 0) issue(std::integral_constant<int, 1>{}, xb);
+          if (st == 2) issue(std::integral_constant<int, 3>{}, xb);
+        } else {
+          tr_wait(xb);
+          if (st == 1) issue(std::integral_constant<int, 2>{}, xa);
+        }
+      }
+      const s16x4(&x)[2 * DB] = (st % 2 == 0) ? xa : xb;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        o[d0 + j] = mfma32(tr_pair(x[2 * (d0 + j)], x[2 * (d0 + j) + 1]), pb[st], o[d0 + j]);
+      if (c < DB) {  // steps 0 and 1: exponentials of key block 1
+#pragma unroll
+        for (int i = 0; i < 16 / DB; ++i) p_exp(sc[1], c * (16 / DB) + i);
+        if ((c + 1) * (16 / DB) == 8) p_pack(sc[1], 0, pb[2]);
+        if (c == DB - 1) p_pack(sc[1], 1, pb[3]);
+      }
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int i = 0; i < 16 / NCB; ++i) {
+          const int r = c * (16 / NCB) + i;
+          mx = __builtin_fmaxf(__builtin_fmaxf(mx, sn[0][r]), sn[1][r]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NEXT) {
+      m_update(mx);
+      sc[0] = sn[0];
+      sc[1] = sn[1];
+    }
+
+    // K(t + 2) and V(t + 1) are in LDS for every wave; K slot 1 - P and V
+    // slot P are free
+    dma_wait();
+    __syncthreads();
+    if (t + 3 < n) load_k(t + 3, 1 - P);
+    if (t + 2 < n) load_v(t + 2, P);
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  int t = 0;
+  for (; t + 2 < n; t += 2) {
+    tile(t, C0{}, Yes{});
+    tile(t + 1, C1{}, Yes{});
+  }
+  if (t + 1 < n) {
+    tile(t, C0{}, Yes{});
+    tile(t + 1, C1{}, No{});
+  } else if (t < n) {
+    tile(t, C0{}, No{});
+  }
 
   const float l_tot = sum_halves(l_run);
   if (row_ok) {
