@@ -175,7 +175,7 @@ typedef struct {
 attn_status attn_plan_get_layout(const attn_plan *plan, attn_plan_layout *out);
 
 /* Bytes of device workspace attn_bwd needs: per (b, h, row) the fp32 values
- * LSE * log2(e) and D = rowsum(dO * O), rows padded to a multiple of 64,
+ * LSE * log2(e) and -D, D = rowsum(dO * O), rows padded to a multiple of 64,
  * then, when the plan split long dK/dV work items into chunks (small S, or
  * key columns seen by every row), fp32 partial dK and dV of 128 keys per
  * chunk slot and batch entry. */
@@ -192,8 +192,8 @@ attn_status attn_fwd(const attn_plan *plan, const void *q, const void *k,
 
 /*
  * Backward: dQ, dK, dV from Q, K, V, the forward's O and LSE, and dO.
- * Three launches on `stream`: D = rowsum(dO * O) and LSE * log2(e) into
- * `ws`; a KV-split pass
+ * Three launches on `stream`: -D, D = rowsum(dO * O), and LSE * log2(e)
+ * into `ws`; a KV-split pass
  * (one workgroup per K-tile and KV head) accumulating dK and dV; a Q-split
  * pass accumulating dQ = scale * sum_j dS_ij K_j (the row/column two-axis
  * split of FlashAttention-2, "core optimisations").  dK and dV of a KV head
@@ -209,9 +209,9 @@ attn_status attn_bwd(const attn_plan *plan, const void *q, const void *k,
  * The three stages of attn_bwd, callable one at a time on the same stream
  * and in this order (attn_bwd is exactly these three calls).  They exist so
  * that callers can interleave other work between stages and time them.
- *   attn_bwd_preprocess: ws <- LSE * log2(e) and D = rowsum(dO * O), fp32.
- *   attn_bwd_dkdv:       dK, dV from Q, K, V, LSE, dO and D in ws.
- *   attn_bwd_dq:         dQ from Q, K, V, LSE, dO and D in ws.
+ *   attn_bwd_preprocess: ws <- LSE * log2(e) and -D, D = rowsum(dO * O), fp32.
+ *   attn_bwd_dkdv:       dK, dV from Q, K, V, dO and the values in ws.
+ *   attn_bwd_dq:         dQ from Q, K, V, dO and the values in ws.
  * Arguments have the meaning and requirements given for attn_bwd.
  */
 attn_status attn_bwd_preprocess(const attn_plan *plan, const void *o, const float *lse,

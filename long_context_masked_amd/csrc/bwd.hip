@@ -22,13 +22,14 @@ namespace lcm {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Workspace rows of (b, h): lse2 at ws + 2 (b Hq + h) S64, D right after.
+// Workspace rows of (b, h): lse2 at ws + 2 (b Hq + h) S64, -D right after.
 __device__ __forceinline__ int64_t ws_row0(int b, int h, int Hq, int S64) {
   return 2 * ((int64_t)b * Hq + h) * S64;
 }
 
-// ws <- {lse * log2(e), D = sum_d dO * O} per (b, h, row); rows in [S, S64)
-// get zeros.  One group of D/8 lanes per row; the grid covers B * S64 * Hq
+// ws <- {lse * log2(e), -D = -sum_d dO * O} per (b, h, row); rows in
+// [S, S64) get zeros.  D is stored negated so that the dK/dV pass can start
+// the accumulation of dP at -D and get dP - D from the products alone.  One group of D/8 lanes per row; the grid covers B * S64 * Hq
 // rows in [b][s][h] order.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const bf16 *dout,
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
   if (r < nrows && c == 0) {
     const int64_t w0 = ws_row0(b, h, Hq, S64);
     ws[w0 + s] = real ? lse[((int64_t)b * Hq + h) * S + s] * kLog2e : 0.f;
-    ws[w0 + S64 + s] = acc;
+    ws[w0 + S64 + s] = -acc;
   }
 }
 
@@ -70,7 +71,8 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
 // from the same tiles by transposed reads.  Each stage is two 32-row units,
 // and each unit u takes three steps:
 //   A(u): S = Q K^T, dP = dO V^T                          (MFMA)
-//   B(u): P = exp2(S c - lse2), dS = P (dP - D)           (VALU)
+//   B(u): P = exp2(S c - lse2), dS = P (dP - D)           (VALU; the sum of
+//         dP starts at -D, loaded from LDS straight into its accumulator)
 //   C(u): dV^T += dO^T P, dK^T += Q^T dS                   (MFMA)
 // Masking costs nothing on stages without masked entries: on a partial
 // stage the accumulation of S starts at -inf on the masked entries (and at
@@ -222,9 +224,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   // (Each result is pinned where it is computed: the values are consumed
   // phases later, and without the pins the compiler sinks the arithmetic
   // next to its uses, undoing the interleave.)
-  auto b_exp = [&](f32x16 &s, f32x16 &dp, int r, float l, float d) {
+  auto b_exp = [&](f32x16 &s, f32x16 &dp, int r, float l) {
     float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l));
-    float ds = p * (dp[r] - d);
+    float ds = p * dp[r];  // dp already holds dP - D
     in_vgpr(p);
     in_vgpr(ds);
     s[r] = p;
@@ -251,7 +253,23 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     return mfma32(aq0, kv[0], (f32x16){});
   };
 
-  f32x16 s0, dp0;  // unit (st, 0): S and dP in VGPRs
+  // Start value of the dP sum of a unit: -D of its rows (the lane's 16
+  // accumulator registers r hold rows 8 (r / 4) + 4 hh + r % 4).
+  auto neg_d = [&](const char *buf, int qh) {
+    const float *src = reinterpret_cast<const float *>(buf + OFF_D) + 32 * qh + 4 * hh;
+    f32x16 x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(src + 8 * c);
+      x[4 * c] = v[0];
+      x[4 * c + 1] = v[1];
+      x[4 * c + 2] = v[2];
+      x[4 * c + 3] = v[3];
+    }
+    return x;
+  };
+
+  f32x16 s0, dp0;  // unit (st, 0): S and dP - D in VGPRs
   uint32_t mwc[2], mwn[2];
   bool pc = false, pn = false;  // stages st and st + 1 are partial
   if (nst > 0) {
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     pc = stage_mask(0, mwc);
     dma_wait();
     __syncthreads();
-    f32x16 sa0 = s_first(rows_q(smem, 0, 0), pc, mwc[0]), dpa0 = (f32x16){};
+    f32x16 sa0 = s_first(rows_q(smem, 0, 0), pc, mwc[0]), dpa0 = neg_d(smem, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks > 0) sa0 = mfma32(rows_q(smem, 0, ks), kv[ks], sa0);
@@ -294,13 +312,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       sa[db][1] = sbase + toff[db][1];
     }
     const float *sl = reinterpret_cast<const float *>(buf + OFF_L) + 4 * hh;
-    const float *sd = reinterpret_cast<const float *>(buf + OFF_D) + 4 * hh;
-    f32x4 l0[4], d0[4], l1[4], d1[4];
+    f32x4 l0[4], l1[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      l0[c] = *reinterpret_cast<const f32x4 *>(sl + 8 * c);
-      d0[c] = *reinterpret_cast<const f32x4 *>(sd + 8 * c);
-    }
+    for (int c = 0; c < 4; ++c) l0[c] = *reinterpret_cast<const f32x4 *>(sl + 8 * c);
     bf16x8 aq[KS], ao[KS];
     aq[0] = rows_q(buf, 1, 0);
     ao[0] = rows_o(buf, 1, 0);
@@ -309,7 +323,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- phase 1: A(st, 1) with the exponentials of B(st, 0)
-    f32x16 sa1 = s_first(aq[0], pc, mwc[1]), dpa1 = (f32x16){};
+    f32x16 sa1 = s_first(aq[0], pc, mwc[1]), dpa1 = neg_d(buf, 1);
     bf16x8 pb0[2], dsb0[2];
     s16x4 xa[4 * DB], xb[4 * DB];
 #pragma unroll
@@ -320,17 +334,14 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       }
       if (ks == KS / 2) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          l1[c] = *reinterpret_cast<const f32x4 *>(sl + 32 + 8 * c);
-          d1[c] = *reinterpret_cast<const f32x4 *>(sd + 32 + 8 * c);
-        }
+        for (int c = 0; c < 4; ++c) l1[c] = *reinterpret_cast<const f32x4 *>(sl + 32 + 8 * c);
       }
       if (ks > 0) sa1 = mfma32(aq[ks], kv[ks], sa1);
       dpa1 = mfma32(ao[ks], vv[ks], dpa1);
 #pragma unroll
       for (int i = 0; i < 16 / KS; ++i) {
         const int r = ks * (16 / KS) + i;
-        b_exp(s0, dp0, r, l0[r >> 2][r & 3], d0[r >> 2][r & 3]);
+        b_exp(s0, dp0, r, l0[r >> 2][r & 3]);
       }
       if ((ks + 1) * (16 / KS) == 8) b_pack(s0, dp0, 0, pb0[0], dsb0[0]);
       if (ks == KS - 1) {
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 8 / NC; ++i) {
         const int r = c * (8 / NC) + i;
-        b_exp(s1, dp1, r, l1[r >> 2][r & 3], d1[r >> 2][r & 3]);
+        b_exp(s1, dp1, r, l1[r >> 2][r & 3]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -380,7 +391,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 
     // ---- phase 3a: A(st + 1, 0) with the exponentials of B(st, 1) rows 8-15
     // (after the last stage A reads a stale buffer and is discarded)
-    f32x16 sa0 = s_first(aq[0], pn, mwn[0]), dpa0 = (f32x16){};
+    f32x16 sa0 = s_first(aq[0], pn, mwn[0]), dpa0 = neg_d(nbuf, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 2 < KS) {
@@ -392,7 +403,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 8 / KS; ++i) {
         const int r = 8 + ks * (8 / KS) + i;
-        b_exp(s1, dp1, r, l1[r >> 2][r & 3], d1[r >> 2][r & 3]);
+        b_exp(s1, dp1, r, l1[r >> 2][r & 3]);
       }
       if (ks == KS - 2) issue_tr(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, xa);
       if (ks == KS - 1) b_pack(s1, dp1, 1, pb1[1], dsb1[1]);
@@ -524,11 +535,11 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
       if (!row_ok) { qv[ks] = (bf16x8){}; dov[ks] = (bf16x8){}; }
     }
   }
-  float lse2 = 0.f, Dr = 0.f;
+  float lse2 = 0.f, nD = 0.f;  // the row's lse * log2(e) and -D
   if (row_ok) {
     const int64_t w0 = ws_row0(b, h, a.Hq, a.S64);
     lse2 = a.ws[w0 + row];
-    Dr = a.ws[w0 + a.S64 + row];
+    nD = a.ws[w0 + a.S64 + row];
   }
   const int4 rb = row_ok ? a.m.rowb[row] : make_int4(0, 0, 0, 0);
   const int hm = bitmap_head(a.m.bm_heads, h, a.Hq, a.G);
@@ -606,7 +617,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2));
-          dp[r] = p * (dp[r] - Dr);
+          dp[r] = p * (dp[r] + nD);
         }
         // dQ^T += K^T dS^T, one 16-key step at a time.
         auto step = [&](auto tc) {

@@ -335,7 +335,7 @@ struct FwdArgs {
 };
 
 // Backward workspace: per (b, h), S64 = S rounded up to 64 rows of
-// lse * log2(e), then S64 rows of D = rowsum(dO * O); pad rows hold 0.
+// lse * log2(e), then S64 rows of -D, D = rowsum(dO * O); pad rows hold 0.
 struct BwdArgs {
   const bf16 *q, *k, *v, *o, *dout;
   const float *lse;
