@@ -152,9 +152,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   // Loads of stage st into `stg`: the Q and dO tiles of head kvh*G + g, and
   // 64 rows each of lse2 and D (lanes 0..7 of every wave, 16 bytes each), so
   // that every wave issues the same number of loads per stage.
-  auto load_stage = [&](int st, char *stg) {
+  auto load_stage = [&](int st, char *stg, uint32_t ent) {
     const int e = st / G, g = st - e * G;
-    const int qt = (int)(list[e] & 0x7fffffffu);
+    const int qt = (int)(ent & 0x7fffffffu);
     const int h = kvh * G + g;
     dma.load(stg, a.q + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
     dma.load(stg + OFF_DO, a.dout + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
@@ -172,9 +172,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 
   // Allowed-row words of the lane's key for the two units of stage st (all
   // ones unless the tile is partial); returns whether it is partial.
-  auto stage_mask = [&](int st, uint32_t (&mw)[2]) -> bool {
-    const int e = st / G, g = st - e * G;
-    const uint32_t ent = list[e];
+  auto stage_mask = [&](int st, uint32_t ent, uint32_t (&mw)[2]) -> bool {
+    const int g = st % G;
     mw[0] = 0xffffffffu;
     mw[1] = 0xffffffffu;
     const bool part = (ent >> 31) != 0;
@@ -273,9 +272,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   uint32_t mwc[2], mwn[2];
   bool pc = false, pn = false;  // stages st and st + 1 are partial
   if (nst > 0) {
-    load_stage(0, smem);
-    if (nst > 1) load_stage(1, smem + STAGE);
-    pc = stage_mask(0, mwc);
+    load_stage(0, smem, list[0]);
+    if (nst > 1) load_stage(1, smem + STAGE, list[1 / G]);
+    pc = stage_mask(0, list[0], mwc);
     dma_wait();
     __syncthreads();
     f32x16 sa0 = s_first(rows_q(smem, 0, 0), pc, mwc[0]), dpa0 = neg_d(smem, 0);
@@ -289,7 +288,11 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   }
 
   int cur = 0;  // buffer of stage st
+  // List entries are read a stage before they are needed, so that the
+  // latency of the scalar load is covered by the products of a stage.
+  uint32_t ent1 = nst > 1 ? list[1 / G] : 0u;  // stage st + 1
   for (int st = 0; st < nst; ++st) {
+    const uint32_t ent2 = st + 2 < nst ? list[(st + 2) / G] : 0u;  // stage st + 2
 #pragma unroll
     for (int i = 0; i < DB; ++i) { in_agpr(dk[i]); in_agpr(dv[i]); }
 #pragma unroll
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     const char *buf = smem + cur * STAGE;
     const char *nbuf = smem + nxt * STAGE;
     if (st + 1 < nst) {
-      pn = stage_mask(st + 1, mwn);
+      pn = stage_mask(st + 1, ent1, mwn);
     } else {
       pn = false;
       mwn[0] = 0xffffffffu;
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     // stage st + 1 is in LDS for every wave, and stage st - 1's buffer is free
     dma_wait();
     __syncthreads();
-    if (st + 2 < nst) load_stage(st + 2, smem + fre * STAGE);
+    if (st + 2 < nst) load_stage(st + 2, smem + fre * STAGE, ent2);
     aq[0] = rows_q(nbuf, 0, 0);
     ao[0] = rows_o(nbuf, 0, 0);
     aq[1] = rows_q(nbuf, 0, 1);
@@ -430,6 +433,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     }
     mwc[0] = mwn[0];
     mwc[1] = mwn[1];
+    ent1 = ent2;
     pc = pn;
     cur = nxt;
   }
