@@ -84,6 +84,33 @@ def forward(q, k, v, spec, scale=None, heads=None, row_block=512):
     return o, lse
 
 
+def merge(o_parts, lse_parts):
+    """O and LSE over a union of disjoint key sets from the results over each
+    set.
+
+    "FlashAttention vs. RingAttention", Ring Attention section (Blockwise
+    Parallel Transformer): the output of each key block is rescaled by the
+    difference between its own softmax normaliser and the global one.  With
+    LSE_c the natural-log normaliser of part c (its LSE):
+        LSE = ln sum_c exp(LSE_c),   O = sum_c exp(LSE_c - LSE) O_c.
+    A row with no key in any part keeps O = 0 and LSE = -inf.
+
+    o_parts: list of [B,S,H,d] float64; lse_parts: list of [B,H,S] float64.
+    """
+    lse = np.stack([np.asarray(x, dtype=np.float64) for x in lse_parts])  # [C,B,H,S]
+    m = lse.max(axis=0)
+    live = np.isfinite(m)
+    m0 = np.where(live, m, 0.0)
+    w = np.exp(lse - m0)                   # exp(-inf) = 0 for empty parts
+    tot = np.where(live, w.sum(axis=0), 1.0)
+    out_lse = np.where(live, m0 + np.log(tot), -np.inf)
+    wn = np.where(live, w / tot, 0.0)      # [C,B,H,S]
+    o = np.zeros_like(np.asarray(o_parts[0], dtype=np.float64))
+    for c, oc in enumerate(o_parts):
+        o += wn[c].transpose(0, 2, 1)[..., None] * oc
+    return o, out_lse
+
+
 def round_bf16(x):
     """Round float64 values to the nearest bfloat16 value (8 significant
     bits, ties to even), returned as float64.  Normal-range values only."""

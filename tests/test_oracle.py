@@ -7,7 +7,9 @@
 * closed forms (uniform V, Q = 0, single-key rows) and invariants (rows of P
   sum to one, sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, unseen keys get zero
   gradient, DOCUMENT = independent per-document attention, GQA = MHA on
-  repeated K/V) pin the arithmetic end to end.
+  repeated K/V) pin the arithmetic end to end;
+* the merge of partial results is pinned by the forward over the union of
+  disjoint key sets, a two-key closed form and empty parts.
 """
 import json
 import math
@@ -395,3 +397,64 @@ def test_grad_rows_matches_backward():
                 np.testing.assert_allclose(r["lse"], g["lse"][0, h, rows], atol=1e-14)
                 np.testing.assert_allclose(r["m_dq"], g["m_dq"][0, rows, h], atol=1e-13)
                 np.testing.assert_allclose(r["m_o"], g["m_o"][0, rows, h], atol=1e-14)
+
+
+def _key_split(base, cuts):
+    """Specs of base restricted to the key ranges between consecutive cuts
+    (a one-row-block bitmap with column blocks at the cuts)."""
+    S = base["S"]
+    offs = [0] + list(cuts) + [S]
+    out = []
+    for c in range(len(offs) - 1):
+        bits = np.zeros((1, 1, len(offs) - 1), dtype=np.uint8)
+        bits[0, 0, c] = 1
+        out.append(syn.with_bitmap(base, [0, S], offs, bits))
+    return out
+
+
+@pytest.mark.parametrize("base,cuts", [
+    (syn.spec_causal(97), [40]),
+    (syn.spec_full(64), [10, 33, 50]),
+    (syn.spec_document([30, 20, 27], True), [25]),
+    (syn.spec_sliding(80, 16, True), [8, 72]),
+])
+def test_merge_over_key_partition_equals_forward(base, cuts):
+    """Attention over the union of disjoint key sets, from the pinned fp64
+    forward over each set, equals the forward over the union; the part
+    order does not matter."""
+    S = base["S"]
+    x = syn.attention_inputs(1, S, 4, 2, 16, seed=4)
+    q, k, v = (syn.bf16_bits_to_f32(x[n]).astype(np.float64) for n in ("q", "k", "v"))
+    parts = [ora.forward(q, k, v, sp) for sp in _key_split(base, cuts)]
+    o, lse = ora.merge([p[0] for p in parts], [p[1] for p in parts])
+    o_ref, lse_ref = ora.forward(q, k, v, base)
+    assert np.abs(o - o_ref).max() < 1e-12
+    fin = np.isfinite(lse_ref)
+    assert (np.isfinite(lse) == fin).all()
+    assert np.abs(lse[fin] - lse_ref[fin]).max() < 1e-12
+    o2, lse2 = ora.merge([p[0] for p in parts[::-1]], [p[1] for p in parts[::-1]])
+    assert np.abs(o2 - o).max() < 1e-12 and np.abs(lse2[fin] - lse[fin]).max() < 1e-12
+
+
+def test_merge_two_single_keys_closed_form():
+    """Two parts of one key each: the merge is the softmax over the two
+    scores written out by hand."""
+    va, vb = np.array([1.0, -2.0, 0.5]), np.array([3.0, 0.25, -1.0])
+    sa, sb = 0.7, -1.3
+    o, lse = ora.merge([va.reshape(1, 1, 1, 3), vb.reshape(1, 1, 1, 3)],
+                       [np.full((1, 1, 1), sa), np.full((1, 1, 1), sb)])
+    pa = math.exp(sa) / (math.exp(sa) + math.exp(sb))
+    assert np.abs(o.reshape(3) - (pa * va + (1 - pa) * vb)).max() < 1e-15
+    assert abs(lse.item() - math.log(math.exp(sa) + math.exp(sb))) < 1e-15
+
+
+def test_merge_empty_parts():
+    """A part with no key for a row (O = 0, LSE = -inf) leaves the other part
+    unchanged; rows empty in every part stay O = 0, LSE = -inf."""
+    o1 = np.arange(6, dtype=np.float64).reshape(1, 2, 1, 3)
+    l1 = np.array([[[0.3, -np.inf]]])
+    o2 = np.zeros((1, 2, 1, 3))
+    l2 = np.full((1, 1, 2), -np.inf)
+    o, lse = ora.merge([o1, o2], [l1, l2])
+    assert (o[0, 0] == o1[0, 0]).all() and lse[0, 0, 0] == 0.3
+    assert (o[0, 1] == 0).all() and np.isneginf(lse[0, 0, 1])
