@@ -118,6 +118,35 @@ def cpu_baseline(seconds_cap=30.0):
                       f"masks {done}: {secs:.1f} s, effective flops as for the GPU"}
 
 
+def merge_rate(lcm, torch, dev, S=16384, Hq=64, d=128, reps=20):
+    """HBM rate of the merge of two fp32 partial results into the final bf16
+    O and LSE at [1, S, Hq, d] (the partial-attention + merge primitive).
+    Algorithmic bytes per (s, h) row: two fp32 O rows and two LSE read, one
+    bf16 O row and one LSE written.  HIP events on the launch stream."""
+    g = torch.Generator(device=dev).manual_seed(0)
+    o1 = torch.randn((1, S, Hq, d), generator=g, device=dev)
+    o2 = torch.randn((1, S, Hq, d), generator=g, device=dev)
+    l1 = torch.randn((1, Hq, S), generator=g, device=dev)
+    l2 = torch.randn((1, Hq, S), generator=g, device=dev)
+    o = torch.empty((1, S, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty_like(l1)
+    lcm.merge(o1, l1, o2, l2, bf16_out=True, out=o, lse_out=lse)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        lcm.merge(o1, l1, o2, l2, bf16_out=True, out=o, lse_out=lse)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = S * Hq * (2 * d * 4 + 2 * 4 + d * 2 + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"shape": [1, S, Hq, d], "ms_per_launch": round(ms, 4), "bytes_per_launch": nbytes,
+            "achieved_GBps": round(gbs, 1), "peak_GBps": PEAK_HBM_GBS,
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def sources_sha256():
     h = hashlib.sha256()
     for rel in TRAFFIC_SOURCES:
@@ -358,6 +387,8 @@ def main():
         "plan_build_s": round(plan_secs, 3),
         "detail": detail,
     }
+    log("merge of partial results")
+    out["merge"] = merge_rate(lcm, torch, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline()

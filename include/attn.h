@@ -224,6 +224,46 @@ attn_status attn_bwd_dq(const attn_plan *plan, const void *q, const void *k,
                         const void *v, const float *lse, const void *dout, void *dq,
                         const void *ws, size_t ws_bytes, attn_stream_t stream);
 
+/*
+ * Partial results for attention over chunks of the keys, the one-GPU
+ * building block of ring-style sequence parallelism ("FlashAttention vs.
+ * RingAttention", Ring Attention section: the Blockwise Parallel Transformer
+ * computes each query block against one key/value block at a time and
+ * rescales each block's output by the difference between its own softmax
+ * normaliser and the global one).
+ *
+ * attn_fwd_partial: attn_fwd with O written in fp32 ([B, S, Hq, d], 16-byte
+ * aligned): the chunk's attention output, normalised by its own sum, and its
+ * LSE.  A chunk is a plan whose mask keeps only that chunk's keys (for
+ * instance a block bitmap with one row block and one column block per
+ * chunk).
+ *
+ * attn_merge: the O and LSE over the union of two disjoint key sets, from the
+ * results over each set:
+ *   LSE = ln(exp(LSE1) + exp(LSE2)),
+ *   O   = exp(LSE1 - LSE) O1 + exp(LSE2 - LSE) O2.
+ *   o1, o2:          [B, S, Hq, d] fp32, 16-byte aligned (attn_fwd_partial
+ *                    results, or earlier merges);
+ *   o:               [B, S, Hq, d], fp32 when o_bf16 == 0 (to merge further),
+ *                    bf16 otherwise (the final O), 16-byte aligned;
+ *   lse1, lse2, lse: [B, Hq, S] fp32, natural log, -inf on rows with no key
+ *                    in that part, 4-byte aligned.
+ * A row with no key in either part gets O = 0 and LSE = -inf.  The outputs
+ * may not overlap the inputs or each other.  Allocates nothing; enqueues one
+ * kernel on `stream`.  Errors: ATTN_ERR_INVALID (NULL or misaligned pointer,
+ * non-positive size, overlapping buffers), ATTN_ERR_UNSUPPORTED (d not 64 or
+ * 128, S >= 2^30, B or Hq > 65535), ATTN_ERR_DEVICE (launch failure).
+ *
+ * The backward over a chunk is attn_bwd with the chunk's plan and the merged
+ * (bf16) O and LSE: it gives the chunk's share of dQ (the shares add up to
+ * dQ) and dK, dV of the chunk's keys (zero for the other keys).
+ */
+attn_status attn_fwd_partial(const attn_plan *plan, const void *q, const void *k,
+                             const void *v, float *o, float *lse, attn_stream_t stream);
+attn_status attn_merge(const float *o1, const float *lse1, const float *o2, const float *lse2,
+                       void *o, int o_bf16, float *lse, int64_t B, int64_t S, int64_t Hq,
+                       int64_t d, attn_stream_t stream);
+
 void attn_plan_destroy(attn_plan *plan);
 
 const char *attn_last_error(void);

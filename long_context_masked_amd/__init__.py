@@ -161,6 +161,47 @@ def bwd(plan: Plan, q, k, v, o, lse, do, workspace=None, grads=None):
     return dq, dk, dv
 
 
+def fwd_partial(plan: Plan, q, k, v, out=None, lse=None):
+    """The forward over the keys the plan's mask keeps, with O in fp32
+    [B,S,Hq,d] (to be merged with other chunks) and LSE [B,Hq,S]."""
+    import torch
+    B, S, Hq, Hkv, d = plan.shape
+    _check_tensor(q, "q", (B, S, Hq, d), torch)
+    _check_tensor(k, "k", (B, S, Hkv, d), torch)
+    _check_tensor(v, "v", (B, S, Hkv, d), torch)
+    plan.bind(q.device)
+    o = torch.empty((B, S, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    P = C.c_void_p
+    L.check(L.lib().attn_fwd_partial(plan.handle, P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
+                                     P(o.data_ptr()), P(lse.data_ptr()), P(stream)))
+    return o, lse
+
+
+def merge(o1, lse1, o2, lse2, bf16_out=False, out=None, lse_out=None):
+    """O and LSE over the union of two disjoint key sets from the results
+    over each set (fp32 O [B,S,Hq,d], LSE [B,Hq,S]); the merged O is fp32,
+    or bf16 with bf16_out (the final result, as attn_fwd returns it)."""
+    import torch
+    B, S, Hq, d = o1.shape
+    for t, n in ((o1, "o1"), (o2, "o2")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, S, Hq, d) or not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous float32 [B, S, Hq, d]")
+    for t, n in ((lse1, "lse1"), (lse2, "lse2")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, Hq, S) or not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous float32 [B, Hq, S]")
+    dt = torch.bfloat16 if bf16_out else torch.float32
+    o = torch.empty((B, S, Hq, d), dtype=dt, device=o1.device) if out is None else out
+    lse = torch.empty_like(lse1) if lse_out is None else lse_out
+    stream = torch.cuda.current_stream(o1.device).cuda_stream
+    P = C.c_void_p
+    L.check(L.lib().attn_merge(P(o1.data_ptr()), P(lse1.data_ptr()), P(o2.data_ptr()),
+                               P(lse2.data_ptr()), P(o.data_ptr()), int(bool(bf16_out)),
+                               P(lse.data_ptr()), B, S, Hq, d, P(stream)))
+    return o, lse
+
+
 def attention(q, k, v, plan: Plan):
     """Differentiable masked attention through torch.autograd."""
     import torch

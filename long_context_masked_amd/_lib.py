@@ -71,6 +71,8 @@ SIGNATURES = {
     "attn_bwd_preprocess": (C.c_int, [C.c_void_p] * 5 + [C.c_size_t, C.c_void_p]),
     "attn_bwd_dkdv": (C.c_int, [C.c_void_p] * 9 + [C.c_size_t, C.c_void_p]),
     "attn_bwd_dq": (C.c_int, [C.c_void_p] * 8 + [C.c_size_t, C.c_void_p]),
+    "attn_fwd_partial": (C.c_int, [C.c_void_p] * 7),
+    "attn_merge": (C.c_int, [C.c_void_p] * 5 + [C.c_int, C.c_void_p] + [C.c_int64] * 4 + [C.c_void_p]),
     "attn_plan_destroy": (None, [C.c_void_p]),
     "attn_last_error": (C.c_char_p, []),
     "attn_version": (C.c_char_p, []),

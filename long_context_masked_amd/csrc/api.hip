@@ -11,6 +11,9 @@ hipError_t launch_fwd(const FwdArgs &a, int d, int HG, int n_items, int B, hipSt
 hipError_t launch_bwd_pre(const BwdArgs &a, int d, int B, hipStream_t st);
 hipError_t launch_dkdv(const BwdArgs &a, int d, int B, hipStream_t st);
 hipError_t launch_dq(const BwdArgs &a, int d, int HG, int B, hipStream_t st);
+hipError_t launch_merge(const float *o1, const float *lse1, const float *o2, const float *lse2,
+                        void *o, bool o_bf16, float *lse, int64_t B, int S, int Hq, int d,
+                        hipStream_t st);
 }  // namespace lcm
 
 using namespace lcm;
@@ -82,8 +85,9 @@ extern "C" attn_status attn_plan_bind(attn_plan *plan, void *dev_buf, size_t byt
   return ATTN_OK;
 }
 
-extern "C" attn_status attn_fwd(const attn_plan *p, const void *q, const void *k, const void *v,
-                                void *o, float *lse, attn_stream_t stream) {
+namespace {
+attn_status fwd_impl(const attn_plan *p, const void *q, const void *k, const void *v, void *o,
+                     bool o32, float *lse, attn_stream_t stream) {
   clear_error();
   attn_status s;
   if ((s = check_plan(p)) != ATTN_OK) return s;
@@ -97,7 +101,8 @@ extern "C" attn_status attn_fwd(const attn_plan *p, const void *q, const void *k
   a.q = static_cast<const bf16 *>(q);
   a.k = static_cast<const bf16 *>(k);
   a.v = static_cast<const bf16 *>(v);
-  a.o = static_cast<bf16 *>(o);
+  if (o32) a.o32 = static_cast<float *>(o);
+  else a.o = static_cast<bf16 *>(o);
   a.lse = lse;
   a.S = (int)p->shape.S;
   a.Hq = (int)p->shape.Hq;
@@ -112,6 +117,18 @@ extern "C" attn_status attn_fwd(const attn_plan *p, const void *q, const void *k
                                   (int)p->shape.B, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;
+}
+}  // namespace
+
+extern "C" attn_status attn_fwd(const attn_plan *p, const void *q, const void *k, const void *v,
+                                void *o, float *lse, attn_stream_t stream) {
+  return fwd_impl(p, q, k, v, o, false, lse, stream);
+}
+
+extern "C" attn_status attn_fwd_partial(const attn_plan *p, const void *q, const void *k,
+                                        const void *v, float *o, float *lse,
+                                        attn_stream_t stream) {
+  return fwd_impl(p, q, k, v, o, true, lse, stream);
 }
 
 namespace {
@@ -259,4 +276,37 @@ extern "C" attn_status attn_bwd(const attn_plan *p, const void *q, const void *k
   LCM_CHECK(launched(launch_bwd_pre(a, d, B, st), "backward preprocess"));
   LCM_CHECK(launched(launch_dkdv(a, d, B, st), "dK/dV"));
   return launched(launch_dq(a, d, p->HG, B, st), "dQ");
+}
+
+extern "C" attn_status attn_merge(const float *o1, const float *lse1, const float *o2,
+                                  const float *lse2, void *o, int o_bf16, float *lse, int64_t B,
+                                  int64_t S, int64_t Hq, int64_t d, attn_stream_t stream) {
+  clear_error();
+  if (B < 1 || S < 1 || Hq < 1) return fail(ATTN_ERR_INVALID, "B, S, Hq must be >= 1");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%lld (supported: 64, 128)", (long long)d);
+  if (S >= (int64_t(1) << 30) || Hq > 65535 || B > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "S must be < 2^30, B and Hq <= 65535");
+  LCM_CHECK(check_tensor(o1, "o1", 16));
+  LCM_CHECK(check_tensor(o2, "o2", 16));
+  LCM_CHECK(check_tensor(o, "o", 16));
+  LCM_CHECK(check_tensor(lse1, "lse1", 4));
+  LCM_CHECK(check_tensor(lse2, "lse2", 4));
+  LCM_CHECK(check_tensor(lse, "lse", 4));
+  // the outputs may not overlap the inputs (every lane of a row reads the
+  // row's LSE before one of them writes it) or each other
+  const uint64_t rows = (uint64_t)(B * S * Hq);
+  const uint64_t ni = rows * (uint64_t)d * 4, no = rows * (uint64_t)d * (o_bf16 ? 2 : 4), nl = rows * 4;
+  auto overlap = [](const void *x, uint64_t nx, const void *y, uint64_t ny) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+    return a < b + ny && b < a + nx;
+  };
+  if (overlap(o, no, o1, ni) || overlap(o, no, o2, ni) || overlap(o, no, lse1, nl) ||
+      overlap(o, no, lse2, nl) || overlap(lse, nl, o1, ni) || overlap(lse, nl, o2, ni) ||
+      overlap(lse, nl, lse1, nl) || overlap(lse, nl, lse2, nl) || overlap(o, no, lse, nl))
+    return fail(ATTN_ERR_INVALID, "outputs overlap the inputs or each other");
+  if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
+  (void)hipGetLastError();
+  return launched(launch_merge(o1, lse1, o2, lse2, o, o_bf16 != 0, lse, B, (int)S, (int)Hq, (int)d,
+                               reinterpret_cast<hipStream_t>(stream)),
+                  "merge");
 }

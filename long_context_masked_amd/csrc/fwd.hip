@@ -304,20 +304,111 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const float l_tot = sum_halves(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16 *orow = a.o + ((int64_t)b * S + row) * ldq + (int64_t)h * D;
+    const int64_t o0 = ((int64_t)b * S + row) * ldq + (int64_t)h * D;
+    if (a.o32) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int d0 = db * 32 + 8 * c + 4 * hh;
-        *reinterpret_cast<bf16x4 *>(orow + d0) = __builtin_shufflevector(
-            cvt2(o[db][4 * c] * inv, o[db][4 * c + 1] * inv),
-            cvt2(o[db][4 * c + 2] * inv, o[db][4 * c + 3] * inv), 0, 1, 2, 3);
-      }
+        for (int c = 0; c < 4; ++c) {
+          const int d0 = db * 32 + 8 * c + 4 * hh;
+          *reinterpret_cast<f32x4 *>(a.o32 + o0 + d0) =
+              (f32x4){o[db][4 * c] * inv, o[db][4 * c + 1] * inv, o[db][4 * c + 2] * inv,
+                      o[db][4 * c + 3] * inv};
+        }
+    } else {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int d0 = db * 32 + 8 * c + 4 * hh;
+          *reinterpret_cast<bf16x4 *>(a.o + o0 + d0) = __builtin_shufflevector(
+              cvt2(o[db][4 * c] * inv, o[db][4 * c + 1] * inv),
+              cvt2(o[db][4 * c + 2] * inv, o[db][4 * c + 3] * inv), 0, 1, 2, 3);
+        }
+    }
     if (hh == 0)
       a.lse[((int64_t)b * a.Hq + h) * S + row] =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of two attention results over disjoint key sets for the same queries
+// ("FlashAttention vs. RingAttention", Ring Attention section: the Blockwise
+// Parallel Transformer rescales each key block's output by the difference
+// between its own softmax normaliser and the global one):
+//   LSE = ln(e^LSE1 + e^LSE2),  O = e^(LSE1 - LSE) O1 + e^(LSE2 - LSE) O2.
+// A row with no key in either part gets O = 0, LSE = -inf.  The parts are
+// fp32; the result is fp32 (to merge further) or bf16 (OB).  One group of
+// D/8 lanes per (b, s, h) row, 8 values per lane, rows in memory order;
+// bound by HBM.
+// ---------------------------------------------------------------------------
+template <int D, bool OB>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float *o1, const float *lse1,
+                                                         const float *o2, const float *lse2,
+                                                         void *o, float *lse, int S, int Hq,
+                                                         int64_t nrows) {
+  constexpr int CPR = D / 8;      // lanes per row
+  constexpr int RPB = 256 / CPR;  // rows per workgroup
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
+  if (r >= nrows) return;
+  const int c = threadIdx.x % CPR;
+  const int h = (int)(r % Hq);
+  const int64_t bs = r / Hq;  // b * S + s
+  const int64_t li = ((bs / S) * Hq + h) * S + bs % S;
+  const float l1 = lse1[li], l2 = lse2[li];
+  const float m = __builtin_fmaxf(l1, l2);
+  float w1 = 0.f, w2 = 0.f, lo = kNegInf;
+  if (m > kNegInf) {
+    const float e1 = __expf(l1 - m), e2 = __expf(l2 - m);  // 0 for an empty part
+    const float t = e1 + e2;
+    w1 = e1 / t;
+    w2 = e2 / t;
+    lo = m + __logf(t);
+  }
+  const int64_t g = r * D + c * 8;
+  const f32x4 x0 = *reinterpret_cast<const f32x4 *>(o1 + g);
+  const f32x4 x1 = *reinterpret_cast<const f32x4 *>(o1 + g + 4);
+  const f32x4 y0 = *reinterpret_cast<const f32x4 *>(o2 + g);
+  const f32x4 y1 = *reinterpret_cast<const f32x4 *>(o2 + g + 4);
+  const f32x4 z0 = w1 * x0 + w2 * y0, z1 = w1 * x1 + w2 * y1;
+  if constexpr (OB) {
+    *reinterpret_cast<bf16x8 *>(static_cast<bf16 *>(o) + g) =
+        pack8(z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]);
+  } else {
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + g) = z0;
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + g + 4) = z1;
+  }
+  if (c == 0) lse[li] = lo;
+}
+
+#define LCM_MERGE(D, OB)                                                                        \
+  template __global__ void attn_merge_kernel<D, OB>(const float *, const float *, const float *, \
+                                                    const float *, void *, float *, int, int,   \
+                                                    int64_t);
+LCM_MERGE(128, true)
+LCM_MERGE(128, false)
+LCM_MERGE(64, true)
+LCM_MERGE(64, false)
+#undef LCM_MERGE
+
+hipError_t launch_merge(const float *o1, const float *lse1, const float *o2, const float *lse2,
+                        void *o, bool o_bf16, float *lse, int64_t B, int S, int Hq, int d,
+                        hipStream_t st) {
+  const int64_t nrows = B * (int64_t)S * Hq;
+  const int rpb = 256 / (d / 8);
+  const dim3 grid((unsigned)((nrows + rpb - 1) / rpb)), block(256);
+  if (d == 128 && o_bf16)
+    hipLaunchKernelGGL((attn_merge_kernel<128, true>), grid, block, 0, st, o1, lse1, o2, lse2, o, lse, S, Hq, nrows);
+  else if (d == 128)
+    hipLaunchKernelGGL((attn_merge_kernel<128, false>), grid, block, 0, st, o1, lse1, o2, lse2, o, lse, S, Hq, nrows);
+  else if (d == 64 && o_bf16)
+    hipLaunchKernelGGL((attn_merge_kernel<64, true>), grid, block, 0, st, o1, lse1, o2, lse2, o, lse, S, Hq, nrows);
+  else if (d == 64)
+    hipLaunchKernelGGL((attn_merge_kernel<64, false>), grid, block, 0, st, o1, lse1, o2, lse2, o, lse, S, Hq, nrows);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // Every variant is instantiated explicitly: implicit instantiation from the

@@ -325,7 +325,8 @@ struct MaskArgs {
 
 struct FwdArgs {
   const bf16 *q, *k, *v;
-  bf16 *o;
+  bf16 *o;      // bf16 output, or
+  float *o32;   // fp32 output (partial results that are merged later)
   float *lse;
   int S, Hq, Hkv, G;
   float sl2;  // softmax scale * log2(e)

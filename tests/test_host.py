@@ -363,6 +363,39 @@ def test_launch_entry_points_validate_before_touching_the_gpu():
     assert lib.attn_bwd_workspace_bytes(p.handle) >= 2 * S * 4
 
 
+def test_merge_validates_before_touching_the_gpu():
+    """attn_merge rejects NULL, misaligned and overlapping buffers and
+    unsupported sizes before any HIP call; a forced device error is reported
+    as such."""
+    lib = L.lib()
+    P = C.c_void_p
+    B, S, H, d = 1, 64, 2, 64
+    ni, no, nl = B * S * H * d * 4, B * S * H * d * 2, B * S * H * 4
+    o1, o2, o = 1 << 20, 2 << 20, 3 << 20          # never dereferenced
+    l1, l2, lo = 4 << 20, 5 << 20, 6 << 20
+
+    def call(a=o1, b=l1, c=o2, e=l2, f=o, g=lo, dd=d, SS=S, ob=1):
+        return lib.attn_merge(P(a), P(b), P(c), P(e), P(f), ob, P(g), B, SS, H, dd, None)
+
+    assert call(a=0) == L.ATTN_ERR_INVALID
+    assert call(g=0) == L.ATTN_ERR_INVALID
+    assert call(c=o2 + 8) == L.ATTN_ERR_INVALID                 # O must be 16-byte aligned
+    assert call(e=l2 + 2) == L.ATTN_ERR_INVALID                 # LSE 4-byte aligned
+    assert call(f=o1) == L.ATTN_ERR_INVALID                     # in place
+    assert b"overlap" in lib.attn_last_error()
+    assert call(f=o2 + ni - 16) == L.ATTN_ERR_INVALID           # partial overlap
+    assert call(g=o + no - 4, ob=1) == L.ATTN_ERR_INVALID       # bf16 output and LSE
+    assert call(g=o + 2 * no - 4, ob=0) == L.ATTN_ERR_INVALID   # fp32 output is twice as long
+    assert call(g=l1 + nl - 4) == L.ATTN_ERR_INVALID
+    assert call(dd=96) == L.ATTN_ERR_UNSUPPORTED
+    assert call(SS=0) == L.ATTN_ERR_INVALID
+    os.environ["ATTN_FORCE_DEVICE_ERROR"] = "1"
+    try:
+        assert call() == L.ATTN_ERR_DEVICE
+    finally:
+        del os.environ["ATTN_FORCE_DEVICE_ERROR"]
+
+
 def test_scale_default_and_stats_fields():
     S = 300
     p = lcm.Plan(3, S, 8, 2, 128, syn.spec_sliding(S, 40, False))
