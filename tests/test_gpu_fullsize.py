@@ -9,8 +9,8 @@ At these sizes the fp64 oracle cannot run whole tensors, so the tests check:
 * every row's mask coverage with Q = 0: all allowed keys then get the same
   weight, so exp(LSE_i) must equal the number of allowed keys n_i (counted
   from the oracle's predicate) and O_i the mean of the allowed v_j (beyond
-  S = 64K on sampled blocks of rows, and with more than 8 bitmap heads on
-  two of them, to keep the oracle's count within a minute);
+  S = 64K on sampled blocks of rows, and with more than 2 bitmap heads on
+  the first and last, to keep the oracle's count within seconds);
 * the identity sum_j dV_j = sum over query rows of the group of dO_i, which
   holds at any size because every probability row sums to one;
 * uniform V: O = v, dQ = dK = 0.
@@ -119,7 +119,7 @@ def test_sampled_rows(label, spec, Hkv):
 @pytest.mark.parametrize("label,spec,Hkv", CASES, ids=IDS)
 def test_mask_coverage_every_row(label, spec, Hkv):
     """Q = 0: exp(LSE_i) = n_i for every row and head (beyond S = 64K on
-    sampled row blocks; with more than 8 bitmap heads on the first and last);
+    sampled row blocks; with more than 2 bitmap heads on the first and last);
     O_i = mean of allowed v_j."""
     S = spec["S"]
     x, t = inputs(S, Hkv)
@@ -132,7 +132,7 @@ def test_mask_coverage_every_row(label, spec, Hkv):
     vbits = x["v"]
     # the oracle counts about 2.5e8 (row, key) pairs per second
     blocks = list(range(0, S, 2048)) if S <= 65536 else [0, S // 2 - 1024, S - 2048]
-    hms = range(nh) if nh <= 8 else [0, nh - 1]
+    hms = range(nh) if nh <= 2 else [0, nh - 1]
     for hm in hms:
         rows = np.concatenate([np.arange(i0, min(S, i0 + 2048)) for i0 in blocks])
         counts = np.concatenate([om.allowed(spec, i0, min(S, i0 + 2048), hm).sum(axis=1) for i0 in blocks])
