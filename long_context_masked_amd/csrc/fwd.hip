@@ -226,6 +226,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    // Two waves share each SIMD (two workgroups per CU).  The wave in phase B
+    // runs at raised priority, so that its products go first while the
+    // other wave's phase A fills the gaps; this staggers the waves' phases.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
     // ---- phase B: O^T += V^T P^T(t), 16 keys per step, with the
     // exponentials of key block 1 (steps 0 and 1) and the max of S^T(t + 1)
     auto issue = [&](auto stc, s16x4(&x)[2 * DB]) {
@@ -272,6 +278,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (NEXT) {
       m_update(mx);
       sc[0] = sn[0];
