@@ -608,12 +608,21 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
     if (active) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
+        // Two waves share each SIMD; the one computing S and dP runs at raised
+        // priority, which staggers the waves so that one's products overlap
+        // the other's softmax-gradient work.
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           s = mfma32(lds_rows(stage, roff[ks] + kh * 32 * T::ROWB), qv[ks], s);
           dp = mfma32(lds_rows(stage + T::BYTES, roff[ks] + kh * 32 * T::ROWB), dov[ks], dp);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
         if (partial) {  // masked scores -> -inf, so that P = 0 there
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[r] = keep_or(mw[kh], 8 * (r >> 2) + (r & 3), s[r], kNegInf);
