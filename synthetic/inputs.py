@@ -232,6 +232,9 @@ def config_mask_specs(config, S=None, Hq=64, Hkv=8, seed=0):
       CAUSAL BLOCKWISE.
     * ``sparse``: uniform 64 / 128 and variable block bitmaps at 50% density,
       per KV head.
+    * ``variants``: FULL SW w=1024, PREFIX LM DOCUMENT and BLOCK CAUSAL
+      DOCUMENT (block 1024) over log-uniform documents in [256, 16K],
+      bidirectional GLOBAL SLIDING, block-causal CAUSAL BLOCKWISE.
     Returns a list of (label, spec).
     """
     if config == "tiny":
@@ -271,6 +274,17 @@ def config_mask_specs(config, S=None, Hq=64, Hkv=8, seed=0):
             ("shared_question", spec_shared_question(q, sample_answers(S - q, 4, seed))),
             ("global_sliding", spec_global_sliding(S, 64, 2048)),
             ("causal_blockwise", spec_causal_blockwise(S, 4096)),
+        ]
+    if config == "variants":
+        S = 32768 if S is None else S
+        docs = sample_doc_lens(S, 256, 16384, seed)
+        return [
+            ("full_sw1024", spec_sliding(S, 1024, False)),
+            ("prefix_lm_document", spec_prefix_lm_document(
+                docs, [sample_prefix(0, L, seed + i) for i, L in enumerate(docs)])),
+            ("block_causal_document", spec_block_causal_document(docs, 1024)),
+            ("global_sliding_bidir", spec_global_sliding(S, 64, 2048, bidirectional=True)),
+            ("causal_blockwise_block_causal", spec_causal_blockwise(S, 4096, "block_causal")),
         ]
     if config == "sparse":
         S = 32768 if S is None else S

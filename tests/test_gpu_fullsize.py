@@ -62,6 +62,8 @@ def _cases():
         out.append(("doc64K_" + label, spec, 8))
     for label, spec in syn.config_mask_specs("hetero"):
         out.append(("hetero32K_" + label, spec, 8))
+    for label, spec in syn.config_mask_specs("variants"):
+        out.append(("variants32K_" + label, spec, 8))
     for label, spec in syn.config_mask_specs("sparse", 32768, Hq=HQ, Hkv=8):
         out.append(("sparse32K_" + label, spec, 8))
     for label, spec in syn.config_mask_specs("sparse", 32768, Hq=HQ, Hkv=64):
