@@ -71,6 +71,11 @@ def workload(name, seqs):
         for label, spec in syn.config_mask_specs("hetero"):
             out.append((label, spec["S"], 64, 8, spec))
         desc = "heterogeneous masks: B=1, S=32K, GQA 64:8, d=128: PREFIX LM CAUSAL, SHARED QUESTION, GLOBAL SLIDING, CAUSAL BLOCKWISE, fwd+bwd"
+    elif name == "tasks":
+        for label, spec in syn.config_mask_specs("tasks"):
+            out.append((label, spec["S"], 64, 8, spec))
+        desc = ("token-level task batches: B=1, S=64K, GQA 64:8, d=128; query shards of 256, 1K "
+                "and 4K tokens, each with a causal context uniform in [shard, 4 shard] tokens, fwd+bwd")
     elif name == "variants":
         for label, spec in syn.config_mask_specs("variants"):
             out.append((label, spec["S"], 64, 8, spec))
@@ -217,7 +222,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="dense", choices=["dense", "document", "hetero", "sparse", "variants"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "document", "hetero", "sparse", "variants", "tasks"])
     ap.add_argument("--seqs", default=None,
                     help="comma-separated sequence lengths (dense: default 1024,8192,16384,49152; "
                          "sparse: default 32768,131072; ignored by document and hetero)")

@@ -28,7 +28,9 @@ __device__ __forceinline__ int64_t ws_row0(int b, int h, int Hq, int S64) {
 }
 
 // ws <- {lse * log2(e), -D = -sum_d dO * O} per (b, h, row); rows in
-// [S, S64) get zeros.  D is stored negated so that the dK/dV pass can start
+// [S, S64) get zeros.  A row with no allowed key (LSE = -inf) gets a large
+// positive lse2 instead, so that the recomputed P = exp2(S c - lse2) is 0 on
+// every key, masked ones (S = -inf) included, rather than -inf + inf.  D is stored negated so that the dK/dV pass can start
 // the accumulation of dP at -D and get dP - D from the products alone.  One group of D/8 lanes per row; the grid covers B * S64 * Hq
 // rows in [b][s][h] order.
 template <int D>
@@ -57,7 +59,8 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
   for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (r < nrows && c == 0) {
     const int64_t w0 = ws_row0(b, h, Hq, S64);
-    ws[w0 + s] = real ? lse[((int64_t)b * Hq + h) * S + s] * kLog2e : 0.f;
+    const float l = real ? lse[((int64_t)b * Hq + h) * S + s] : 0.f;
+    ws[w0 + s] = l > kNegInf ? l * kLog2e : kEmptyRowLse2;
     ws[w0 + S64 + s] = -acc;
   }
 }

@@ -43,6 +43,7 @@ constexpr float kNegInf = -__builtin_inff();
 // O / l is unchanged (all terms of a row share the same stale maximum).
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kMinit = -1.0e30f;  // finite start value of the running max
+constexpr float kEmptyRowLse2 = 1.0e30f;  // lse2 of a row with no allowed key
 constexpr int kDkdvKeys = 128;      // keys per dK/dV workgroup (4 waves x 32)
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {

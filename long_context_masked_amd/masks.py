@@ -20,6 +20,9 @@ Readings of the families (the review names them only):
   PREFIX LM DOCUMENT: the prefix-LM rule inside each document.
   BLOCK CAUSAL DOCUMENT b: same document and blk(j) <= blk(i), blocks counted
     from the document start.
+  TASK BATCH: token-level tasks fused into one launch; task t is a segment of
+    kv_t context tokens whose last q_t are queries, causal inside the segment;
+    its other rows have no keys.
 A block bitmap, when present, is ANDed with the family.
 """
 from __future__ import annotations
@@ -89,6 +92,14 @@ def column_bounds(spec):
         cb[:, 0] = ends[doc]
         cb[:, 1] = S
         cb[:, 3] = bstart
+    elif fam == "task_batch":
+        lens = np.asarray(spec["kv_lens"], dtype=np.int64)
+        ql = np.asarray(spec["q_lens"], dtype=np.int64)
+        ends = np.cumsum(lens)
+        seg = np.searchsorted(ends, j, side="right")
+        cb[:, 0] = ends[seg]                              # rows after the segment
+        cb[:, 1] = S
+        cb[:, 3] = np.maximum(j, ends[seg] - ql[seg])     # earlier rows, non-query rows
     else:
         raise ValueError(f"family {fam!r} has its own descriptor kind")
     return _i32(cb)
@@ -126,7 +137,7 @@ class MaskDescriptor:
             self._set_docs(d, spec["doc_lens"])
             d.prefix_lens = self._ptr32(_i32(spec["prefix_lens"]))
         elif fam in ("shared_question", "global_sliding", "causal_blockwise",
-                     "block_causal_document"):
+                     "block_causal_document", "task_batch"):
             d.kind = L.MASK_COLUMN_BOUNDS
             d.col_bounds = self._ptr32(column_bounds(spec))
         elif fam == "column_bounds":

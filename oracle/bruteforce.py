@@ -81,6 +81,11 @@ def allowed(spec, i, j, hm=0):
         dj, sj = _segment_of(j, spec["doc_lens"])
         b = spec["block"]
         ok = di == dj and (j - sj) // b <= (i - si) // b
+    elif fam == "task_batch":
+        ti, si = _segment_of(i, spec["kv_lens"])
+        tj, _ = _segment_of(j, spec["kv_lens"])
+        end = si + spec["kv_lens"][ti]
+        ok = ti == tj and j <= i and i >= end - spec["q_lens"][ti]
     else:
         raise ValueError(fam)
     if ok and "bitmap" in spec:

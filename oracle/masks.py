@@ -118,6 +118,25 @@ def base_allowed(spec, i0, i1):
         same = doc[i0:i1][:, None] == doc[None, :]
         return same & (blk[None, :] <= blk[i0:i1][:, None])
 
+    if fam == "task_batch":
+        # TASK BATCH: token-level core-attention tasks fused into one launch
+        # ("Efficient Long-context Language Model Training by Core Attention
+        # Disaggregation", abstract: core attention is composable, kernels
+        # keep their efficiency on fused batches of token-level shards of
+        # arbitrary length).  Reading: task t is a segment of kv_t tokens, the
+        # context of a query shard (its document up to the shard's end), whose
+        # last q_t tokens are the shard's queries; a query sees the keys of its
+        # own segment up to itself, and the segment's other rows are not
+        # queries (no keys).
+        lens = spec["kv_lens"]
+        seg = _doc_ids(lens)
+        start = _doc_starts(lens)
+        end = start + np.asarray(lens, dtype=np.int64)
+        ql = np.asarray(spec["q_lens"], dtype=np.int64)
+        si = seg[i0:i1][:, None]
+        same = si == seg[None, :]
+        return same & (j <= i) & (i >= end[si] - ql[si])
+
     raise ValueError(f"unknown mask family {fam!r}")
 
 

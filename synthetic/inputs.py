@@ -26,8 +26,8 @@ __all__ = [
     "spec_full", "spec_causal", "spec_sliding", "spec_document",
     "spec_prefix_lm_causal", "spec_shared_question", "spec_global_sliding",
     "spec_causal_blockwise", "spec_prefix_lm_document",
-    "spec_block_causal_document", "with_bitmap", "spec_seq_len",
-    "sample_doc_lens", "sample_prefix", "sample_answers",
+    "spec_block_causal_document", "spec_task_batch", "with_bitmap", "spec_seq_len",
+    "sample_doc_lens", "sample_prefix", "sample_answers", "sample_tasks",
     "uniform_block_bitmap", "variable_block_bitmap", "variable_partition",
     "config_mask_specs",
 ]
@@ -135,6 +135,31 @@ def spec_block_causal_document(doc_lens, block):
             "doc_lens": doc_lens, "block": int(block)}
 
 
+def spec_task_batch(kv_lens, q_lens):
+    """Fused batch of token-level tasks: segment t has kv_lens[t] tokens of
+    context, the last q_lens[t] of them queries."""
+    kv_lens = [int(x) for x in kv_lens]
+    q_lens = [int(x) for x in q_lens]
+    assert len(kv_lens) == len(q_lens) and all(0 <= q <= k for q, k in zip(q_lens, kv_lens))
+    return {"family": "task_batch", "S": int(sum(kv_lens)), "kv_lens": kv_lens, "q_lens": q_lens}
+
+
+def sample_tasks(S, shard, seed, kv_max=None):
+    """Tasks that fill S tokens: query shards of `shard` tokens, each with a
+    context drawn uniformly from [shard, kv_max] tokens (default 4 * shard:
+    a shard at a random position in the first four shards of its document);
+    the last task is cut to fit."""
+    kv_max = 4 * shard if kv_max is None else int(kv_max)
+    rng = np.random.default_rng(seed)
+    kv, q, left = [], [], int(S)
+    while left > 0:
+        k = min(int(rng.integers(shard, kv_max + 1)), left)
+        kv.append(k)
+        q.append(min(shard, k))
+        left -= k
+    return kv, q
+
+
 def with_bitmap(spec, q_offsets, k_offsets, bits):
     """Attach a block bitmap ``bits[hm][qb][kb]`` (uint8 0/1) to a base spec.
 
@@ -232,6 +257,8 @@ def config_mask_specs(config, S=None, Hq=64, Hkv=8, seed=0):
       CAUSAL BLOCKWISE.
     * ``sparse``: uniform 64 / 128 and variable block bitmaps at 50% density,
       per KV head.
+    * ``tasks``: fused batches of token-level tasks (query shards of 256, 1K
+      or 4K tokens, contexts uniform in [shard, 4 shard]) filling S = 64K.
     * ``variants``: FULL SW w=1024, PREFIX LM DOCUMENT and BLOCK CAUSAL
       DOCUMENT (block 1024) over log-uniform documents in [256, 16K],
       bidirectional GLOBAL SLIDING, block-causal CAUSAL BLOCKWISE.
@@ -257,7 +284,12 @@ def config_mask_specs(config, S=None, Hq=64, Hkv=8, seed=0):
             ("block_causal_document", spec_block_causal_document(docs, 64)),
             ("block64_50", with_bitmap(spec_full(S), *_dup(uniform_block_bitmap(S, 64, Hkv, 0.5, seed)))),
             ("varblock_50", with_bitmap(spec_full(S), *_dup(variable_block_bitmap(S, 32, 224, Hkv, 0.5, seed)))),
+            ("task_batch", spec_task_batch(*sample_tasks(S, 48, seed, kv_max=200))),
         ]
+    if config == "tasks":
+        S = 65536 if S is None else S
+        return [(f"tasks_shard{sh}", spec_task_batch(*sample_tasks(S, sh, seed + i)))
+                for i, sh in enumerate((256, 1024, 4096))]
     if config == "dense":
         return [("full", spec_full(S)), ("causal", spec_causal(S)),
                 ("causal_sw1024", spec_sliding(S, 1024, True))]

@@ -78,6 +78,8 @@ def _ragged_specs(S, Hkv):
         ("causal_blockwise", syn.spec_causal_blockwise(S, 256)),
         ("block64", syn.with_bitmap(syn.spec_full(S), uoffs, uoffs, ubits)),
         ("varblock", syn.with_bitmap(syn.spec_full(S), offs, offs, bits)),
+        # rows with no key inside listed tiles (each task's context rows)
+        ("task_batch", syn.spec_task_batch(*syn.sample_tasks(S, 37, 5, kv_max=150))),
     ]
 
 

@@ -73,6 +73,7 @@ def _tiny_specs(S):
         syn.spec_causal_blockwise(S, 8), syn.spec_causal_blockwise(S, 8, "block_causal"),
         syn.spec_prefix_lm_document(docs, [2, 13, 0, 5]),
         syn.spec_block_causal_document(docs, 4),
+        syn.spec_task_batch(docs, [3, 13, 1, 4]),
     ]
     offs, bits = syn.variable_block_bitmap(S, 3, 9, 2, 0.5, seed=3)
     out.append(syn.with_bitmap(syn.spec_causal(S), offs, offs, bits))
@@ -116,6 +117,9 @@ def test_nnz_closed_forms():
     n = S // b
     assert om.nnz(syn.spec_causal_blockwise(S, b)) == n * b * (b + 1) // 2 + (S - b) * b
     assert om.nnz(syn.spec_causal_blockwise(S, b, "block_causal")) == b * b * n * (n + 1) // 2
+    kv, ql = [300, 5, 450, 245], [300, 1, 17, 100]
+    want = sum(qq * (qq + 1) // 2 + qq * (k - qq) for k, qq in zip(kv, ql))
+    assert om.nnz(syn.spec_task_batch(kv, ql)) == want
     offs, bits = syn.variable_block_bitmap(S, 32, 224, 2, 0.5, seed=2)
     sizes = np.diff(offs)
     for hm in range(2):
