@@ -88,9 +88,14 @@ def workload(name, seqs):
             for Hkv, heads in ((8, "gqa"), (64, "mha")):
                 for label, spec in syn.config_mask_specs("sparse", S, Hq=64, Hkv=Hkv):
                     out.append((f"S{S // 1024}K_{heads}_{label}", S, 64, Hkv, spec))
+        # one bitmap per query head under GQA
+        offs, bits = syn.uniform_block_bitmap(seqs[0], 128, 64, 0.5, 1)
+        out.append((f"S{seqs[0] // 1024}K_gqa_perhead_block128_50", seqs[0], 64, 8,
+                    syn.with_bitmap(syn.spec_full(seqs[0]), offs, offs, bits)))
         desc = ("block-sparse masks: B=1, d=128, S in {" + ", ".join(f"{s // 1024}K" for s in seqs)
                 + "} x {GQA 64:8, MHA 64:64}, bitmap per KV head at 50% density, uniform 64/128 and "
-                  "variable blocks, fwd+bwd")
+                  f"variable blocks; plus a bitmap per query head under GQA (128 blocks, "
+                  f"{seqs[0] // 1024}K), fwd+bwd")
     else:
         raise SystemExit(f"unknown workload {name}")
     return out, desc

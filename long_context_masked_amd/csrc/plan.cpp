@@ -356,8 +356,6 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     const int nh = desc->bitmap_heads;
     if (nh != 1 && nh != sh.Hkv && nh != sh.Hq)
       return fail(ATTN_ERR_INVALID, "bitmap_heads must be 1, Hkv or Hq");
-    if (nh == sh.Hq && nh != sh.Hkv)
-      return fail(ATTN_ERR_UNSUPPORTED, "per-query-head bitmaps need Hq == Hkv");
     if (desc->n_qblk < 1 || desc->n_kblk < 1) return fail(ATTN_ERR_INVALID, "n_qblk, n_kblk must be >= 1");
     attn_status st = check_offsets(desc->q_blk_offsets, desc->n_qblk, S, "q_blk_offsets");
     if (st != ATTN_OK) return st;
@@ -401,64 +399,111 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   const int MC = kBwdKeyTile / kMicro;                     // micro cols per bwd tile
   const int64_t nBK = (S + kBwdKeyTile - 1) / kBwdKeyTile;  // bwd K tiles
   const int n_mask_heads = has_bm ? bm.heads : 1;
+  auto hm_of = [&](int64_t h) -> int {
+    if (!has_bm || bm.heads == 1) return 0;
+    if (bm.heads == sh.Hkv) return (int)(h / G);
+    return (int)h;
+  };
+  // Work lists are built per list group: the mask heads one work item covers.
+  // With one bitmap per query head under GQA, a forward item covers the HG
+  // mask heads of its query heads and a dK/dV item the G heads of its KV
+  // head; a tile is listed if any of them allows a pair in it, and full only
+  // if it is full for all of them (the kernels mask per query head).
+  // Otherwise every item covers a single mask head and a group is that head.
+  const bool per_qhead = has_bm && bm.heads == sh.Hq && G > 1;
+  const int n_fgroups = per_qhead ? (int)(sh.Hq / p->HG) : n_mask_heads;
+  const int n_bgroups = per_qhead ? (int)sh.Hkv : n_mask_heads;
+  auto fgroup_of = [&](int64_t h0) -> int { return per_qhead ? (int)(h0 / p->HG) : hm_of(h0); };
+  auto bgroup_of = [&](int64_t kvh) -> int { return per_qhead ? (int)kvh : hm_of(kvh * G); };
 
   std::vector<uint32_t> fwd_list, bwd_list;
-  std::vector<int64_t> fwd_off((size_t)n_mask_heads * nFQ), bwd_off((size_t)n_mask_heads * nBK);
+  std::vector<int64_t> fwd_off((size_t)n_fgroups * nFQ), bwd_off((size_t)n_bgroups * nBK);
   std::vector<int32_t> fwd_len(fwd_off.size()), bwd_len(bwd_off.size());
   std::vector<int32_t> fwd_npart(fwd_off.size()), bwd_npart(bwd_off.size());
   std::vector<int64_t> nnz_head((size_t)n_mask_heads, nnz_base);
-  std::vector<uint8_t> cls;
-  for (int hm = 0; hm < n_mask_heads; ++hm) {
-    const std::vector<uint8_t> *C = &base;
-    if (has_bm) {
-      classify_bitmap(S, base, bm, hm, cls);
-      C = &cls;
-      nnz_head[hm] = nnz_with_bitmap(S, rowb, bm, hm);
-    }
-    for (int64_t qt = 0; qt < nFQ; ++qt) {
-      const size_t slot = (size_t)hm * nFQ + qt;
-      fwd_off[slot] = (int64_t)fwd_list.size();
-      int32_t npart = 0;
-      const int64_t I0 = qt * MR, I1 = std::min<int64_t>(nM, I0 + MR);
-      for (int64_t J = 0; J < nM; ++J) {
-        bool any = false, all = true;
-        for (int64_t I = I0; I < I1; ++I) {
-          const uint8_t c = (*C)[I * nM + J];
-          any |= c != kEmpty; all &= c == kFull;
+  // Tile class of a union over the mask heads `hs` (classifications in C):
+  // bit 0 = some pair allowed, bit 1 = every pair allowed.
+  auto lists_for = [&](const std::vector<const std::vector<uint8_t> *> &C, int64_t fslot0,
+                       bool do_fwd, int64_t bslot0, bool do_bwd) {
+    if (do_fwd)
+      for (int64_t qt = 0; qt < nFQ; ++qt) {
+        const size_t slot = (size_t)(fslot0 + qt);
+        fwd_off[slot] = (int64_t)fwd_list.size();
+        int32_t npart = 0;
+        const int64_t I0 = qt * MR, I1 = std::min<int64_t>(nM, I0 + MR);
+        for (int64_t J = 0; J < nM; ++J) {
+          bool any = false, all = true;
+          for (const auto *c : C)
+            for (int64_t I = I0; I < I1; ++I) {
+              const uint8_t x = (*c)[I * nM + J];
+              any |= x != kEmpty; all &= x == kFull;
+            }
+          if (!any) continue;
+          const bool ragged = (J + 1) * kFwdKeyTile > S;
+          const bool part = !all || ragged;
+          npart += part;
+          fwd_list.push_back((uint32_t)J | (part ? kPartialBit : 0u));
         }
-        if (!any) continue;
-        const bool ragged = (J + 1) * kFwdKeyTile > S;
-        const bool part = !all || ragged;
-        npart += part;
-        fwd_list.push_back((uint32_t)J | (part ? kPartialBit : 0u));
+        fwd_len[slot] = (int32_t)(fwd_list.size() - fwd_off[slot]);
+        fwd_npart[slot] = npart;
       }
-      fwd_len[slot] = (int32_t)(fwd_list.size() - fwd_off[slot]);
-      fwd_npart[slot] = npart;
-    }
-    for (int64_t kt = 0; kt < nBK; ++kt) {
-      const size_t slot = (size_t)hm * nBK + kt;
-      bwd_off[slot] = (int64_t)bwd_list.size();
-      int32_t npart = 0;
-      const int64_t J0 = kt * MC, J1 = std::min<int64_t>(nM, J0 + MC);
-      for (int64_t I = 0; I < nM; ++I) {
-        bool any = false, all = true;
-        for (int64_t J = J0; J < J1; ++J) {
-          const uint8_t c = (*C)[I * nM + J];
-          any |= c != kEmpty; all &= c == kFull;
+    if (do_bwd)
+      for (int64_t kt = 0; kt < nBK; ++kt) {
+        const size_t slot = (size_t)(bslot0 + kt);
+        bwd_off[slot] = (int64_t)bwd_list.size();
+        int32_t npart = 0;
+        const int64_t J0 = kt * MC, J1 = std::min<int64_t>(nM, J0 + MC);
+        for (int64_t I = 0; I < nM; ++I) {
+          bool any = false, all = true;
+          for (const auto *c : C)
+            for (int64_t J = J0; J < J1; ++J) {
+              const uint8_t x = (*c)[I * nM + J];
+              any |= x != kEmpty; all &= x == kFull;
+            }
+          if (!any) continue;
+          const bool ragged = (I + 1) * kBwdRowTile > S || (J1 - J0) < MC;
+          const bool part = !all || ragged;
+          npart += part;
+          bwd_list.push_back((uint32_t)I | (part ? kPartialBit : 0u));
         }
-        if (!any) continue;
-        const bool ragged = (I + 1) * kBwdRowTile > S || (J1 - J0) < MC;
-        const bool part = !all || ragged;
-        npart += part;
-        bwd_list.push_back((uint32_t)I | (part ? kPartialBit : 0u));
+        // Descending Q-tile order: the items of a K-tile band that run at once
+        // then all start from the last Q-tiles (which every lower-triangular or
+        // banded mask shares) and move down together, so the Q/dO tiles they
+        // stream are fetched once per L2.
+        std::reverse(bwd_list.begin() + bwd_off[slot], bwd_list.end());
+        bwd_len[slot] = (int32_t)(bwd_list.size() - bwd_off[slot]);
+        bwd_npart[slot] = npart;
       }
-      // Descending Q-tile order: the items of a K-tile band that run at once
-      // then all start from the last Q-tiles (which every lower-triangular or
-      // banded mask shares) and move down together, so the Q/dO tiles they
-      // stream are fetched once per L2.
-      std::reverse(bwd_list.begin() + bwd_off[slot], bwd_list.end());
-      bwd_len[slot] = (int32_t)(bwd_list.size() - bwd_off[slot]);
-      bwd_npart[slot] = npart;
+  };
+  if (per_qhead) {
+    // one KV head at a time: its G classifications, its forward groups and
+    // its dK/dV group
+    std::vector<std::vector<uint8_t>> cls((size_t)G);
+    for (int64_t kvh = 0; kvh < sh.Hkv; ++kvh) {
+      for (int g = 0; g < G; ++g) {
+        const int hm = (int)(kvh * G + g);
+        classify_bitmap(S, base, bm, hm, cls[(size_t)g]);
+        nnz_head[(size_t)hm] = nnz_with_bitmap(S, rowb, bm, hm);
+      }
+      for (int g0 = 0; g0 < G; g0 += p->HG) {
+        std::vector<const std::vector<uint8_t> *> C;
+        for (int g = g0; g < g0 + p->HG; ++g) C.push_back(&cls[(size_t)g]);
+        lists_for(C, (int64_t)fgroup_of(kvh * G + g0) * nFQ, true, 0, false);
+      }
+      std::vector<const std::vector<uint8_t> *> C;
+      for (int g = 0; g < G; ++g) C.push_back(&cls[(size_t)g]);
+      lists_for(C, 0, false, (int64_t)bgroup_of(kvh) * nBK, true);
+    }
+  } else {
+    std::vector<uint8_t> cls;
+    for (int hm = 0; hm < n_mask_heads; ++hm) {
+      const std::vector<uint8_t> *C = &base;
+      if (has_bm) {
+        classify_bitmap(S, base, bm, hm, cls);
+        C = &cls;
+        nnz_head[hm] = nnz_with_bitmap(S, rowb, bm, hm);
+      }
+      lists_for({C}, (int64_t)hm * nFQ, true, (int64_t)hm * nBK, true);
     }
   }
   if (fwd_list.size() > 0x7fffffffu || bwd_list.size() > 0x7fffffffu) {
@@ -466,29 +511,23 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     return fail(ATTN_ERR_UNSUPPORTED, "work lists exceed 2^31 entries");
   }
 
-  auto hm_of = [&](int64_t h) -> int {
-    if (!has_bm || bm.heads == 1) return 0;
-    if (bm.heads == sh.Hkv) return (int)(h / G);
-    return (int)h;
-  };
-
   // Step 6: items and longest-first order.  A partial tile costs more than a
   // full one (per-element masking); an item also pays a fixed epilogue.
   const double kPartCost = 1.25, kItemCost = 0.75;
   std::vector<Item> fi, bi;
   for (int64_t h0 = 0; h0 < sh.Hq; h0 += p->HG) {
-    const int hm = hm_of(h0);
+    const int fg = fgroup_of(h0);
     for (int64_t qt = 0; qt < nFQ; ++qt) {
-      const size_t slot = (size_t)hm * nFQ + qt;
+      const size_t slot = (size_t)fg * nFQ + qt;
       const int32_t len = fwd_len[slot], np = fwd_npart[slot];
       fi.push_back({(int32_t)qt, (int32_t)h0, (int32_t)fwd_off[slot], len,
                     (len - np) + kPartCost * np + kItemCost});
     }
   }
   for (int64_t kvh = 0; kvh < sh.Hkv; ++kvh) {
-    const int hm = hm_of(kvh * G);
+    const int bg = bgroup_of(kvh);
     for (int64_t kt = 0; kt < nBK; ++kt) {
-      const size_t slot = (size_t)hm * nBK + kt;
+      const size_t slot = (size_t)bg * nBK + kt;
       const int32_t len = bwd_len[slot], np = bwd_npart[slot];
       bi.push_back({(int32_t)kt, (int32_t)kvh, (int32_t)bwd_off[slot], len,
                     G * ((len - np) + kPartCost * np) + kItemCost});
@@ -596,9 +635,9 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     *it++ = x.tile; *it++ = x.head; *it++ = x.off; *it++ = x.len;
   }
   for (int64_t h0 = 0; h0 < sh.Hq; h0 += p->HG) {
-    const int hm = hm_of(h0);
+    const int fg = fgroup_of(h0);
     for (int64_t qt = 0; qt < nFQ; ++qt) {
-      const size_t slot = (size_t)hm * nFQ + qt;
+      const size_t slot = (size_t)fg * nFQ + qt;
       fpart += fwd_npart[slot]; ffull += fwd_len[slot] - fwd_npart[slot];
     }
   }
@@ -612,9 +651,9 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   for (const auto &r : reduce)
     for (int t = 0; t < 4; ++t) *it++ = r[t];
   for (int64_t kvh = 0; kvh < sh.Hkv; ++kvh) {
-    const int hm = hm_of(kvh * G);
+    const int bg = bgroup_of(kvh);
     for (int64_t kt = 0; kt < nBK; ++kt) {
-      const size_t slot = (size_t)hm * nBK + kt;
+      const size_t slot = (size_t)bg * nBK + kt;
       bpart += bwd_npart[slot]; bfull += bwd_len[slot] - bwd_npart[slot];
     }
   }

@@ -72,6 +72,9 @@ def _cases():
         out.append(("sparse32K_mha_" + label, spec, 64))
     for label, spec in syn.config_mask_specs("sparse", 131072, Hq=HQ, Hkv=8):
         out.append(("sparse128K_" + label, spec, 8))
+    # one bitmap per query head under GQA (work lists are unions over heads)
+    offs, bits = syn.uniform_block_bitmap(32768, 128, HQ, 0.5, 1)
+    out.append(("sparse32K_perhead_block128_50", syn.with_bitmap(syn.spec_full(32768), offs, offs, bits), 8))
     # one 128K MHA mask: its plan alone lists about 10^8 tiles per direction
     offs, bits = syn.uniform_block_bitmap(131072, 128, 64, 0.5, 0)
     out.append(("sparse128K_mha_block128_50", syn.with_bitmap(syn.spec_full(131072), offs, offs, bits), 64))

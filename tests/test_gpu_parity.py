@@ -101,6 +101,18 @@ def test_d128_mha_ragged(label, spec):
     run_case(spec, 1, 2, 2, 128, seed=6)
 
 
+@pytest.mark.parametrize("S,Hq,Hkv,d,kind", [(512, 4, 2, 64, "uniform64"), (700, 8, 2, 128, "variable"),
+                                               (333, 6, 2, 128, "uniform64")])
+def test_per_query_head_bitmaps_under_gqa(S, Hq, Hkv, d, kind):
+    """One bitmap per query head with query heads sharing KV heads: the work
+    lists are unions over the heads of an item, masking is per head."""
+    if kind == "uniform64":
+        offs, bits = syn.uniform_block_bitmap(S, 64, Hq, 0.5, seed=11)
+    else:
+        offs, bits = syn.variable_block_bitmap(S, 32, 224, Hq, 0.5, seed=12)
+    run_case(syn.with_bitmap(syn.spec_causal(S), offs, offs, bits), 1, Hq, Hkv, d, seed=13)
+
+
 def test_d64_mha_odd_group_and_short():
     """Hq=3 over Hkv=1 (odd group), S=65 and S=1."""
     run_case(syn.spec_causal(65), 1, 3, 1, 64, seed=7)

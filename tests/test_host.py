@@ -113,16 +113,19 @@ def _check_lists(p, spec, Hq, Hkv):
         tiles = (ents & 0x7FFFFFFF).astype(int)
         assert len(set(tiles.tolist())) == len(tiles)
         r0, r1 = qt * FR, min(S, qt * FR + FR)
+        # an item's list serves all its heads: a listed tile has an allowed
+        # pair for some head, and a FULL tile is fully allowed for every head
+        for t, e in zip(tiles, ents):
+            c0, c1 = t * FC, min(S, t * FC + FC)
+            blks = [dm(h)[r0:r1, c0:c1] for h in range(h0, h0 + HG)]
+            assert any(b.any() for b in blks), "empty tile listed"
+            if not (e >> 31):
+                assert all(b.all() for b in blks) and c1 - c0 == FC, "FULL tile not fully allowed"
         for h in range(h0, h0 + HG):
             a = dm(h)[r0:r1]
             cover = np.zeros(S, dtype=bool)
-            for t, e in zip(tiles, ents):
-                c0, c1 = t * FC, min(S, t * FC + FC)
-                blk = a[:, c0:c1]
-                assert blk.any(), "empty tile listed"
-                if not (e >> 31):
-                    assert blk.all() and c1 - c0 == FC, "FULL tile not fully allowed"
-                cover[c0:c1] = True
+            for t in tiles:
+                cover[t * FC:min(S, t * FC + FC)] = True
             assert not a[:, ~cover].any(), "allowed pair outside the listed tiles"
     assert len(seen) == (Hq // HG) * ((S + FR - 1) // FR)
 
@@ -180,6 +183,9 @@ def test_work_lists_ragged_and_head_groupings(Hq, Hkv):
     specs = _family_specs(S, 3)[:12]
     offs, bits = syn.variable_block_bitmap(S, 20, 90, Hkv, 0.5, seed=5)
     specs.append(syn.with_bitmap(syn.spec_causal(S), offs, offs, bits))
+    # one bitmap per query head (under GQA the lists are unions over heads)
+    offs, bits = syn.variable_block_bitmap(S, 20, 90, Hq, 0.5, seed=6)
+    specs.append(syn.with_bitmap(syn.spec_full(S), offs, offs, bits))
     for spec in specs:
         _check_lists(lcm.Plan(1, S, Hq, Hkv, 128, spec), spec, Hq, Hkv)
 
@@ -332,7 +338,7 @@ def test_plan_create_errors():
     assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
     offs, bits = syn.uniform_block_bitmap(S, 64, 4, 0.5, 0)
     d = lcm.MaskDescriptor(syn.with_bitmap(syn.spec_full(S), offs, offs, bits))
-    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_UNSUPPORTED
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_OK   # one bitmap per query head, GQA
     assert _create((1, S, 4, 4, 64, 0.0), d.c) == L.ATTN_OK
     bad_offs = np.array([0, 64, 64, 192, 256], dtype=np.int32)
     d.c.q_blk_offsets = bad_offs.ctypes.data_as(L.P32)
