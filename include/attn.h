@@ -79,8 +79,11 @@ typedef enum {
  * bitmap[hm][qblk(i)][kblk(j)], where qblk(i) is the b with
  * q_blk_offsets[b] <= i < q_blk_offsets[b+1] (likewise kblk) and hm is the
  * bitmap head of query head h: 0 if bitmap_heads == 1, h / (Hq / Hkv) if
- * bitmap_heads == Hkv, h if bitmap_heads == Hq (the last only when
- * Hq == Hkv).
+ * bitmap_heads == Hkv, h if bitmap_heads == Hq.
+ * With dynamic = 1 the plan keeps room for every work list at its largest
+ * and the bitmap can be replaced on the device, without a new plan, by
+ * attn_plan_set_bitmap (content-adaptive block masks, whose bitmap changes
+ * from step to step).
  */
 typedef enum {
   ATTN_MASK_FULL = 0,
@@ -110,6 +113,9 @@ typedef struct {
   int32_t bitmap_heads, n_qblk, n_kblk;
   const int32_t *q_blk_offsets;  /* [n_qblk+1], 0 = o_0 < ... < o_n = S        */
   const int32_t *k_blk_offsets;  /* [n_kblk+1], likewise                       */
+  int32_t dynamic;               /* 0, or 1 (needs block_bitmap): the bitmap
+                                    may later be replaced by
+                                    attn_plan_set_bitmap                         */
 } attn_mask_desc;
 
 typedef struct attn_plan attn_plan;
@@ -148,6 +154,35 @@ size_t attn_plan_device_bytes(const attn_plan *plan);
  */
 attn_status attn_plan_bind(attn_plan *plan, void *dev_buf, size_t bytes,
                            attn_stream_t stream);
+
+/*
+ * Replace the block bitmap of a dynamic plan on the device and rebuild its
+ * work lists there, for the dynamic block-sparse masks of the
+ * "Long-Context Attention Benchmark" review (xllm-io), "paper summary",
+ * innovation 3: the blocks are chosen from the input, so the bitmap changes
+ * every step and the lists cannot wait for a host compile.
+ *
+ *   bits  device memory, uint8 [bitmap_heads][n_qblk][n_kblk] in the block
+ *         partition the plan was created with; nonzero = block allowed.
+ *         16-byte aligned, must not overlap the plan's device buffer; read
+ *         by work enqueued on `stream` only (the caller keeps it alive and
+ *         unchanged until that work has run).
+ *
+ * Enqueues two kernels on `stream`: the first copies the bitmap into the
+ * plan's buffer and rebuilds every forward / dQ and dK/dV list, the second
+ * stores each work item's new length.  The lists equal, entry for entry,
+ * those attn_plan_create would build for the new bitmap; the order of the
+ * work items stays the one chosen at creation, and no dK/dV item is split.
+ * Later attn_fwd / attn_bwd calls on `stream` see the new mask; calls on
+ * other streams must be ordered after it by the caller.  attn_plan_stats
+ * and attn_plan_get_layout keep describing the creation bitmap, and binding
+ * the plan again uploads that bitmap and its lists.
+ *
+ * Errors: ATTN_ERR_INVALID for a NULL or unbound plan, a plan created
+ * without dynamic = 1, a NULL, misaligned or overlapping `bits`;
+ * ATTN_ERR_DEVICE if a launch fails.  Nothing is enqueued on an error.
+ */
+attn_status attn_plan_set_bitmap(attn_plan *plan, const uint8_t *bits, attn_stream_t stream);
 
 attn_status attn_plan_stats(const attn_plan *plan, attn_stats *out);
 

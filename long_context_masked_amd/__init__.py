@@ -46,6 +46,7 @@ class Plan:
         self.stats = {name: getattr(st, name) for name, _ in L.Stats._fields_}
         self._dev = None
         self._dev_index = None
+        self._dev_off = 0
 
     @property
     def handle(self):
@@ -70,14 +71,47 @@ class Plan:
         stream = torch.cuda.current_stream(dev).cuda_stream
         L.check(L.lib().attn_plan_bind(self._h, C.c_void_p(ptr + off), C.c_size_t(n),
                                        C.c_void_p(stream)))
-        self._dev, self._dev_index = buf, idx
+        self._dev, self._dev_index, self._dev_off = buf, idx, off
+        return self
+
+    def set_bitmap(self, bits):
+        """Replace the block bitmap of a dynamic plan (created with
+        ``"dynamic": True`` in its mask spec) by ``bits``, a uint8 or bool GPU
+        tensor [bitmap_heads, n_qblk, n_kblk], and rebuild the work lists on
+        the GPU, on the current stream."""
+        import torch
+        d = self.desc.c
+        shape = (int(d.bitmap_heads), int(d.n_qblk), int(d.n_kblk))
+        if bits.dtype not in (torch.uint8, torch.bool) or not bits.is_cuda:
+            raise TypeError("bits must be a uint8 or bool GPU tensor")
+        if tuple(bits.shape) != shape or not bits.is_contiguous():
+            raise ValueError(f"bits must be contiguous with shape {shape}")
+        self.bind(bits.device)
+        stream = torch.cuda.current_stream(bits.device).cuda_stream
+        L.check(L.lib().attn_plan_set_bitmap(self._h, C.c_void_p(bits.data_ptr()),
+                                             C.c_void_p(stream)))
         return self
 
     def layout(self):
-        """Host copy of the device blob's sections as numpy arrays."""
+        """Host copy of the blob's sections as numpy arrays (as created)."""
         lay = L.Layout()
         L.check(L.lib().attn_plan_get_layout(self._h, C.byref(lay)))
         raw = np.ctypeslib.as_array((C.c_uint8 * lay.blob_bytes).from_address(lay.blob)).copy()
+        return self._sections(lay, raw)
+
+    def device_layout(self):
+        """The same sections read back from the bound device buffer (after
+        set_bitmap they hold the rebuilt lists)."""
+        import torch
+        if self._dev is None:
+            raise RuntimeError("plan is not bound")
+        lay = L.Layout()
+        L.check(L.lib().attn_plan_get_layout(self._h, C.byref(lay)))
+        torch.cuda.current_stream(self._dev.device).synchronize()
+        raw = self._dev[self._dev_off:self._dev_off + lay.blob_bytes].cpu().numpy()
+        return self._sections(lay, raw)
+
+    def _sections(self, lay, raw):
         S = self.shape[1]
 
         def i32(off, n):

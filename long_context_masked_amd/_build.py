@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
-HIP_SOURCES = ["api.hip", "fwd.hip", "bwd.hip"]
+HIP_SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "dyn.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -31,7 +31,8 @@ class MaskDesc(C.Structure):
                 ("window_right", C.c_int32), ("num_docs", C.c_int32),
                 ("cu_seqlens", P32), ("prefix_lens", P32), ("col_bounds", P32),
                 ("block_bitmap", PU8), ("bitmap_heads", C.c_int32), ("n_qblk", C.c_int32),
-                ("n_kblk", C.c_int32), ("q_blk_offsets", P32), ("k_blk_offsets", P32)]
+                ("n_kblk", C.c_int32), ("q_blk_offsets", P32), ("k_blk_offsets", P32),
+                ("dynamic", C.c_int32)]
 
 
 class Stats(C.Structure):
@@ -63,6 +64,7 @@ SIGNATURES = {
     "attn_plan_create": (C.c_int, [C.POINTER(Shape), C.POINTER(MaskDesc), C.POINTER(C.c_void_p)]),
     "attn_plan_device_bytes": (C.c_size_t, [C.c_void_p]),
     "attn_plan_bind": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "attn_plan_set_bitmap": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
     "attn_plan_stats": (C.c_int, [C.c_void_p, C.POINTER(Stats)]),
     "attn_plan_get_layout": (C.c_int, [C.c_void_p, C.POINTER(Layout)]),
     "attn_bwd_workspace_bytes": (C.c_size_t, [C.c_void_p]),

@@ -14,6 +14,7 @@ hipError_t launch_dq(const BwdArgs &a, int d, int HG, int B, hipStream_t st);
 hipError_t launch_merge(const float *o1, const float *lse1, const float *o2, const float *lse2,
                         void *o, bool o_bf16, float *lse, int64_t B, int S, int Hq, int d,
                         hipStream_t st);
+hipError_t launch_dyn(const DynArgs &a, hipStream_t st);
 }  // namespace lcm
 
 using namespace lcm;
@@ -82,6 +83,54 @@ extern "C" attn_status attn_plan_bind(attn_plan *plan, void *dev_buf, size_t byt
   if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "plan upload failed: %s", hipGetErrorString(e));
   plan->dev_blob = dev_buf;
   plan->dev_bytes = bytes;
+  return ATTN_OK;
+}
+
+extern "C" attn_status attn_plan_set_bitmap(attn_plan *plan, const uint8_t *bits,
+                                            attn_stream_t stream) {
+  clear_error();
+  if (plan && !plan->dyn.on) return fail(ATTN_ERR_INVALID, "plan was not created with dynamic = 1");
+  attn_status st0 = check_plan(plan);
+  if (st0 != ATTN_OK) return st0;
+  st0 = check_tensor(bits, "bits", 16);
+  if (st0 != ATTN_OK) return st0;
+  const int64_t nbits = (int64_t)plan->bitmap_heads * plan->nqb * plan->nkb;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(bits);
+  const uintptr_t p0 = reinterpret_cast<uintptr_t>(plan->dev_blob);
+  if (b0 < p0 + (uintptr_t)plan->lay.total && p0 < b0 + (uintptr_t)nbits)
+    return fail(ATTN_ERR_INVALID, "bits overlaps the plan's device buffer");
+  if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
+  const DynInfo &D = plan->dyn;
+  const Layout &L = plan->lay;
+  uint8_t *blob = static_cast<uint8_t *>(plan->dev_blob);
+  DynArgs a{};
+  a.src = bits;
+  a.bits = blob + L.bits;
+  a.nbits = nbits;
+  a.base = blob + L.dyn_base;
+  a.qblk = reinterpret_cast<const int *>(blob + L.qblk);
+  a.kblk = reinterpret_cast<const int *>(blob + L.kblk);
+  a.fwd_list = reinterpret_cast<uint32_t *>(blob + L.fwd_list);
+  a.bwd_list = reinterpret_cast<uint32_t *>(blob + L.bwd_list);
+  a.slot_len = reinterpret_cast<int *>(blob + L.dyn_len);
+  a.fitems = reinterpret_cast<int *>(blob + L.fwd_items);
+  a.bitems = reinterpret_cast<int *>(blob + L.bwd_items);
+  a.n_fitems = (int)L.n_fwd_items;
+  a.n_bitems = (int)L.n_bwd_items;
+  a.S = (int)plan->shape.S;
+  a.nM = (int)D.nM;
+  a.MR = D.MR;
+  a.MC = D.MC;
+  a.nqb = plan->nqb;
+  a.nkb = plan->nkb;
+  a.nFQ = (int)D.nFQ;
+  a.nBK = (int)D.nBK;
+  a.n_fslots = (int)D.n_fslots;
+  a.n_bslots = (int)D.n_bslots;
+  a.fheads = D.fheads;
+  a.bheads = D.bheads;
+  const hipError_t e = launch_dyn(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "list rebuild launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;
 }
 

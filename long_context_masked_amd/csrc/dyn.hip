@@ -1,0 +1,169 @@
+// Device side of dynamic block-sparse masks: rebuild a plan's work lists
+// from a new block bitmap without going back to the host.
+//
+// Method: "Long-Context Attention Benchmark" review (xllm-io), paper summary,
+// innovation 3 (block-sparse masks whose blocks are chosen from the input,
+// so the bitmap changes every step) and section 3 "mask taxonomy" (uniform
+// and variable block masks).  The mask is the plan's base mask AND the
+// bitmap.  A 64x64 micro tile of mask head h is empty if its base class is
+// empty or no bitmap block it touches is on, full if its base class is full
+// and every block it touches is on, and partial otherwise.  A kernel tile is
+// listed when some micro tile in it is non-empty for some mask head of the
+// list's group, and marked partial unless all of them are full and the tile
+// is whole.  These are the host compiler's rules on the same inputs (the
+// base classes it stored in the plan), so the lists come out identical.
+//
+// One wave builds one list.  Lane l classifies tile c + l of a run of 64; a
+// ballot compacts the listed tiles in order; the wave moves to the next 64.
+// Forward / dQ lists run over key tiles J ascending, dK/dV lists over
+// Q-tiles I descending (the order the host gives them).  A second launch
+// copies each list's new length into the work items that read it.
+#include <algorithm>
+
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace lcm {
+
+namespace {
+
+// Class of micro tile (I, J) for mask head h; the tile's key columns touch
+// bitmap column blocks [klo, khi].
+__device__ __forceinline__ int micro_class(const DynArgs &a, int h, int I, int J, int klo,
+                                           int khi) {
+  const uint8_t b = a.base[(int64_t)I * a.nM + J];
+  if (b == kEmpty) return kEmpty;
+  const int r1 = min(a.S, I * kMicro + kMicro);
+  const int qlo = a.qblk[I * kMicro], qhi = a.qblk[r1 - 1];
+  const uint8_t *bm = a.src + (int64_t)h * a.nqb * a.nkb;
+  bool any = false, all = true;
+  for (int qb = qlo; qb <= qhi; ++qb)
+    for (int kb = klo; kb <= khi; ++kb) {
+      const bool on = bm[(int64_t)qb * a.nkb + kb] != 0;
+      any |= on;
+      all &= on;
+    }
+  return !any ? kEmpty : (all && b == kFull ? kFull : kPartial);
+}
+
+__device__ __forceinline__ int key_block_lo(const DynArgs &a, int J) { return a.kblk[J * kMicro]; }
+__device__ __forceinline__ int key_block_hi(const DynArgs &a, int J) {
+  return a.kblk[min(a.S, J * kMicro + kMicro) - 1];
+}
+
+// Lanes below this one whose bit is set in m.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// 0/1 per byte of w: 1 where the byte is nonzero.
+__device__ __forceinline__ uint32_t bytes_nonzero(uint32_t w) {
+  return ((((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w) & 0x80808080u) >> 7;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void attn_dyn_lists_kernel(DynArgs a) {
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < a.copy_blocks) {
+    const int64_t n16 = a.nbits / 16, stride = (int64_t)a.copy_blocks * 256;
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(a.src);
+    uint4 *d4 = reinterpret_cast<uint4 *>(a.bits);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < n16; i += stride) {
+      uint4 v = s4[i];
+      v.x = bytes_nonzero(v.x); v.y = bytes_nonzero(v.y);
+      v.z = bytes_nonzero(v.z); v.w = bytes_nonzero(v.w);
+      d4[i] = v;
+    }
+    for (int64_t i = n16 * 16 + (int64_t)blockIdx.x * 256 + tid; i < a.nbits; i += stride)
+      a.bits[i] = a.src[i] != 0 ? 1 : 0;
+    return;
+  }
+  const int w = ((int)blockIdx.x - a.copy_blocks) * 4 + tid / 64;
+  const int lane = tid & 63;
+  const int nM = a.nM;
+  if (w < a.n_fslots) {
+    // forward / dQ list of (group g, Q-tile qt): key tiles J ascending
+    const int g = w / a.nFQ, qt = w - g * a.nFQ;
+    const int I0 = qt * a.MR, I1 = min(nM, I0 + a.MR);
+    uint32_t *out = a.fwd_list + (int64_t)w * nM;
+    int cnt = 0;
+    for (int c = 0; c < nM; c += 64) {
+      const int J = c + lane;
+      bool any = false, all = true;
+      if (J < nM) {
+        const int klo = key_block_lo(a, J), khi = key_block_hi(a, J);
+        for (int hh = 0; hh < a.fheads; ++hh)
+          for (int I = I0; I < I1; ++I) {
+            const int x = micro_class(a, g * a.fheads + hh, I, J, klo, khi);
+            any |= x != kEmpty;
+            all &= x == kFull;
+          }
+      }
+      const uint64_t m = __ballot(any);
+      if (any) {
+        const bool part = !all || (J + 1) * kFwdKeyTile > a.S;
+        out[cnt + lanes_below(m)] = (uint32_t)J | (part ? kPartialBit : 0u);
+      }
+      cnt += __popcll(m);
+    }
+    if (lane == 0) a.slot_len[w] = cnt;
+  } else if (w < a.n_fslots + a.n_bslots) {
+    // dK/dV list of (group g, K-tile kt): Q-tiles I descending
+    const int wb = w - a.n_fslots;
+    const int g = wb / a.nBK, kt = wb - g * a.nBK;
+    const int J0 = kt * a.MC, J1 = min(nM, J0 + a.MC);
+    uint32_t *out = a.bwd_list + (int64_t)wb * nM;
+    int cnt = 0;
+    for (int c = 0; c < nM; c += 64) {
+      const int I = nM - 1 - (c + lane);
+      bool any = false, all = true;
+      if (I >= 0) {
+        for (int hh = 0; hh < a.bheads; ++hh)
+          for (int J = J0; J < J1; ++J) {
+            const int x = micro_class(a, g * a.bheads + hh, I, J, key_block_lo(a, J),
+                                      key_block_hi(a, J));
+            any |= x != kEmpty;
+            all &= x == kFull;
+          }
+      }
+      const uint64_t m = __ballot(any);
+      if (any) {
+        const bool part = !all || (I + 1) * kBwdRowTile > a.S || (J1 - J0) < a.MC;
+        out[cnt + lanes_below(m)] = (uint32_t)I | (part ? kPartialBit : 0u);
+      }
+      cnt += __popcll(m);
+    }
+    if (lane == 0) a.slot_len[w] = cnt;
+  }
+}
+
+// Every work item reads the list at its offset; offsets are slot * nM.
+__global__ __launch_bounds__(256) void attn_dyn_items_kernel(DynArgs a) {
+  const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (i < a.n_fitems) {
+    int *it = a.fitems + 4 * (int64_t)i;
+    it[3] = a.slot_len[it[2] / a.nM];
+  } else if (i < a.n_fitems + a.n_bitems) {
+    int *it = a.bitems + 4 * (int64_t)(i - a.n_fitems);
+    it[3] = a.slot_len[a.n_fslots + it[2] / a.nM];
+  }
+}
+
+hipError_t launch_dyn(const DynArgs &a0, hipStream_t st) {
+  DynArgs a = a0;
+  const int64_t n16 = a.nbits / 16;
+  a.copy_blocks = (int)std::max<int64_t>(1, std::min<int64_t>(256, (n16 + 255) / 256));
+  const int64_t waves = (int64_t)a.n_fslots + a.n_bslots;
+  const int64_t blocks = a.copy_blocks + (waves + 3) / 4;
+  hipLaunchKernelGGL(attn_dyn_lists_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)a.n_fitems + a.n_bitems;
+  if (n > 0)
+    hipLaunchKernelGGL(attn_dyn_items_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace lcm

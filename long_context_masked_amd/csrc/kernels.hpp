@@ -357,6 +357,22 @@ struct BwdArgs {
   MaskArgs m;
 };
 
+// Rebuild of a dynamic plan's work lists from a new bitmap (dyn.hip).
+struct DynArgs {
+  const uint8_t *src;      // new bitmap [heads][nqb][nkb], nonzero = on
+  uint8_t *bits;           // the plan's copy of it, 0/1
+  int64_t nbits;
+  const uint8_t *base;     // base-mask micro-tile classes [nM][nM]
+  const int *qblk, *kblk;  // bitmap block of each position [S]
+  uint32_t *fwd_list, *bwd_list;
+  int *slot_len;           // [n_fslots + n_bslots]
+  int *fitems, *bitems;    // int32 [n][4]: tile, head, list offset, length
+  int n_fitems, n_bitems;
+  int S, nM, MR, MC, nqb, nkb, nFQ, nBK;
+  int n_fslots, n_bslots, fheads, bheads;
+  int copy_blocks;
+};
+
 // Allowed-key bits of query row `row` over keys [t0, t0 + 64).
 __device__ __forceinline__ uint64_t row_mask(const MaskArgs &m, int4 rb, int qb, int hm,
                                              int t0, int S) {

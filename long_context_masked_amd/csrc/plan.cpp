@@ -50,8 +50,6 @@ void clear_error() { g_err.clear(); }
 
 namespace {
 
-enum : uint8_t { kEmpty = 0, kPartial = 1, kFull = 2 };
-
 struct Run { int32_t a0, b0, a1, b1; };
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
@@ -352,6 +350,9 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   // bitmap
   Bitmap bm;
   const bool has_bm = desc->block_bitmap != nullptr;
+  if (desc->dynamic != 0 && desc->dynamic != 1) return fail(ATTN_ERR_INVALID, "dynamic must be 0 or 1");
+  const bool dynamic = desc->dynamic == 1;
+  if (dynamic && !has_bm) return fail(ATTN_ERR_INVALID, "dynamic = 1 needs a block_bitmap");
   if (has_bm) {
     const int nh = desc->bitmap_heads;
     if (nh != 1 && nh != sh.Hkv && nh != sh.Hq)
@@ -506,6 +507,34 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
       lists_for({C}, (int64_t)hm * nFQ, true, (int64_t)hm * nBK, true);
     }
   }
+  if (dynamic) {
+    // Every list gets room for all nM tiles of its row or column, at
+    // slot * nM, so that the device can rebuild any list in place.
+    const int64_t nfs = (int64_t)n_fgroups * nFQ, nbs = (int64_t)n_bgroups * nBK;
+    if (nfs * nM > 0x7fffffff || nbs * nM > 0x7fffffff) {
+      delete p;
+      return fail(ATTN_ERR_UNSUPPORTED, "dynamic work lists would exceed 2^31 entries");
+    }
+    auto widen = [&](std::vector<uint32_t> &list, std::vector<int64_t> &offs,
+                     const std::vector<int32_t> &lens) {
+      std::vector<uint32_t> w((size_t)(offs.size() * nM), 0u);
+      for (size_t sl = 0; sl < offs.size(); ++sl) {
+        std::copy(list.begin() + offs[sl], list.begin() + offs[sl] + lens[sl],
+                  w.begin() + (int64_t)sl * nM);
+        offs[sl] = (int64_t)sl * nM;
+      }
+      list.swap(w);
+    };
+    widen(fwd_list, fwd_off, fwd_len);
+    widen(bwd_list, bwd_off, bwd_len);
+    DynInfo &D = p->dyn;
+    D.on = true;
+    D.nM = nM; D.nFQ = nFQ; D.nBK = nBK;
+    D.n_fslots = nfs; D.n_bslots = nbs;
+    D.MR = MR; D.MC = MC;
+    D.fheads = per_qhead ? p->HG : 1;
+    D.bheads = per_qhead ? G : 1;
+  }
   if (fwd_list.size() > 0x7fffffffu || bwd_list.size() > 0x7fffffffu) {
     delete p;
     return fail(ATTN_ERR_UNSUPPORTED, "work lists exceed 2^31 entries");
@@ -542,7 +571,8 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   // of consecutive listed Q-tiles (all query heads of the group), so that no
   // single workgroup outlasts the rest (small S, or key columns that every
   // row sees).  A chunk is an item of its own over a slice of the item's
-  // list, and gets a partial-result slot; slots follow list order.
+  // list, and gets a partial-result slot; slots follow list order.  Items of
+  // a dynamic plan are never split: their lists change after creation.
   std::vector<int32_t> slot_of;
   std::vector<std::array<int32_t, 4>> reduce;
   {
@@ -554,7 +584,7 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     int32_t slots = 0;
     for (const Item &x : bi) {
       int32_t n = 1;
-      if (x.cost * (double)sh.B > share && x.len > 1)
+      if (!dynamic && x.cost * (double)sh.B > share && x.len > 1)
         n = (int32_t)std::min<double>({(double)kSplitMax, (double)x.len,
                                        std::ceil(x.cost * (double)sh.B / share)});
       if (n <= 1) {
@@ -619,6 +649,10 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     L.qoffs = sect((int64_t)(bm.nqb + 1) * 4);
     L.koffs = sect((int64_t)(bm.nkb + 1) * 4);
   }
+  if (dynamic) {
+    L.dyn_base = sect(nM * nM);
+    L.dyn_len = sect((p->dyn.n_fslots + p->dyn.n_bslots) * 4);
+  }
   L.total = off;
   try {
     p->blob.assign((size_t)L.total, 0);
@@ -664,6 +698,12 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     std::memcpy(blob + L.kblk, bm.kblk.data(), (size_t)S * 4);
     std::memcpy(blob + L.qoffs, bm.qoffs.data(), bm.qoffs.size() * 4);
     std::memcpy(blob + L.koffs, bm.koffs.data(), bm.koffs.size() * 4);
+  }
+  if (dynamic) {
+    std::memcpy(blob + L.dyn_base, base.data(), base.size());
+    int32_t *ln = reinterpret_cast<int32_t *>(blob + L.dyn_len);
+    for (int32_t x : fwd_len) *ln++ = x;
+    for (int32_t x : bwd_len) *ln++ = x;
   }
 
   int64_t nnz_b = 0;

@@ -19,6 +19,8 @@ constexpr int kBwdRowTile = 64;   // dK/dV: query rows per Q-tile
 constexpr int kWgRowsHeads = 128; // forward / dQ: (rows x heads) per workgroup
 
 constexpr uint32_t kPartialBit = 0x80000000u;
+// Class of a 64x64 micro tile (stored as uint8 in a dynamic plan's blob).
+enum : uint8_t { kEmpty = 0, kPartial = 1, kFull = 2 };
 
 // Byte offsets of the sections of the device blob (all 256-byte aligned).
 struct Layout {
@@ -28,7 +30,20 @@ struct Layout {
   int64_t bits = -1, qblk = -1, kblk = -1, qoffs = -1, koffs = -1;
   int64_t n_fwd_items = 0, n_fwd_list = 0, n_bwd_items = 0, n_bwd_list = 0;
   int64_t n_bwd_reduce = 0, n_slots = 0;
+  int64_t dyn_base = -1, dyn_len = -1;  // dynamic plans only
   int64_t total = 0;
+};
+
+// What the device list builder of a dynamic plan needs.  List group g of
+// the forward covers mask heads [g * fheads, (g + 1) * fheads) and owns the
+// forward lists of slots [g * nFQ, (g + 1) * nFQ), one per Q-tile; likewise
+// the dK/dV groups with bheads and nBK.  Every list has room for nM entries
+// at list + slot * nM.
+struct DynInfo {
+  bool on = false;
+  int64_t nM = 0, nFQ = 0, nBK = 0;
+  int64_t n_fslots = 0, n_bslots = 0;
+  int MR = 1, MC = 2, fheads = 1, bheads = 1;
 };
 
 // dK/dV items whose work exceeds the share of one workgroup are split into
@@ -51,6 +66,7 @@ struct attn_plan {
   int nqb = 0, nkb = 0;
   std::vector<uint8_t> blob;  // host copy of the device blob
   lcm::Layout lay;
+  lcm::DynInfo dyn;
   attn_stats stats{};
   void *dev_blob = nullptr;
   size_t dev_bytes = 0;

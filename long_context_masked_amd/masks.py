@@ -154,6 +154,7 @@ class MaskDescriptor:
             d.bitmap_heads, d.n_qblk, d.n_kblk = (int(x) for x in bits.shape)
             d.q_blk_offsets = self._ptr32(_i32(bm["q_offsets"]))
             d.k_blk_offsets = self._ptr32(_i32(bm["k_offsets"]))
+        d.dynamic = 1 if spec.get("dynamic") else 0
         self.c = d
 
     def _ptr32(self, arr):

@@ -28,7 +28,7 @@ __all__ = [
     "spec_causal_blockwise", "spec_prefix_lm_document",
     "spec_block_causal_document", "spec_task_batch", "with_bitmap", "spec_seq_len",
     "sample_doc_lens", "sample_prefix", "sample_answers", "sample_tasks",
-    "uniform_block_bitmap", "variable_block_bitmap", "variable_partition",
+    "uniform_block_bitmap", "variable_block_bitmap", "variable_partition", "partition_bitmap",
     "config_mask_specs",
 ]
 
@@ -234,6 +234,12 @@ def variable_partition(S, lo, hi, seed):
     while offs[-1] < S:
         offs.append(min(S, offs[-1] + int(rng.integers(lo, hi + 1))))
     return offs
+
+
+def partition_bitmap(q_offsets, k_offsets, heads, density=0.5, seed=0, diag_on=True):
+    """Bernoulli(density) bits over given row and column block partitions
+    (which may differ), blocks (b, b) forced on when ``diag_on``."""
+    return _bernoulli_bits(heads, len(q_offsets) - 1, len(k_offsets) - 1, density, seed, diag_on)
 
 
 def variable_block_bitmap(S, lo, hi, heads, density=0.5, seed=0):

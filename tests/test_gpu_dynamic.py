@@ -1,0 +1,199 @@
+"""GPU tests of dynamic block-sparse plans: attn_plan_set_bitmap rebuilds the
+work lists on the device.
+
+* The rebuilt lists equal, entry for entry, the lists the host compiler
+  builds for the same bitmap (and the host compiler's lists are checked
+  against the oracle's dense mask in test_host.py).
+* After an update, the forward and backward agree with the fp64 oracle for
+  the new mask (the gate of gpu_util; the backward runs on the oracle's bf16
+  O and LSE, so that both sides form D = rowsum(dO * O) from the same O), and
+  O, LSE and dQ equal bit for bit what the ordinary plan for that bitmap
+  gives (same lists, same per-item arithmetic; dK/dV may differ in rounding
+  where the ordinary plan splits an item).
+* Several updates in a row, an all-zero bitmap, and byte values other than
+  0/1 (any nonzero byte turns a block on).
+"""
+import numpy as np
+import pytest
+
+import synthetic as syn
+from oracle import attention as ora
+
+from gpu_util import gate, to_dev, to_f64, f64
+from plan_util import lists_by_item
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import long_context_masked_amd as lcm  # noqa: E402
+
+
+def _cases():
+    out = []
+    S = 700
+    o = syn.uniform_block_bitmap(S, 64, 1, seed=0)[0]
+    out.append(("uniform64_causal_gqa", syn.spec_causal(S), o, o, 8, 2, 128, 2))
+    S = 1000
+    qo = syn.variable_partition(S, 20, 150, seed=2)
+    ko = syn.variable_partition(S, 40, 200, seed=3)
+    out.append(("distinct_qk_partitions", syn.spec_full(S), qo, ko, 4, 2, 64, 1))
+    S = 512
+    o = syn.uniform_block_bitmap(S, 128, 1, seed=0)[0]
+    out.append(("per_query_head_gqa", syn.spec_causal(S), o, o, 8, 2, 64, 8))
+    S = 333
+    o = syn.uniform_block_bitmap(S, 32, 1, seed=0)[0]
+    out.append(("mha_ragged", syn.spec_full(S), o, o, 2, 2, 128, 2))
+    S = 900
+    o = syn.variable_partition(S, 30, 130, seed=9)
+    docs = syn.sample_doc_lens(S, 64, 400, 4)
+    out.append(("causal_document_base", syn.spec_document(docs, True), o, o, 4, 1, 64, 1))
+    return out
+
+
+CASES = _cases()
+
+
+def _bits(qo, ko, heads, density, seed, diag_on=True):
+    return syn.partition_bitmap(qo, ko, heads, density, seed, diag_on)
+
+
+def _dev_bits(bits, scale=1):
+    return torch.from_numpy(np.ascontiguousarray(bits * scale, dtype=np.uint8)).cuda()
+
+
+def _check_lists_equal(dyn, spec_new, B, Hq, Hkv, d, bits_new):
+    ref = lcm.Plan(B, spec_new["S"], Hq, Hkv, d, spec_new)
+    fs, bs = lists_by_item(ref.layout())
+    dl = dyn.device_layout()
+    fd, bd = lists_by_item(dl)
+    assert fd == fs, "forward / dQ lists differ from the host compiler's"
+    assert bd == bs, "dK/dV lists differ from the host compiler's"
+    return ref
+
+
+def _check_bits_section(dyn, bits_new):
+    lay = L_layout(dyn)
+    raw = dyn._dev[dyn._dev_off:dyn._dev_off + lay.blob_bytes].cpu().numpy()
+    got = raw[lay.off_bits:lay.off_bits + bits_new.size]
+    assert (got == (bits_new.ravel() != 0)).all()
+
+
+def L_layout(plan):
+    import ctypes as C
+    from long_context_masked_amd import _lib as L
+    lay = L.Layout()
+    L.check(L.lib().attn_plan_get_layout(plan.handle, C.byref(lay)))
+    return lay
+
+
+def _oracle_check(plan, spec, B, Hq, Hkv, d, seed, x=None):
+    """Forward against the oracle's O and LSE; backward run on the oracle's
+    bf16 O and fp32 LSE (so that D = rowsum(dO * O) is formed from the same
+    O on both sides) against the oracle's gradients."""
+    S = spec["S"]
+    x = syn.attention_inputs(B, S, Hq, Hkv, d, seed) if x is None else x
+    q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
+    qf, kf, vf, dof = (f64(x[n]) for n in ("q", "k", "v", "do"))
+    ref = ora.backward(qf, kf, vf, dof, spec, o_for_d="bf16", magnitudes=True)
+    o, lse = lcm.fwd(plan, q, k, v)
+    torch.cuda.synchronize()
+    gate("O", to_f64(o), ref["o"], ref["m_o"])
+    lg = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref["lse"])
+    assert (np.isneginf(lg) == ~fin).all()
+    if fin.any():
+        assert np.abs(lg[fin] - ref["lse"][fin]).max() <= 5e-3
+    o_r = torch.from_numpy(ora.round_bf16(ref["o"]).astype(np.float32)).to(torch.bfloat16).cuda()
+    lse_r = torch.from_numpy(ref["lse"].astype(np.float32)).cuda()
+    dq, dk, dv = lcm.bwd(plan, q, k, v, o_r, lse_r, do)
+    torch.cuda.synchronize()
+    gate("dQ", to_f64(dq), ref["dq"], ref["m_dq"])
+    gate("dK", to_f64(dk), ref["dk"], ref["m_dk"])
+    gate("dV", to_f64(dv), ref["dv"], ref["m_dv"])
+    return (q, k, v, do), (o, lse, o_r, lse_r, dq)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_set_bitmap_rebuilds_host_lists_and_matches_oracle(case):
+    label, base, qo, ko, Hq, Hkv, d, heads = case
+    B = 1
+    print(f"dynamic case {label}", flush=True)
+    b1 = _bits(qo, ko, heads, 0.5, seed=1)
+    b2 = _bits(qo, ko, heads, 0.3, seed=2)
+    dyn = lcm.Plan(B, base["S"], Hq, Hkv, d, dict(syn.with_bitmap(base, qo, ko, b1), dynamic=True))
+    dyn.bind()
+    spec2 = syn.with_bitmap(base, qo, ko, b2)
+    dyn.set_bitmap(_dev_bits(b2, scale=5))          # any nonzero byte is "on"
+    static2 = _check_lists_equal(dyn, spec2, B, Hq, Hkv, d, b2)
+    _check_bits_section(dyn, b2)
+    (q, k, v, do), (o, lse, o_r, lse_r, dq) = _oracle_check(dyn, spec2, B, Hq, Hkv, d, seed=3)
+    # same lists and per-item arithmetic as the ordinary plan for b2, also
+    # with the backward chained on the forward's own O and LSE
+    o2, lse2 = lcm.fwd(static2, q, k, v)
+    dq2, _, _ = lcm.bwd(static2, q, k, v, o_r, lse_r, do)
+    dq3, _, _ = lcm.bwd(dyn, q, k, v, o, lse, do)
+    dq4, _, _ = lcm.bwd(static2, q, k, v, o2, lse2, do)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(dq, dq2)
+    assert torch.equal(dq3, dq4)
+
+
+@pytest.mark.parametrize("case", CASES[:3], ids=[c[0] for c in CASES[:3]])
+def test_repeated_updates(case):
+    """b1 -> b2 -> b3 (no diagonal: rows and columns without keys) -> b1."""
+    label, base, qo, ko, Hq, Hkv, d, heads = case
+    B = 2
+    b1 = _bits(qo, ko, heads, 0.5, seed=11)
+    b2 = _bits(qo, ko, heads, 0.8, seed=12)
+    b3 = _bits(qo, ko, heads, 0.2, seed=13, diag_on=False)
+    dyn = lcm.Plan(B, base["S"], Hq, Hkv, d, dict(syn.with_bitmap(base, qo, ko, b1), dynamic=True))
+    dyn.bind()
+    x = syn.attention_inputs(B, base["S"], Hq, Hkv, d, 21)
+    for step, b in enumerate((b2, b3, b1)):
+        print(f"dynamic case {label} update {step}", flush=True)
+        spec = syn.with_bitmap(base, qo, ko, b)
+        dyn.set_bitmap(_dev_bits(b))
+        _check_lists_equal(dyn, spec, B, Hq, Hkv, d, b)
+        _oracle_check(dyn, spec, B, Hq, Hkv, d, seed=0, x=x)
+
+
+def test_all_zero_bitmap_then_back():
+    """Every list empty: O = 0, LSE = -inf, zero gradients; then a bitmap
+    with blocks on again."""
+    label, base, qo, ko, Hq, Hkv, d, heads = CASES[0]
+    S, B = base["S"], 1
+    b1 = _bits(qo, ko, heads, 0.5, seed=31)
+    dyn = lcm.Plan(B, S, Hq, Hkv, d, dict(syn.with_bitmap(base, qo, ko, b1), dynamic=True))
+    dyn.bind()
+    dyn.set_bitmap(torch.zeros(b1.shape, dtype=torch.bool, device="cuda"))
+    dl = dyn.device_layout()
+    assert (dl["fwd_items"][:, 3] == 0).all() and (dl["bwd_items"][:, 3] == 0).all()
+    x = syn.attention_inputs(B, S, Hq, Hkv, d, 32)
+    q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
+    o, lse = lcm.fwd(dyn, q, k, v)
+    dq, dk, dv = lcm.bwd(dyn, q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    assert (o == 0).all() and torch.isneginf(lse).all()
+    assert (dq == 0).all() and (dk == 0).all() and (dv == 0).all()
+    dyn.set_bitmap(_dev_bits(b1))
+    _check_lists_equal(dyn, syn.with_bitmap(base, qo, ko, b1), B, Hq, Hkv, d, b1)
+    _oracle_check(dyn, syn.with_bitmap(base, qo, ko, b1), B, Hq, Hkv, d, seed=33, x=x)
+
+
+def test_set_bitmap_argument_errors():
+    label, base, qo, ko, Hq, Hkv, d, heads = CASES[0]
+    b1 = _bits(qo, ko, heads, 0.5, seed=41)
+    dyn = lcm.Plan(1, base["S"], Hq, Hkv, d, dict(syn.with_bitmap(base, qo, ko, b1), dynamic=True))
+    dyn.bind()
+    with pytest.raises(ValueError):
+        dyn.set_bitmap(torch.zeros((heads + 1,) + b1.shape[1:], dtype=torch.uint8, device="cuda"))
+    import ctypes as C
+    from long_context_masked_amd import _lib as L
+    t = torch.zeros(b1.size + 16, dtype=torch.uint8, device="cuda")
+    assert L.lib().attn_plan_set_bitmap(dyn.handle, C.c_void_p(t.data_ptr() + 1), None) == L.ATTN_ERR_INVALID
+    inside = dyn._dev.data_ptr() + dyn._dev_off   # the plan's own buffer
+    assert L.lib().attn_plan_set_bitmap(dyn.handle, C.c_void_p(inside), None) == L.ATTN_ERR_INVALID
+    assert b"overlaps" in L.lib().attn_last_error()

@@ -9,6 +9,7 @@ import pytest
 
 import synthetic as syn
 from oracle import masks as om
+from plan_util import lists_by_item
 
 lcm = pytest.importorskip("long_context_masked_amd")
 from long_context_masked_amd import _lib as L  # noqa: E402
@@ -410,3 +411,59 @@ def test_scale_default_and_stats_fields():
     assert st["bwd_tile_cols"] == 128 and st["bwd_tile_rows"] == 64
     assert st["device_bytes"] == p.device_bytes()
     assert p.workspace_bytes() >= 3 * 8 * S * 4
+
+
+def _dynamic_cases():
+    S = 333
+    uo, ub = syn.uniform_block_bitmap(S, 64, 2, 0.5, seed=1)
+    qo = syn.variable_partition(S, 20, 150, seed=2)
+    ko = syn.variable_partition(S, 40, 200, seed=3)
+    vb = syn.partition_bitmap(qo, ko, 1, 0.5, seed=4)
+    po, pb = syn.uniform_block_bitmap(S, 32, 8, 0.4, seed=5)
+    return [
+        ("uniform64_gqa", syn.with_bitmap(syn.spec_causal(S), uo, uo, ub), 4, 2),
+        ("distinct_qk_partitions", syn.with_bitmap(syn.spec_full(S), qo, ko, vb), 4, 2),
+        ("per_query_head_gqa", syn.with_bitmap(syn.spec_causal(S), po, po, pb), 8, 2),
+        ("per_query_head_odd_group", syn.with_bitmap(syn.spec_full(S), po[:], po, pb[:3]), 3, 1),
+    ]
+
+
+@pytest.mark.parametrize("label,spec,Hq,Hkv", _dynamic_cases(), ids=[c[0] for c in _dynamic_cases()])
+def test_dynamic_plan_lists_equal_static(label, spec, Hq, Hkv):
+    """A dynamic plan lists the same tiles, entry for entry, as the ordinary
+    plan for its creation bitmap; each list sits at slot * nM (room for every
+    tile of its row or column) and no dK/dV item is split."""
+    S = spec["S"]
+    static = lcm.Plan(1, S, Hq, Hkv, 64, spec)
+    dyn = lcm.Plan(1, S, Hq, Hkv, 64, dict(spec, dynamic=True))
+    ls, ld = static.layout(), dyn.layout()
+    fs, bs = lists_by_item(ls)
+    fd, bd = lists_by_item(ld)
+    assert fs == fd and bs == bd
+    nM = (S + 63) // 64
+    assert (ld["fwd_items"][:, 2] % nM == 0).all() and (ld["bwd_items"][:, 2] % nM == 0).all()
+    assert len(set(ld["fwd_items"][:, 2].tolist())) <= ld["fwd_list"].size // nM
+    assert (ld["bwd_slot"] == -1).all() and ld["n_slots"] == 0 and len(ld["bwd_reduce"]) == 0
+    assert dyn.stats["nnz_total"] == static.stats["nnz_total"]
+    _check_lists(dyn, spec, Hq, Hkv)
+
+
+def test_dynamic_plan_errors():
+    S = 256
+    lib = L.lib()
+    d = lcm.MaskDescriptor(dict(syn.spec_causal(S), dynamic=True))
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_INVALID   # no bitmap
+    assert b"block_bitmap" in lib.attn_last_error()
+    offs, bits = syn.uniform_block_bitmap(S, 64, 2, 0.5, 0)
+    spec = syn.with_bitmap(syn.spec_causal(S), offs, offs, bits)
+    d = lcm.MaskDescriptor(spec)
+    d.c.dynamic = 2
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
+    a = C.c_void_p(4096)  # never dereferenced: validation fails first
+    static = lcm.Plan(1, S, 4, 2, 64, spec)
+    assert lib.attn_plan_set_bitmap(static.handle, a, None) == L.ATTN_ERR_INVALID
+    assert b"dynamic" in lib.attn_last_error()
+    dyn = lcm.Plan(1, S, 4, 2, 64, dict(spec, dynamic=True))
+    assert lib.attn_plan_set_bitmap(dyn.handle, a, None) == L.ATTN_ERR_INVALID
+    assert b"not bound" in lib.attn_last_error()
+    assert lib.attn_plan_set_bitmap(None, a, None) == L.ATTN_ERR_INVALID
