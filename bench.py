@@ -163,6 +163,63 @@ def merge_rate(lcm, torch, dev, S=16384, Hq=64, d=128, reps=20):
             "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def dynamic_rebuild(lcm, torch, dev, tensors_for, reps=20, steps=3):
+    """Dynamic block-sparse plans: time of one attn_plan_set_bitmap (the
+    device list rebuild, HIP events on the launch stream) against the host
+    compile of an ordinary plan for the same bitmap, and the fwd+bwd time on
+    the rebuilt lists against the ordinary plan's (the dynamic plan keeps
+    its creation-time item order and does not split dK/dV items)."""
+    import numpy as np
+    import synthetic as syn
+    d, out = 128, {}
+    cases = [("S32K_gqa_block64_50", 32768, 8, 64, 8), ("S32K_gqa_perhead_block128_50", 32768, 8, 128, 64),
+             ("S128K_gqa_block128_50", 131072, 8, 128, 8)]
+    stream = torch.cuda.current_stream(dev)
+    for label, S, Hkv, blk, heads in cases:
+        offs, b1 = syn.uniform_block_bitmap(S, blk, heads, 0.5, seed=1)
+        _, b2 = syn.uniform_block_bitmap(S, blk, heads, 0.5, seed=2)
+        base = syn.spec_full(S)
+        t0 = time.perf_counter()
+        static = lcm.Plan(1, S, 64, Hkv, d, syn.with_bitmap(base, offs, offs, b2))
+        host_s = time.perf_counter() - t0
+        dyn = lcm.Plan(1, S, 64, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b1), dynamic=True))
+        dyn.bind(dev)
+        static.bind(dev)
+        g1 = torch.from_numpy(b1).to(dev)
+        g2 = torch.from_numpy(b2).to(dev)
+        dyn.set_bitmap(g2)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            dyn.set_bitmap(g1 if i % 2 == 0 else g2)   # ends on b2
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rebuild_ms = e0.elapsed_time(e1) / reps
+        tt = tensors_for(S, Hkv)
+        ms = {}
+        for name, plan in (("dynamic", dyn), ("static", static)):
+            o, lse = lcm.fwd(plan, tt["q"], tt["k"], tt["v"], out=tt["o"], lse=tt["lse"])
+            lcm.bwd(plan, tt["q"], tt["k"], tt["v"], o, lse, tt["do"], grads=(tt["dq"], tt["dk"], tt["dv"]))
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(steps):
+                o, lse = lcm.fwd(plan, tt["q"], tt["k"], tt["v"], out=tt["o"], lse=tt["lse"])
+                lcm.bwd(plan, tt["q"], tt["k"], tt["v"], o, lse, tt["do"], grads=(tt["dq"], tt["dk"], tt["dv"]))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms[name] = e0.elapsed_time(e1) / steps
+        nnz = static.stats["nnz_total"]
+        out[label] = {"rebuild_us": round(rebuild_ms * 1e3, 1), "host_plan_ms": round(host_s * 1e3, 1),
+                      "fwd_bwd_ms_dynamic": round(ms["dynamic"], 3), "fwd_bwd_ms_static": round(ms["static"], 3),
+                      "tflops_dynamic": round(14.0 * d * nnz / (ms["dynamic"] * 1e-3) / 1e12, 1),
+                      "tflops_static": round(14.0 * d * nnz / (ms["static"] * 1e-3) / 1e12, 1),
+                      "plan_device_MB": round(dyn.device_bytes() / 1e6, 1)}
+        log(f"dynamic {label}: {out[label]}")
+        del dyn, static, g1, g2
+    return out
+
+
 def sources_sha256():
     h = hashlib.sha256()
     for rel in TRAFFIC_SOURCES:
@@ -232,6 +289,8 @@ def main():
                     help="comma-separated sequence lengths (dense: default 1024,8192,16384,49152; "
                          "sparse: default 32768,131072; ignored by document and hetero)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dynamic", action="store_true",
+                    help="sparse workload: skip the dynamic block-sparse (device list rebuild) figures")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size before warmup (counter scale)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -405,6 +464,18 @@ def main():
     }
     log("merge of partial results")
     out["merge"] = merge_rate(lcm, torch, dev)
+    if args.workload == "sparse" and not args.no_dynamic:
+        log("dynamic block-sparse: device list rebuild")
+
+        def tensors_for(S, Hkv):
+            if (S, Hkv) not in tensors:
+                x = syn.attention_inputs(1, S, 64, Hkv, d, seed=0)
+                q, k, v, do = t(x["q"]), t(x["k"]), t(x["v"]), t(x["do"])
+                tensors[(S, Hkv)] = dict(q=q, k=k, v=v, do=do, o=torch.empty_like(q),
+                                         lse=torch.empty((1, 64, S), dtype=torch.float32, device=dev),
+                                         dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
+            return tensors[(S, Hkv)]
+        out["dynamic"] = dynamic_rebuild(lcm, torch, dev, tensors_for)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline()

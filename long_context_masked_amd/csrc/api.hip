@@ -112,11 +112,17 @@ extern "C" attn_status attn_plan_set_bitmap(attn_plan *plan, const uint8_t *bits
   a.kblk = reinterpret_cast<const int *>(blob + L.kblk);
   a.fwd_list = reinterpret_cast<uint32_t *>(blob + L.fwd_list);
   a.bwd_list = reinterpret_cast<uint32_t *>(blob + L.bwd_list);
-  a.slot_len = reinterpret_cast<int *>(blob + L.dyn_len);
-  a.fitems = reinterpret_cast<int *>(blob + L.fwd_items);
-  a.bitems = reinterpret_cast<int *>(blob + L.bwd_items);
-  a.n_fitems = (int)L.n_fwd_items;
-  a.n_bitems = (int)L.n_bwd_items;
+  a.slot_len = reinterpret_cast<int2 *>(blob + L.dyn_len);
+  a.fitems = reinterpret_cast<int4 *>(blob + L.fwd_items);
+  a.bitems = reinterpret_cast<int4 *>(blob + L.bwd_items);
+  a.fshare = reinterpret_cast<const int *>(blob + L.dyn_fshare);
+  a.bshare = reinterpret_cast<const int *>(blob + L.dyn_bshare);
+  a.fpos = reinterpret_cast<const int *>(blob + L.dyn_fpos);
+  a.bpos = reinterpret_cast<const int *>(blob + L.dyn_bpos);
+  a.fnat = reinterpret_cast<const int4 *>(blob + L.dyn_fnat);
+  a.bnat = reinterpret_cast<const int4 *>(blob + L.dyn_bnat);
+  a.n_fshares = D.n_fshares;
+  a.n_bshares = D.n_bshares;
   a.S = (int)plan->shape.S;
   a.nM = (int)D.nM;
   a.MR = D.MR;

@@ -16,8 +16,17 @@
 // One wave builds one list.  Lane l classifies tile c + l of a run of 64; a
 // ballot compacts the listed tiles in order; the wave moves to the next 64.
 // Forward / dQ lists run over key tiles J ascending, dK/dV lists over
-// Q-tiles I descending (the order the host gives them).  A second launch
-// copies each list's new length into the work items that read it.
+// Q-tiles I descending (the order the host gives them).
+//
+// A second launch puts the work items back in longest-first order, the
+// order that keeps the tail of a launch short.  The item array is dealt to
+// XCD shares at creation (each XCD's workgroups serve a fixed set of heads,
+// so that its L2 holds their tiles); one workgroup re-sorts the items of one
+// share by their new cost, 4 x tiles + partial tiles (a partial tile costs
+// 1.25 full ones), ties in natural order, with a bitonic sort in LDS, and
+// writes them, with their new lengths, into the share's positions.  That is
+// the host compiler's order whenever its deal does not depend on the costs
+// (Hkv a multiple of 8, or no deal at all).
 #include <algorithm>
 
 #include "kernels.hpp"
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(256) void attn_dyn_lists_kernel(DynArgs a) {
     const int g = w / a.nFQ, qt = w - g * a.nFQ;
     const int I0 = qt * a.MR, I1 = min(nM, I0 + a.MR);
     uint32_t *out = a.fwd_list + (int64_t)w * nM;
-    int cnt = 0;
+    int cnt = 0, npart = 0;
     for (int c = 0; c < nM; c += 64) {
       const int J = c + lane;
       bool any = false, all = true;
@@ -101,21 +110,20 @@ __global__ __launch_bounds__(256) void attn_dyn_lists_kernel(DynArgs a) {
             all &= x == kFull;
           }
       }
+      const bool part = !all || (J + 1) * kFwdKeyTile > a.S;
       const uint64_t m = __ballot(any);
-      if (any) {
-        const bool part = !all || (J + 1) * kFwdKeyTile > a.S;
-        out[cnt + lanes_below(m)] = (uint32_t)J | (part ? kPartialBit : 0u);
-      }
+      if (any) out[cnt + lanes_below(m)] = (uint32_t)J | (part ? kPartialBit : 0u);
       cnt += __popcll(m);
+      npart += __popcll(__ballot(any && part));
     }
-    if (lane == 0) a.slot_len[w] = cnt;
+    if (lane == 0) a.slot_len[w] = make_int2(cnt, npart);
   } else if (w < a.n_fslots + a.n_bslots) {
     // dK/dV list of (group g, K-tile kt): Q-tiles I descending
     const int wb = w - a.n_fslots;
     const int g = wb / a.nBK, kt = wb - g * a.nBK;
     const int J0 = kt * a.MC, J1 = min(nM, J0 + a.MC);
     uint32_t *out = a.bwd_list + (int64_t)wb * nM;
-    int cnt = 0;
+    int cnt = 0, npart = 0;
     for (int c = 0; c < nM; c += 64) {
       const int I = nM - 1 - (c + lane);
       bool any = false, all = true;
@@ -128,26 +136,71 @@ __global__ __launch_bounds__(256) void attn_dyn_lists_kernel(DynArgs a) {
             all &= x == kFull;
           }
       }
+      const bool part = !all || (I + 1) * kBwdRowTile > a.S || (J1 - J0) < a.MC;
       const uint64_t m = __ballot(any);
-      if (any) {
-        const bool part = !all || (I + 1) * kBwdRowTile > a.S || (J1 - J0) < a.MC;
-        out[cnt + lanes_below(m)] = (uint32_t)I | (part ? kPartialBit : 0u);
-      }
+      if (any) out[cnt + lanes_below(m)] = (uint32_t)I | (part ? kPartialBit : 0u);
       cnt += __popcll(m);
+      npart += __popcll(__ballot(any && part));
     }
-    if (lane == 0) a.slot_len[w] = cnt;
+    if (lane == 0) a.slot_len[w] = make_int2(cnt, npart);
   }
 }
 
-// Every work item reads the list at its offset; offsets are slot * nM.
-__global__ __launch_bounds__(256) void attn_dyn_items_kernel(DynArgs a) {
-  const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
-  if (i < a.n_fitems) {
-    int *it = a.fitems + 4 * (int64_t)i;
-    it[3] = a.slot_len[it[2] / a.nM];
-  } else if (i < a.n_fitems + a.n_bitems) {
-    int *it = a.bitems + 4 * (int64_t)(i - a.n_fitems);
-    it[3] = a.slot_len[a.n_fslots + it[2] / a.nM];
+// One workgroup per XCD share of either pass.  A share larger than
+// kSortCap items keeps its items in natural order (lengths updated).
+constexpr int kSortCap = 8192;
+constexpr int kSortThreads = 1024;
+
+__global__ __launch_bounds__(kSortThreads) void attn_dyn_sort_kernel(DynArgs a) {
+  __shared__ uint64_t key[kSortCap];
+  const int tid = threadIdx.x;
+  const bool fwd = (int)blockIdx.x < a.n_fshares;
+  const int c = fwd ? (int)blockIdx.x : (int)blockIdx.x - a.n_fshares;
+  const int *off = fwd ? a.fshare : a.bshare;
+  const int m0 = off[c], m = off[c + 1] - m0;
+  const int *pos = (fwd ? a.fpos : a.bpos) + m0;
+  const int4 *nat = (fwd ? a.fnat : a.bnat) + m0;
+  int4 *items = fwd ? a.fitems : a.bitems;
+  const int2 *len = a.slot_len + (fwd ? 0 : a.n_fslots);
+  if (m > kSortCap) {
+    for (int i = tid; i < m; i += kSortThreads) {
+      int4 it = nat[i];
+      it.w = len[it.z / a.nM].x;
+      items[pos[i]] = it;
+    }
+    return;
+  }
+  int n = 1;
+  while (n < m) n <<= 1;
+  // ascending order of (0xffffffff - cost) << 32 | natural index
+  for (int i = tid; i < n; i += kSortThreads) {
+    uint64_t k = ~0ull;
+    if (i < m) {
+      const int2 ln = len[nat[i].z / a.nM];
+      const uint32_t cost = 4u * (uint32_t)ln.x + (uint32_t)ln.y;
+      k = ((uint64_t)(0xffffffffu - cost) << 32) | (uint32_t)i;
+    }
+    key[i] = k;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n; i += kSortThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = key[i], y = key[ixj];
+          if ((x > y) == ((i & k) == 0)) {
+            key[i] = y;
+            key[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = tid; i < m; i += kSortThreads) {
+    int4 it = nat[(uint32_t)key[i]];
+    it.w = len[it.z / a.nM].x;
+    items[pos[i]] = it;
   }
 }
 
@@ -160,9 +213,8 @@ hipError_t launch_dyn(const DynArgs &a0, hipStream_t st) {
   hipLaunchKernelGGL(attn_dyn_lists_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)a.n_fitems + a.n_bitems;
-  if (n > 0)
-    hipLaunchKernelGGL(attn_dyn_items_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(attn_dyn_sort_kernel, dim3((unsigned)(a.n_fshares + a.n_bshares)),
+                     dim3(kSortThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -365,9 +365,13 @@ struct DynArgs {
   const uint8_t *base;     // base-mask micro-tile classes [nM][nM]
   const int *qblk, *kblk;  // bitmap block of each position [S]
   uint32_t *fwd_list, *bwd_list;
-  int *slot_len;           // [n_fslots + n_bslots]
-  int *fitems, *bitems;    // int32 [n][4]: tile, head, list offset, length
-  int n_fitems, n_bitems;
+  int2 *slot_len;          // [n_fslots + n_bslots]: entries, partial entries
+  int4 *fitems, *bitems;   // tile, head, list offset, length
+  // XCD shares of each pass: share c owns item positions pos[off[c] ..
+  // off[c+1]) and the items nat[off[c] ..) (natural order)
+  const int *fshare, *bshare, *fpos, *bpos;
+  const int4 *fnat, *bnat;
+  int n_fshares, n_bshares;
   int S, nM, MR, MC, nqb, nkb, nFQ, nBK;
   int n_fslots, n_bslots, fheads, bheads;
   int copy_blocks;

@@ -296,12 +296,18 @@ struct Item { int32_t tile, head, off, len; double cost; };
 // XCD x takes the heads h with h % 8 == x; when Hkv divides 8, each head's
 // items go to the least-loaded of the XCDs congruent to it modulo Hkv (the
 // longest-processing-time rule within that set).  Otherwise the order is
-// left as it is.  Each XCD's share stays in longest-first order.
+// left as it is.  Each XCD's share stays in longest-first order.  If `cls`
+// is given it receives the XCD share (0 when the order is left) of every
+// position of the result.
 constexpr int kXcds = 8;
-void xcd_interleave(std::vector<Item> &v, int64_t Hkv, int64_t heads_per_kv) {
+void xcd_interleave(std::vector<Item> &v, int64_t Hkv, int64_t heads_per_kv,
+                    std::vector<int32_t> *cls = nullptr) {
   const bool by_mod = Hkv % kXcds == 0;
   const bool spread = kXcds % Hkv == 0;
-  if (!by_mod && !spread) return;
+  if (!by_mod && !spread) {
+    if (cls) cls->assign(v.size(), 0);
+    return;
+  }
   std::vector<std::vector<Item>> q(kXcds);
   std::vector<double> load(kXcds, 0.0);
   for (const Item &x : v) {
@@ -315,11 +321,43 @@ void xcd_interleave(std::vector<Item> &v, int64_t Hkv, int64_t heads_per_kv) {
     load[(size_t)slot] += x.cost;
   }
   v.clear();
+  if (cls) cls->clear();
   for (size_t i = 0;; ++i) {
     bool any = false;
     for (int x = 0; x < kXcds; ++x)
-      if (i < q[x].size()) { v.push_back(q[x][i]); any = true; }
+      if (i < q[x].size()) {
+        v.push_back(q[x][i]);
+        if (cls) cls->push_back(x);
+        any = true;
+      }
     if (!any) break;
+  }
+}
+
+// The reorder tables of one pass of a dynamic plan: for each XCD share c,
+// its item positions (ascending) at pos[off[c] .. off[c+1]) and its items in
+// natural order at nat[off[c] ..).  The device sorts each share's items by
+// their new cost and writes them back into the share's positions.
+void share_tables(const std::vector<Item> &v, const std::vector<int32_t> &cls,
+                  const std::vector<int64_t> &natural, std::vector<int32_t> &off,
+                  std::vector<int32_t> &pos, std::vector<std::array<int32_t, 4>> &nat) {
+  int32_t nc = 1;
+  for (int32_t c : cls) nc = std::max(nc, c + 1);
+  off.assign((size_t)nc + 1, 0);
+  for (int32_t c : cls) off[(size_t)c + 1]++;
+  for (int32_t c = 0; c < nc; ++c) off[(size_t)c + 1] += off[(size_t)c];
+  std::vector<int32_t> fill(off.begin(), off.end() - 1);
+  pos.assign(v.size(), 0);
+  for (size_t p = 0; p < v.size(); ++p) pos[(size_t)fill[(size_t)cls[p]]++] = (int32_t)p;
+  nat.assign(v.size(), {0, 0, 0, 0});
+  for (int32_t c = 0; c < nc; ++c) {
+    std::vector<int32_t> mem(pos.begin() + off[(size_t)c], pos.begin() + off[(size_t)c + 1]);
+    std::stable_sort(mem.begin(), mem.end(),
+                     [&](int32_t a, int32_t b) { return natural[(size_t)a] < natural[(size_t)b]; });
+    for (size_t i = 0; i < mem.size(); ++i) {
+      const Item &x = v[(size_t)mem[i]];
+      nat[(size_t)off[(size_t)c] + i] = {x.tile, x.head, x.off, x.len};
+    }
   }
 }
 
@@ -575,6 +613,7 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   // a dynamic plan are never split: their lists change after creation.
   std::vector<int32_t> slot_of;
   std::vector<std::array<int32_t, 4>> reduce;
+  std::vector<int32_t> fcls, bcls;  // XCD share of each item position
   {
     double total = 0.0;
     for (const Item &x : bi) total += x.cost;
@@ -615,8 +654,8 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
       bi.push_back(y);
     }
     p->n_slots = slots;
-    xcd_interleave(fi, sh.Hkv, G);  // forward items carry their first query head
-    xcd_interleave(bi, sh.Hkv, 1);  // dK/dV items carry their KV head
+    xcd_interleave(fi, sh.Hkv, G, &fcls);  // forward items carry their first query head
+    xcd_interleave(bi, sh.Hkv, 1, &bcls);  // dK/dV items carry their KV head
     for (Item &y : bi) {
       const size_t i = (size_t)y.off;
       y.off = split[i].off;
@@ -649,9 +688,25 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     L.qoffs = sect((int64_t)(bm.nqb + 1) * 4);
     L.koffs = sect((int64_t)(bm.nkb + 1) * 4);
   }
+  std::vector<int32_t> fsh_off, fsh_pos, bsh_off, bsh_pos;
+  std::vector<std::array<int32_t, 4>> fsh_nat, bsh_nat;
   if (dynamic) {
+    // natural order: forward (query-head group, Q-tile), dK/dV (KV head, K-tile)
+    std::vector<int64_t> fn(fi.size()), bn(bi.size());
+    for (size_t i = 0; i < fi.size(); ++i) fn[i] = (int64_t)(fi[i].head / p->HG) * nFQ + fi[i].tile;
+    for (size_t i = 0; i < bi.size(); ++i) bn[i] = (int64_t)bi[i].head * nBK + bi[i].tile;
+    share_tables(fi, fcls, fn, fsh_off, fsh_pos, fsh_nat);
+    share_tables(bi, bcls, bn, bsh_off, bsh_pos, bsh_nat);
+    p->dyn.n_fshares = (int)fsh_off.size() - 1;
+    p->dyn.n_bshares = (int)bsh_off.size() - 1;
     L.dyn_base = sect(nM * nM);
-    L.dyn_len = sect((p->dyn.n_fslots + p->dyn.n_bslots) * 4);
+    L.dyn_len = sect((p->dyn.n_fslots + p->dyn.n_bslots) * 8);
+    L.dyn_fshare = sect((int64_t)fsh_off.size() * 4);
+    L.dyn_fpos = sect(std::max<int64_t>(1, (int64_t)fsh_pos.size()) * 4);
+    L.dyn_fnat = sect(std::max<int64_t>(1, (int64_t)fsh_nat.size()) * 16);
+    L.dyn_bshare = sect((int64_t)bsh_off.size() * 4);
+    L.dyn_bpos = sect(std::max<int64_t>(1, (int64_t)bsh_pos.size()) * 4);
+    L.dyn_bnat = sect(std::max<int64_t>(1, (int64_t)bsh_nat.size()) * 16);
   }
   L.total = off;
   try {
@@ -702,8 +757,14 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   if (dynamic) {
     std::memcpy(blob + L.dyn_base, base.data(), base.size());
     int32_t *ln = reinterpret_cast<int32_t *>(blob + L.dyn_len);
-    for (int32_t x : fwd_len) *ln++ = x;
-    for (int32_t x : bwd_len) *ln++ = x;
+    for (size_t i = 0; i < fwd_len.size(); ++i) { *ln++ = fwd_len[i]; *ln++ = fwd_npart[i]; }
+    for (size_t i = 0; i < bwd_len.size(); ++i) { *ln++ = bwd_len[i]; *ln++ = bwd_npart[i]; }
+    std::memcpy(blob + L.dyn_fshare, fsh_off.data(), fsh_off.size() * 4);
+    if (!fsh_pos.empty()) std::memcpy(blob + L.dyn_fpos, fsh_pos.data(), fsh_pos.size() * 4);
+    if (!fsh_nat.empty()) std::memcpy(blob + L.dyn_fnat, fsh_nat.data(), fsh_nat.size() * 16);
+    std::memcpy(blob + L.dyn_bshare, bsh_off.data(), bsh_off.size() * 4);
+    if (!bsh_pos.empty()) std::memcpy(blob + L.dyn_bpos, bsh_pos.data(), bsh_pos.size() * 4);
+    if (!bsh_nat.empty()) std::memcpy(blob + L.dyn_bnat, bsh_nat.data(), bsh_nat.size() * 16);
   }
 
   int64_t nnz_b = 0;

@@ -30,7 +30,11 @@ struct Layout {
   int64_t bits = -1, qblk = -1, kblk = -1, qoffs = -1, koffs = -1;
   int64_t n_fwd_items = 0, n_fwd_list = 0, n_bwd_items = 0, n_bwd_list = 0;
   int64_t n_bwd_reduce = 0, n_slots = 0;
-  int64_t dyn_base = -1, dyn_len = -1;  // dynamic plans only
+  // dynamic plans only: base micro-tile classes, (length, partial tiles) of
+  // every list, and the per-XCD-share reorder tables of both passes
+  int64_t dyn_base = -1, dyn_len = -1;
+  int64_t dyn_fshare = -1, dyn_fpos = -1, dyn_fnat = -1;
+  int64_t dyn_bshare = -1, dyn_bpos = -1, dyn_bnat = -1;
   int64_t total = 0;
 };
 
@@ -38,12 +42,15 @@ struct Layout {
 // the forward covers mask heads [g * fheads, (g + 1) * fheads) and owns the
 // forward lists of slots [g * nFQ, (g + 1) * nFQ), one per Q-tile; likewise
 // the dK/dV groups with bheads and nBK.  Every list has room for nM entries
-// at list + slot * nM.
+// at list + slot * nM.  The items of each pass are dealt to XCD shares
+// (fixed at creation); a share's items are re-sorted, longest first, within
+// the share's positions of the item array.
 struct DynInfo {
   bool on = false;
   int64_t nM = 0, nFQ = 0, nBK = 0;
   int64_t n_fslots = 0, n_bslots = 0;
   int MR = 1, MC = 2, fheads = 1, bheads = 1;
+  int n_fshares = 1, n_bshares = 1;
 };
 
 // dK/dV items whose work exceeds the share of one workgroup are split into

@@ -50,6 +50,11 @@ def _cases():
     o = syn.variable_partition(S, 30, 130, seed=9)
     docs = syn.sample_doc_lens(S, 64, 400, 4)
     out.append(("causal_document_base", syn.spec_document(docs, True), o, o, 4, 1, 64, 1))
+    # items dealt to the 8 XCDs by KV head, and not dealt at all
+    S = 700
+    o = syn.uniform_block_bitmap(S, 64, 1, seed=0)[0]
+    out.append(("mha8_by_head_deal", syn.spec_causal(S), o, o, 8, 8, 64, 8))
+    out.append(("gqa6_3_no_deal", syn.spec_full(S), o, o, 6, 3, 128, 3))
     return out
 
 
@@ -64,6 +69,24 @@ def _dev_bits(bits, scale=1):
     return torch.from_numpy(np.ascontiguousarray(bits * scale, dtype=np.uint8)).cuda()
 
 
+def _rows_sorted(a):
+    a = np.asarray(a)
+    return a[np.lexsort(a.T[::-1])]
+
+
+def _check_items(dl, fresh_layout, Hkv):
+    """Device-rebuilt items against those of a dynamic plan created with the
+    new bitmap: identical, order included, when the host deals items to
+    XCDs by head (Hkv a multiple of 8) or not at all (8 % Hkv != 0); the
+    same set otherwise (the deal is by load and stays the creation-time one)."""
+    for key in ("fwd_items", "bwd_items"):
+        a, b = dl[key], fresh_layout[key]
+        if Hkv % 8 == 0 or 8 % Hkv != 0:
+            assert np.array_equal(a, b), f"{key}: order differs from the host compiler's"
+        else:
+            assert np.array_equal(_rows_sorted(a), _rows_sorted(b)), f"{key} differ"
+
+
 def _check_lists_equal(dyn, spec_new, B, Hq, Hkv, d, bits_new):
     ref = lcm.Plan(B, spec_new["S"], Hq, Hkv, d, spec_new)
     fs, bs = lists_by_item(ref.layout())
@@ -71,6 +94,8 @@ def _check_lists_equal(dyn, spec_new, B, Hq, Hkv, d, bits_new):
     fd, bd = lists_by_item(dl)
     assert fd == fs, "forward / dQ lists differ from the host compiler's"
     assert bd == bs, "dK/dV lists differ from the host compiler's"
+    fresh = lcm.Plan(B, spec_new["S"], Hq, Hkv, d, dict(spec_new, dynamic=True))
+    _check_items(dl, fresh.layout(), Hkv)
     return ref
 
 
@@ -197,3 +222,70 @@ def test_set_bitmap_argument_errors():
     inside = dyn._dev.data_ptr() + dyn._dev_off   # the plan's own buffer
     assert L.lib().attn_plan_set_bitmap(dyn.handle, C.c_void_p(inside), None) == L.ATTN_ERR_INVALID
     assert b"overlaps" in L.lib().attn_last_error()
+
+
+@pytest.mark.parametrize("blk,heads", [(64, 8), (128, 64)], ids=["block64_per_kv_head", "block128_per_query_head"])
+def test_fullsize_sparse_32k_gqa(blk, heads):
+    """The sparse workload's shape (S = 32K, GQA 64:8, d = 128): after an
+    update the device lists equal the host compiler's for the new bitmap, O,
+    LSE and dQ equal the ordinary plan's bit for bit, and dK/dV (the ordinary
+    plan splits long items, with another summation order) agree to one bf16
+    rounding."""
+    from plan_util import concat_lists
+    S, Hq, Hkv, d = 32768, 64, 8, 128
+    print(f"dynamic full size S={S} block {blk} bitmap heads {heads}", flush=True)
+    offs, b1 = syn.uniform_block_bitmap(S, blk, heads, 0.5, seed=1)
+    _, b2 = syn.uniform_block_bitmap(S, blk, heads, 0.5, seed=2)
+    base = syn.spec_full(S)
+    dyn = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b1), dynamic=True))
+    static = lcm.Plan(1, S, Hq, Hkv, d, syn.with_bitmap(base, offs, offs, b2))
+    dyn.bind()
+    dyn.set_bitmap(_dev_bits(b2))
+    dl = dyn.device_layout()
+    (fk, fl, fe), (bk, bl, be) = concat_lists(dl)
+    (gk, gl, ge), (ck, cl, ce) = concat_lists(static.layout())
+    assert np.array_equal(fk, gk) and np.array_equal(fl, gl) and np.array_equal(fe, ge)
+    assert np.array_equal(bk, ck) and np.array_equal(bl, cl) and np.array_equal(be, ce)
+    fresh = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b2), dynamic=True))
+    _check_items(dl, fresh.layout(), Hkv)   # longest first, as a fresh plan
+    del fresh
+    x = syn.attention_inputs(1, S, Hq, Hkv, d, 7)
+    q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
+    del x
+    o1, l1 = lcm.fwd(dyn, q, k, v)
+    o2, l2 = lcm.fwd(static, q, k, v)
+    g1 = lcm.bwd(dyn, q, k, v, o1, l1, do)
+    g2 = lcm.bwd(static, q, k, v, o1, l1, do)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(g1[0], g2[0])
+    for a, b in zip(g1[1:], g2[1:]):
+        a, b = a.float(), b.float()
+        rms = float(b.pow(2).mean().sqrt())
+        assert bool(((a - b).abs() <= 2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 1e-4 * rms).all())
+
+
+def test_share_above_sort_cap_keeps_natural_order():
+    """No XCD deal (Hkv = 12) and more than 8192 items in the one share: the
+    items stay in natural order (query-head group, Q-tile) / (KV head,
+    K-tile), with their new lengths; lists as the host compiler's."""
+    S, Hq, Hkv, d = 90112, 12, 12, 64
+    offs, b1 = syn.uniform_block_bitmap(S, 128, 1, 0.5, seed=51)
+    _, b2 = syn.uniform_block_bitmap(S, 128, 1, 0.3, seed=52)
+    base = syn.spec_causal(S)
+    dyn = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b1), dynamic=True))
+    assert dyn.stats["fwd_items"] > 8192 and dyn.stats["bwd_items"] > 8192
+    dyn.bind()
+    dyn.set_bitmap(_dev_bits(b2))
+    from plan_util import concat_lists
+    dl = dyn.device_layout()
+    fresh = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b2), dynamic=True))
+    fl = fresh.layout()
+    for (a, b) in zip(concat_lists(dl), concat_lists(fl)):
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    nFQ, nBK = (S + 127) // 128, (S + 127) // 128
+    fi, bi = dl["fwd_items"], dl["bwd_items"]
+    assert np.array_equal(fi[:, 1] * nFQ + fi[:, 0], np.arange(len(fi)))   # HG = 1 (no GQA)
+    assert np.array_equal(bi[:, 1] * nBK + bi[:, 0], np.arange(len(bi)))
+    assert np.array_equal(_rows_sorted(fi), _rows_sorted(fl["fwd_items"]))
+    assert np.array_equal(_rows_sorted(bi), _rows_sorted(fl["bwd_items"]))
