@@ -301,6 +301,61 @@ attn_status attn_merge(const float *o1, const float *lse1, const float *o2, cons
 
 void attn_plan_destroy(attn_plan *plan);
 
+/*
+ * Calls that take the shape and the mask descriptor directly, for callers
+ * that do not keep plans: the one input representation of the
+ * "Long-Context Attention Benchmark" review (xllm-io), section 3, components
+ * table (the kernel adapter), with the compiled mask cached.
+ *
+ * Plan cache.  The library compiles each distinct (shape, descriptor
+ * content) once and keeps the host plan in a process-wide cache of at most
+ * ATTN_DESC_CACHE_PLANS plans, least recently used evicted first; lookups
+ * compare the full content (shape, scalars and every array the kind reads),
+ * so equal masks from different arrays share a plan and different masks
+ * never do.  All calls below are thread-safe against each other.
+ *
+ * Plan buffer.  The plan's device blob lives in `plan_buf`, device memory
+ * the caller provides (>= the plan bytes that attn_desc_plan_bytes returns,
+ * 256-byte aligned) and dedicates to the cache: the library records which
+ * plan's blob each buffer holds and uploads (synchronising `stream`) only
+ * when a call passes a buffer that holds another plan's blob or none.  The
+ * caller must not write to a plan buffer, and must call
+ * attn_desc_release(plan_buf) before freeing or reusing its memory.  One
+ * buffer per mask avoids uploads; a single buffer shared by several masks
+ * works, with an upload whenever the mask changes.
+ *
+ * Descriptors with dynamic = 1 are rejected (ATTN_ERR_INVALID): a dynamic
+ * plan is updated in place and is not shareable.  Errors are those of
+ * attn_plan_create, attn_plan_bind and attn_fwd / attn_bwd.
+ */
+#define ATTN_DESC_CACHE_PLANS 32
+
+/* Compile (or find) the plan of (shape, desc).  Outputs, each optional
+ * (NULL to skip): the plan buffer size, the attn_bwd workspace size, and a
+ * 64-bit hash of the cache key (equal masks give equal hashes; a caller may
+ * use it to keep one plan buffer per mask). */
+attn_status attn_desc_plan_bytes(const attn_shape *shape, const attn_mask_desc *desc,
+                                 size_t *plan_bytes, size_t *ws_bytes, uint64_t *key_hash);
+
+/* attn_fwd on the cached plan of (shape, desc), its blob in plan_buf. */
+attn_status attn_fwd_desc(const attn_shape *shape, const attn_mask_desc *desc, const void *q,
+                          const void *k, const void *v, void *o, float *lse, void *plan_buf,
+                          size_t plan_buf_bytes, attn_stream_t stream);
+
+/* attn_bwd on the cached plan of (shape, desc), its blob in plan_buf. */
+attn_status attn_bwd_desc(const attn_shape *shape, const attn_mask_desc *desc, const void *q,
+                          const void *k, const void *v, const void *o, const float *lse,
+                          const void *dout, void *dq, void *dk, void *dv, void *ws,
+                          size_t ws_bytes, void *plan_buf, size_t plan_buf_bytes,
+                          attn_stream_t stream);
+
+/* Forget that plan_buf holds a plan blob (call before freeing or reusing
+ * it).  Unknown buffers are ignored.  Never fails. */
+void attn_desc_release(void *plan_buf);
+
+/* Empty the plan cache (all plans destroyed, all buffers forgotten). */
+void attn_desc_cache_clear(void);
+
 const char *attn_last_error(void);
 
 /* Library version string. */

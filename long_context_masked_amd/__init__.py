@@ -11,6 +11,7 @@ library is not built, every call raises.
 """
 from __future__ import annotations
 
+import collections
 import ctypes as C
 
 import numpy as np
@@ -19,7 +20,8 @@ from . import _lib as L
 from .masks import MaskDescriptor, column_bounds  # noqa: F401
 
 __all__ = ["Plan", "fwd", "bwd", "attention", "MaskDescriptor", "column_bounds",
-           "AttnError", "library_path"]
+           "AttnError", "library_path", "fwd_partial", "merge", "fwd_desc", "bwd_desc",
+           "desc_cache_clear"]
 
 AttnError = L.AttnError
 library_path = L.LIB_PATH
@@ -234,6 +236,93 @@ def merge(o1, lse1, o2, lse2, bf16_out=False, out=None, lse_out=None):
                                P(lse2.data_ptr()), P(o.data_ptr()), int(bool(bf16_out)),
                                P(lse.data_ptr()), B, S, Hq, d, P(stream)))
     return o, lse
+
+
+# Plan buffers of the descriptor calls: one torch buffer per (device, mask
+# content hash, size), least recently used dropped first; the library is
+# told before a buffer is dropped.
+_DESC_BUFS = collections.OrderedDict()
+_DESC_BUF_LIMIT = 32
+
+
+def _aligned(buf):
+    ptr = buf.data_ptr()
+    return ptr + (-ptr) % 256
+
+
+def _desc_setup(q, k, mask, scale):
+    """(shape struct, descriptor, plan buffer pointer, plan bytes, workspace bytes)."""
+    import torch
+    B, S, Hq, d = (int(x) for x in q.shape)
+    Hkv = int(k.shape[2])
+    desc = mask if isinstance(mask, MaskDescriptor) else MaskDescriptor(mask)
+    sh = L.Shape(B, S, Hq, Hkv, d, float(scale))
+    pb, wb, kh = C.c_size_t(), C.c_size_t(), C.c_uint64()
+    L.check(L.lib().attn_desc_plan_bytes(C.byref(sh), C.byref(desc.c), C.byref(pb), C.byref(wb),
+                                         C.byref(kh)))
+    idx = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    key = (idx, kh.value, pb.value)
+    buf = _DESC_BUFS.get(key)
+    if buf is None:
+        buf = torch.empty(max(pb.value, 256) + 256, dtype=torch.uint8, device=q.device)
+        _DESC_BUFS[key] = buf
+        while len(_DESC_BUFS) > _DESC_BUF_LIMIT:
+            _, old = _DESC_BUFS.popitem(last=False)
+            L.lib().attn_desc_release(C.c_void_p(_aligned(old)))
+    else:
+        _DESC_BUFS.move_to_end(key)
+    return sh, desc, _aligned(buf), pb.value, wb.value
+
+
+def fwd_desc(q, k, v, mask, scale=0.0, out=None, lse=None):
+    """fwd() from the mask spec (or MaskDescriptor) directly: the library
+    compiles each distinct mask once and caches it (attn_fwd_desc)."""
+    import torch
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    _check_tensor(q, "q", (B, S, Hq, d), torch)
+    _check_tensor(k, "k", (B, S, Hkv, d), torch)
+    _check_tensor(v, "v", (B, S, Hkv, d), torch)
+    sh, desc, pbuf, pbytes, _ = _desc_setup(q, k, mask, scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    P = C.c_void_p
+    L.check(L.lib().attn_fwd_desc(C.byref(sh), C.byref(desc.c), P(q.data_ptr()), P(k.data_ptr()),
+                                  P(v.data_ptr()), P(o.data_ptr()), P(lse.data_ptr()), P(pbuf),
+                                  C.c_size_t(pbytes), P(stream)))
+    return o, lse
+
+
+def bwd_desc(q, k, v, o, lse, do, mask, scale=0.0, workspace=None):
+    """bwd() from the mask spec (or MaskDescriptor) directly (attn_bwd_desc)."""
+    import torch
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    for t, n, s in ((q, "q", (B, S, Hq, d)), (k, "k", (B, S, Hkv, d)), (v, "v", (B, S, Hkv, d)),
+                    (o, "o", (B, S, Hq, d)), (do, "do", (B, S, Hq, d))):
+        _check_tensor(t, n, s, torch)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, Hq, S]")
+    sh, desc, pbuf, pbytes, nws = _desc_setup(q, k, mask, scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(nws + 256, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    P = C.c_void_p
+    L.check(L.lib().attn_bwd_desc(C.byref(sh), C.byref(desc.c), P(q.data_ptr()), P(k.data_ptr()),
+                                  P(v.data_ptr()), P(o.data_ptr()), P(lse.data_ptr()),
+                                  P(do.data_ptr()), P(dq.data_ptr()), P(dk.data_ptr()),
+                                  P(dv.data_ptr()), P(_aligned(ws)), C.c_size_t(nws), P(pbuf),
+                                  C.c_size_t(pbytes), P(stream)))
+    return dq, dk, dv
+
+
+def desc_cache_clear():
+    """Drop every cached plan and plan buffer of the descriptor calls."""
+    for buf in _DESC_BUFS.values():
+        L.lib().attn_desc_release(C.c_void_p(_aligned(buf)))
+    _DESC_BUFS.clear()
+    L.lib().attn_desc_cache_clear()
 
 
 def attention(q, k, v, plan: Plan):

@@ -15,7 +15,7 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
 HIP_SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "dyn.hip"]
-CXX_SOURCES = ["plan.cpp"]
+CXX_SOURCES = ["plan.cpp", "desc_cache.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

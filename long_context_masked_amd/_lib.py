@@ -75,6 +75,14 @@ SIGNATURES = {
     "attn_bwd_dq": (C.c_int, [C.c_void_p] * 8 + [C.c_size_t, C.c_void_p]),
     "attn_fwd_partial": (C.c_int, [C.c_void_p] * 7),
     "attn_merge": (C.c_int, [C.c_void_p] * 5 + [C.c_int, C.c_void_p] + [C.c_int64] * 4 + [C.c_void_p]),
+    "attn_desc_plan_bytes": (C.c_int, [C.POINTER(Shape), C.POINTER(MaskDesc), C.POINTER(C.c_size_t),
+                                       C.POINTER(C.c_size_t), C.POINTER(C.c_uint64)]),
+    "attn_fwd_desc": (C.c_int, [C.POINTER(Shape), C.POINTER(MaskDesc)] + [C.c_void_p] * 6
+                      + [C.c_size_t, C.c_void_p]),
+    "attn_bwd_desc": (C.c_int, [C.POINTER(Shape), C.POINTER(MaskDesc)] + [C.c_void_p] * 10
+                      + [C.c_size_t, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "attn_desc_release": (None, [C.c_void_p]),
+    "attn_desc_cache_clear": (None, []),
     "attn_plan_destroy": (None, [C.c_void_p]),
     "attn_last_error": (C.c_char_p, []),
     "attn_version": (C.c_char_p, []),

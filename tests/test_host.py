@@ -467,3 +467,99 @@ def test_dynamic_plan_errors():
     assert lib.attn_plan_set_bitmap(dyn.handle, a, None) == L.ATTN_ERR_INVALID
     assert b"not bound" in lib.attn_last_error()
     assert lib.attn_plan_set_bitmap(None, a, None) == L.ATTN_ERR_INVALID
+
+
+def _desc_bytes(shape, desc):
+    sh = L.Shape(*shape)
+    pb, wb, kh = C.c_size_t(), C.c_size_t(), C.c_uint64()
+    st = L.lib().attn_desc_plan_bytes(C.byref(sh), C.byref(desc), C.byref(pb), C.byref(wb), C.byref(kh))
+    return st, pb.value, wb.value, kh.value
+
+
+def test_desc_plan_cache_keys_on_content():
+    """Equal masks from different arrays share one cached plan (same sizes
+    and key hash); any change of shape, scalar, array or bitmap bit gives
+    another; the sizes are those of an ordinary plan."""
+    lib = L.lib()
+    lib.attn_desc_cache_clear()
+    S = 300
+    shape = (1, S, 4, 2, 64, 0.0)
+    docs = [100, 120, 80]
+    d1 = lcm.MaskDescriptor(syn.spec_document(docs, True))
+    d2 = lcm.MaskDescriptor(syn.spec_document(list(docs), True))   # other arrays, same content
+    st1, pb1, wb1, h1 = _desc_bytes(shape, d1.c)
+    st2, pb2, wb2, h2 = _desc_bytes(shape, d2.c)
+    assert st1 == st2 == L.ATTN_OK and (pb1, wb1, h1) == (pb2, wb2, h2)
+    p = lcm.Plan(*shape[:5], syn.spec_document(docs, True))
+    assert pb1 == p.device_bytes() and wb1 == p.workspace_bytes()
+    hashes = {h1}
+    for spec in (syn.spec_document(docs, False), syn.spec_document([100, 121, 79], True),
+                 syn.spec_causal(S), syn.spec_sliding(S, 64, True), syn.spec_sliding(S, 65, True)):
+        st, _, _, h = _desc_bytes(shape, lcm.MaskDescriptor(spec).c)
+        assert st == L.ATTN_OK
+        hashes.add(h)
+    st, _, _, h = _desc_bytes((2, S, 4, 2, 64, 0.0), d1.c)
+    hashes.add(h)
+    st, _, _, h = _desc_bytes((1, S, 4, 2, 64, 0.1), d1.c)
+    hashes.add(h)
+    offs, bits = syn.uniform_block_bitmap(S, 64, 2, 0.5, seed=3)
+    b = syn.with_bitmap(syn.spec_causal(S), offs, offs, bits)
+    _, _, _, hb = _desc_bytes(shape, lcm.MaskDescriptor(b).c)
+    b5 = syn.with_bitmap(syn.spec_causal(S), offs, offs, bits * 5)   # nonzero = on
+    _, _, _, hb5 = _desc_bytes(shape, lcm.MaskDescriptor(b5).c)
+    assert hb == hb5
+    flipped = bits.copy()
+    flipped[1, 2, 3] ^= 1
+    _, _, _, hf = _desc_bytes(shape, lcm.MaskDescriptor(syn.with_bitmap(syn.spec_causal(S), offs, offs, flipped)).c)
+    hashes.update({hb, hf})
+    assert len(hashes) == 10
+
+
+def test_desc_plan_cache_errors_and_eviction():
+    lib = L.lib()
+    S = 256
+    shape = (1, S, 4, 2, 64, 0.0)
+    offs, bits = syn.uniform_block_bitmap(S, 64, 2, 0.5, 0)
+    dyn = lcm.MaskDescriptor(dict(syn.with_bitmap(syn.spec_causal(S), offs, offs, bits), dynamic=True))
+    assert _desc_bytes(shape, dyn.c)[0] == L.ATTN_ERR_INVALID
+    assert b"dynamic" in lib.attn_last_error()
+    bad = lcm.MaskDescriptor(syn.spec_causal(S))
+    bad.c.kind = 99
+    assert _desc_bytes(shape, bad.c)[0] == L.ATTN_ERR_INVALID
+    assert _desc_bytes((1, S, 4, 2, 96, 0.0), lcm.MaskDescriptor(syn.spec_causal(S)).c)[0] == L.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_desc_plan_bytes(None, None, None, None, None) == L.ATTN_ERR_INVALID
+    # more distinct masks than the cache holds: the oldest are evicted and
+    # compiled again when asked for
+    first = _desc_bytes(shape, lcm.MaskDescriptor(syn.spec_sliding(S, 1, True)).c)
+    for w in range(1, 45):
+        st, pb, _, _ = _desc_bytes(shape, lcm.MaskDescriptor(syn.spec_sliding(S, w, True)).c)
+        assert st == L.ATTN_OK and pb > 0
+    again = _desc_bytes(shape, lcm.MaskDescriptor(syn.spec_sliding(S, 1, True)).c)
+    assert again == first
+    lib.attn_desc_cache_clear()
+    lib.attn_desc_release(None)   # unknown buffers are ignored
+
+
+def test_desc_calls_validate_before_touching_the_gpu():
+    """Argument errors of attn_fwd_desc / attn_bwd_desc return before any
+    upload or launch (this host has no GPU)."""
+    lib = L.lib()
+    S = 128
+    sh = L.Shape(1, S, 2, 1, 64, 0.0)
+    d = lcm.MaskDescriptor(syn.spec_causal(S))
+    P = C.c_void_p
+    a = P(4096)  # never dereferenced
+    big = C.c_size_t(1 << 24)
+    assert lib.attn_fwd_desc(C.byref(sh), C.byref(d.c), None, a, a, a, a, a, big, None) == L.ATTN_ERR_INVALID
+    assert lib.attn_fwd_desc(C.byref(sh), C.byref(d.c), a, a, a, a, P(4098), a, big, None) == L.ATTN_ERR_INVALID
+    assert lib.attn_fwd_desc(C.byref(sh), C.byref(d.c), a, a, a, a, a, None, big, None) == L.ATTN_ERR_INVALID
+    assert lib.attn_fwd_desc(C.byref(sh), C.byref(d.c), a, a, a, a, a, P(4096 + 16), big, None) == L.ATTN_ERR_INVALID
+    assert lib.attn_fwd_desc(C.byref(sh), C.byref(d.c), a, a, a, a, a, a, C.c_size_t(8), None) == L.ATTN_ERR_INVALID
+    assert lib.attn_bwd_desc(C.byref(sh), C.byref(d.c), a, a, a, a, a, a, a, a, a, a, C.c_size_t(16), a, big,
+                             None) == L.ATTN_ERR_INVALID
+    assert b"workspace" in lib.attn_last_error()
+    os.environ["ATTN_FORCE_DEVICE_ERROR"] = "1"
+    try:
+        assert lib.attn_fwd_desc(C.byref(sh), C.byref(d.c), a, a, a, a, a, a, big, None) == L.ATTN_ERR_DEVICE
+    finally:
+        del os.environ["ATTN_FORCE_DEVICE_ERROR"]
