@@ -153,8 +153,14 @@ def _check_tensor(t, name, shape, torch):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
 
 
-def fwd(plan: Plan, q, k, v, out=None, lse=None):
-    """O [B,S,Hq,d] bf16 and LSE [B,Hq,S] fp32 (natural log)."""
+def fwd(plan, q, k, v=None, out=None, lse=None):
+    """O [B,S,Hq,d] bf16 and LSE [B,Hq,S] fp32 (natural log).
+
+    ``fwd(plan, q, k, v)`` runs on a compiled Plan; ``fwd(q, k, v, mask)``
+    takes the mask spec (or MaskDescriptor) and uses the library's plan
+    cache (fwd_desc)."""
+    if not isinstance(plan, Plan):
+        return fwd_desc(plan, q, k, v, out=out, lse=lse)
     import torch
     B, S, Hq, Hkv, d = plan.shape
     _check_tensor(q, "q", (B, S, Hq, d), torch)
@@ -170,8 +176,16 @@ def fwd(plan: Plan, q, k, v, out=None, lse=None):
     return o, lse
 
 
-def bwd(plan: Plan, q, k, v, o, lse, do, workspace=None, grads=None):
-    """dQ, dK, dV (bf16) from the forward's O and LSE and the output gradient dO."""
+def bwd(plan, q, k, v, o, lse, do, workspace=None, grads=None):
+    """dQ, dK, dV (bf16) from the forward's O and LSE and the output gradient dO.
+
+    ``bwd(plan, q, k, v, o, lse, do)`` runs on a compiled Plan;
+    ``bwd(q, k, v, o, lse, do, mask)`` takes the mask and uses the plan cache
+    (bwd_desc)."""
+    if not isinstance(plan, Plan):
+        if grads is not None:
+            raise ValueError("grads= is only for the Plan form")
+        return bwd_desc(plan, q, k, v, o, lse, do, workspace=workspace)
     import torch
     B, S, Hq, Hkv, d = plan.shape
     for t, n, s in ((q, "q", (B, S, Hq, d)), (k, "k", (B, S, Hkv, d)), (v, "v", (B, S, Hkv, d)),
@@ -325,20 +339,26 @@ def desc_cache_clear():
     L.lib().attn_desc_cache_clear()
 
 
-def attention(q, k, v, plan: Plan):
-    """Differentiable masked attention through torch.autograd."""
+def attention(q, k, v, plan):
+    """Differentiable masked attention through torch.autograd; ``plan`` is a
+    Plan or a mask spec / MaskDescriptor (then the plan cache is used)."""
     import torch
 
     class _Attn(torch.autograd.Function):
         @staticmethod
         def forward(ctx, q_, k_, v_):
-            o, lse = fwd(plan, q_, k_, v_)
+            if isinstance(plan, Plan):
+                o, lse = fwd(plan, q_, k_, v_)
+            else:
+                o, lse = fwd_desc(q_, k_, v_, plan)
             ctx.save_for_backward(q_, k_, v_, o, lse)
             return o
 
         @staticmethod
         def backward(ctx, do):
             q_, k_, v_, o, lse = ctx.saved_tensors
-            return bwd(plan, q_, k_, v_, o, lse, do.contiguous())
+            if isinstance(plan, Plan):
+                return bwd(plan, q_, k_, v_, o, lse, do.contiguous())
+            return bwd_desc(q_, k_, v_, o, lse, do.contiguous(), plan)
 
     return _Attn.apply(q, k, v)

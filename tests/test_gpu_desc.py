@@ -114,3 +114,24 @@ def test_cache_clear_then_calls_again():
     o2, l2 = lcm.fwd_desc(q, k, v, spec)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_python_forms_with_a_mask_and_autograd():
+    """fwd(q, k, v, mask), bwd(q, k, v, o, lse, do, mask) and attention(q, k,
+    v, mask) equal the Plan forms."""
+    _, (q, k, v, do) = _inputs(5)
+    spec = SPECS[2][1]
+    plan = lcm.Plan(B, S, Hq, Hkv, d, spec)
+    o1, l1 = lcm.fwd(q, k, v, spec)
+    g1 = lcm.bwd(q, k, v, o1, l1, do, spec)
+    o2, l2 = lcm.fwd(plan, q, k, v)
+    g2 = lcm.bwd(plan, q, k, v, o2, l2, do)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    oa = lcm.attention(qa, ka, va, spec)
+    oa.backward(do)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.detach(), o2)
+    assert torch.equal(qa.grad, g2[0]) and torch.equal(ka.grad, g2[1]) and torch.equal(va.grad, g2[2])
