@@ -46,6 +46,14 @@ COPY_KERNEL_HINT = "copy"
 # flops, of each kernel: forward = Q K^T + P V; dK/dV pass = Q K^T, dO V^T,
 # P^T dO, dS^T Q; dQ pass = Q K^T, dO V^T, dS K.
 KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dkdv": 8, "dq": 6}
+# MFMA-busy fraction and shader clock of the three main kernels, from one
+# rocprofv3 --pmc pass (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE) over a bench
+# step, stored in MFMA_FILE with a hash of the kernels' sources, as for traffic.
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_dense.json")
+MFMA_SOURCES = ["long_context_masked_amd/csrc/fwd.hip", "long_context_masked_amd/csrc/bwd.hip",
+                "long_context_masked_amd/csrc/kernels.hpp"]
+MFMA_KERNELS = {"fwd": "attn_fwd_kernel", "dkdv": "attn_dkdv_kernel", "dq": "attn_dq_kernel"}
+N_CU, N_SIMD, BF16_FLOP_PER_CLK_CU, N_XCD = 256, 1024, 4096, 8
 
 
 def log(*a):
@@ -226,9 +234,9 @@ def dynamic_rebuild(lcm, torch, dev, tensors_for, reps=20, steps=3):
     return out
 
 
-def sources_sha256():
+def sources_sha256(sources=None):
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in (TRAFFIC_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -285,6 +293,44 @@ def traffic_for(desc):
     return t.get("bytes_per_launch")
 
 
+def summarize_mfma(csv_path, workload_desc, commands):
+    """Per main kernel: the MFMA-busy fraction (busy cycles over all SIMDs
+    divided by the active clocks of one XCD times the SIMD count) and the
+    shader clock (active clocks of one XCD over the dispatch durations)."""
+    disp = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+            e = disp.setdefault(key, {"t": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = {"workload": workload_desc, "commands": commands, "sources": MFMA_SOURCES,
+           "source_sha256": sources_sha256(MFMA_SOURCES), "kernels": {}}
+    for short, name in MFMA_KERNELS.items():
+        rows = [e for (k, _), e in disp.items() if name in k]
+        if not rows:
+            raise SystemExit(f"{csv_path}: no {name} dispatches")
+        clk = sum(e["GRBM_GUI_ACTIVE"] for e in rows) / N_XCD   # cycles, per XCD
+        busy = sum(e["SQ_VALU_MFMA_BUSY_CYCLES"] for e in rows)
+        ns = sum(e["t"] for e in rows)
+        out["kernels"][short] = {"dispatches": len(rows), "mfma_busy_frac": round(busy / (clk * N_SIMD), 4),
+                                 "clock_GHz": round(clk / ns, 3),
+                                 "mfma_insts": sum(e.get("SQ_INSTS_MFMA", 0.0) for e in rows)}
+    return out
+
+
+def mfma_for(desc):
+    """The stored MFMA counters if taken on this workload with the current
+    kernel sources, else None."""
+    try:
+        with open(MFMA_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != sources_sha256(MFMA_SOURCES) or t.get("workload") != desc:
+        return None
+    return t["kernels"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,7 +348,17 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic file from two counter runs and exit (no GPU)")
     ap.add_argument("--traffic-commands", default="", help="commands recorded in the traffic file")
+    ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
+                    help="write the MFMA counter file from one counter run and exit (no GPU)")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        seqs = [int(x) for x in args.seqs.split(",") if x] if args.seqs else []
+        _, desc = workload(args.workload, seqs)
+        t = summarize_mfma(args.summarize_mfma, desc, args.traffic_commands)
+        with open(MFMA_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return
     if args.summarize_traffic:
         seqs = [int(x) for x in args.seqs.split(",") if x] if args.seqs else []
         _, desc = workload(args.workload, seqs)
@@ -465,9 +521,24 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for(desc) if dom == "dkdv" else None},
+        "kernel_tflops": {k: round(alg[k] / kern[k] / 1e12, 2) for k in alg},
         "plan_build_s": round(plan_secs, 3),
         "detail": detail,
     }
+    mf = mfma_for(desc)
+    if mf:
+        # the same kernels against the MFMA peak at the clock they ran at,
+        # beside the counters' MFMA-busy fraction
+        mcnt = {}
+        for key, m in mf.items():
+            peak_clk = N_CU * BF16_FLOP_PER_CLK_CU * m["clock_GHz"] / 1e3
+            ach = alg[key] / kern[key] / 1e12
+            mcnt[key] = {"mfma_busy_frac": m["mfma_busy_frac"], "clock_GHz": m["clock_GHz"],
+                         "peak_at_clock_tflops": round(peak_clk, 1),
+                         "frac_at_clock": round(ach / peak_clk, 4)}
+        out["mfma_counters"] = mcnt
+        out["roofline"]["mfma_busy_frac"] = mcnt[dom]["mfma_busy_frac"]
+        out["roofline"]["frac_at_measured_clock"] = mcnt[dom]["frac_at_clock"]
     log("merge of partial results")
     out["merge"] = merge_rate(lcm, torch, dev)
     if args.workload == "sparse" and not args.no_dynamic:
