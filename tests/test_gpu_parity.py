@@ -173,3 +173,10 @@ def test_forced_device_error_leaves_outputs_untouched(monkeypatch):
     monkeypatch.delenv("ATTN_FORCE_DEVICE_ERROR")
     torch.cuda.synchronize()
     assert (o == 7.0).all() and (lse == 3.0).all()
+
+
+def test_smoke_entry_point():
+    """The package's smoke check (one causal fwd + bwd at S = 512 against the
+    oracle, with the gate above) passes."""
+    import __graft_entry__
+    __graft_entry__.smoke()
