@@ -294,6 +294,19 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   // List entries are read a stage before they are needed, so that the
   // latency of the scalar load is covered by the products of a stage.
   uint32_t ent1 = nst > 1 ? list[1 / G] : 0u;  // stage st + 1
+  // The first operand rows and the LSE rows of a stage's phase 1 are read
+  // during the previous stage's phase 3b (stage 0: here).
+  f32x4 l0n[4];
+  bf16x8 aqn[2], aon[2];
+  {
+    const float *sl0 = reinterpret_cast<const float *>(smem + OFF_L) + 4 * hh;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) l0n[c] = *reinterpret_cast<const f32x4 *>(sl0 + 8 * c);
+    aqn[0] = rows_q(smem, 1, 0);
+    aon[0] = rows_o(smem, 1, 0);
+    aqn[1] = rows_q(smem, 1, 1);
+    aon[1] = rows_o(smem, 1, 1);
+  }
   for (int st = 0; st < nst; ++st) {
     const uint32_t ent2 = st + 2 < nst ? list[(st + 2) / G] : 0u;  // stage st + 2
 #pragma unroll
@@ -320,12 +333,12 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     const float *sl = reinterpret_cast<const float *>(buf + OFF_L) + 4 * hh;
     f32x4 l0[4], l1[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) l0[c] = *reinterpret_cast<const f32x4 *>(sl + 8 * c);
+    for (int c = 0; c < 4; ++c) l0[c] = l0n[c];
     bf16x8 aq[KS], ao[KS];
-    aq[0] = rows_q(buf, 1, 0);
-    ao[0] = rows_o(buf, 1, 0);
-    aq[1] = rows_q(buf, 1, 1);
-    ao[1] = rows_o(buf, 1, 1);
+    aq[0] = aqn[0];
+    ao[0] = aon[0];
+    aq[1] = aqn[1];
+    ao[1] = aon[1];
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- phase 1: A(st, 1) with the exponentials of B(st, 0)
@@ -431,6 +444,16 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       for (int i = 0; i < 16 / NC; ++i) {
         const int r = c * (16 / NC) + i;
         b_read(s0, dp0, sa0, dpa0, r);
+      }
+      if (c == DB) {
+        // phase 1 of stage st + 1 reads nbuf: start its first reads now
+        const float *sln = reinterpret_cast<const float *>(nbuf + OFF_L) + 4 * hh;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) l0n[q4] = *reinterpret_cast<const f32x4 *>(sln + 8 * q4);
+        aqn[0] = rows_q(nbuf, 1, 0);
+        aon[0] = rows_o(nbuf, 1, 0);
+        aqn[1] = rows_q(nbuf, 1, 1);
+        aon[1] = rows_o(nbuf, 1, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
