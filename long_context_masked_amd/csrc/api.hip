@@ -135,6 +135,7 @@ extern "C" attn_status attn_plan_set_bitmap(attn_plan *plan, const uint8_t *bits
   a.n_bslots = (int)D.n_bslots;
   a.fheads = D.fheads;
   a.bheads = D.bheads;
+  (void)hipGetLastError();
   const hipError_t e = launch_dyn(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "list rebuild launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;

@@ -181,6 +181,8 @@ extern "C" attn_status attn_desc_plan_bytes(const attn_shape *shape, const attn_
     return ATTN_OK;
   } catch (const std::bad_alloc &) {
     return fail(ATTN_ERR_NOMEM, "host allocation failed in the plan cache");
+  } catch (...) {
+    return fail(ATTN_ERR_INVALID, "unexpected error in the plan cache");
   }
 }
 
@@ -202,6 +204,8 @@ extern "C" attn_status attn_fwd_desc(const attn_shape *shape, const attn_mask_de
     return attn_fwd(e->plan, q, k, v, o, lse, stream);
   } catch (const std::bad_alloc &) {
     return fail(ATTN_ERR_NOMEM, "host allocation failed in the plan cache");
+  } catch (...) {
+    return fail(ATTN_ERR_INVALID, "unexpected error in the plan cache");
   }
 }
 
@@ -232,6 +236,8 @@ extern "C" attn_status attn_bwd_desc(const attn_shape *shape, const attn_mask_de
     return attn_bwd(e->plan, q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, stream);
   } catch (const std::bad_alloc &) {
     return fail(ATTN_ERR_NOMEM, "host allocation failed in the plan cache");
+  } catch (...) {
+    return fail(ATTN_ERR_INVALID, "unexpected error in the plan cache");
   }
 }
 
