@@ -385,10 +385,14 @@ __device__ __forceinline__ uint64_t row_mask(const MaskArgs &m, int4 rb, int qb,
     const int last = (t0 + 63 < S ? t0 + 63 : S - 1);
     const int kb0 = m.kblk[t0], kb1 = m.kblk[last];
     const uint8_t *brow = m.bits + ((int64_t)hm * m.nqb + qb) * m.nkb;
-    uint64_t keep = 0;
-    for (int kb = kb0; kb <= kb1; ++kb)
-      if (brow[kb]) keep |= range64(m.koffs[kb] - t0, m.koffs[kb + 1] - t0);
-    bits &= keep;
+    if (kb0 == kb1) {  // the tile lies in one key block: all or nothing
+      if (!brow[kb0]) bits = 0;
+    } else {
+      uint64_t keep = 0;
+      for (int kb = kb0; kb <= kb1; ++kb)
+        if (brow[kb]) keep |= range64(m.koffs[kb] - t0, m.koffs[kb + 1] - t0);
+      bits &= keep;
+    }
   }
   return bits;
 }
@@ -402,10 +406,14 @@ __device__ __forceinline__ uint64_t col_mask(const MaskArgs &m, int4 cb, int kb,
     const int last = (r0 + 63 < S ? r0 + 63 : S - 1);
     const int qb0 = m.qblk[r0], qb1 = m.qblk[last];
     const uint8_t *bcol = m.bits + (int64_t)hm * m.nqb * m.nkb + kb;
-    uint64_t keep = 0;
-    for (int qb = qb0; qb <= qb1; ++qb)
-      if (bcol[(int64_t)qb * m.nkb]) keep |= range64(m.qoffs[qb] - r0, m.qoffs[qb + 1] - r0);
-    bits &= keep;
+    if (qb0 == qb1) {  // the tile's rows lie in one row block: all or nothing
+      if (!bcol[(int64_t)qb0 * m.nkb]) bits = 0;
+    } else {
+      uint64_t keep = 0;
+      for (int qb = qb0; qb <= qb1; ++qb)
+        if (bcol[(int64_t)qb * m.nkb]) keep |= range64(m.qoffs[qb] - r0, m.qoffs[qb + 1] - r0);
+      bits &= keep;
+    }
   }
   return bits;
 }
