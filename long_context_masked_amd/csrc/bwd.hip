@@ -554,6 +554,11 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
   const bf16 *kbase = a.k + (int64_t)b * S * ldk + (int64_t)kvh * D;
   const bf16 *vbase = a.v + (int64_t)b * S * ldk + (int64_t)kvh * D;
   const bool row_ok = row < S;
+  if (item.w == 0) {
+    // no listed tile: dQ of the item's rows is 0
+    if (row_ok) zero_half_row<D>(a.dq + ((int64_t)b * S + row) * ldq + (int64_t)h * D, hh);
+    return;
+  }
 
   bf16x8 qv[KS], dov[KS];
   {

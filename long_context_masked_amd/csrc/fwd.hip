@@ -54,6 +54,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const bf16 *kbase = a.k + (int64_t)b * S * ldk + (int64_t)kvh * D;
   const bf16 *vbase = a.v + (int64_t)b * S * ldk + (int64_t)kvh * D;
   const bool row_ok = row < S;
+  if (item.w == 0) {
+    // no listed tile: no row of the item has an allowed key (O = 0, LSE = -inf)
+    if (row_ok) {
+      const int64_t o0 = ((int64_t)b * S + row) * ldq + (int64_t)h * D;
+      if (a.o32) zero_half_row<D>(a.o32 + o0, hh);
+      else zero_half_row<D>(a.o + o0, hh);
+      if (hh == 0) a.lse[((int64_t)b * a.Hq + h) * S + row] = kNegInf;
+    }
+    return;
+  }
 
   bf16x8 qv[KS];
   {

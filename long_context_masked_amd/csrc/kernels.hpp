@@ -377,6 +377,15 @@ struct DynArgs {
   int copy_blocks;
 };
 
+// Zeros over half hh of a D-wide row (the two lane halves split it).
+template <int D, typename E>
+__device__ __forceinline__ void zero_half_row(E *row, int hh) {
+  constexpr int PER = 16 / sizeof(E);  // elements per 16-byte store
+  E *p = row + hh * (D / 2);
+#pragma unroll
+  for (int i = 0; i < D / 2; i += PER) *reinterpret_cast<uint4 *>(p + i) = make_uint4(0u, 0u, 0u, 0u);
+}
+
 // Allowed-key bits of query row `row` over keys [t0, t0 + 64).
 __device__ __forceinline__ uint64_t row_mask(const MaskArgs &m, int4 rb, int qb, int hm,
                                              int t0, int S) {
