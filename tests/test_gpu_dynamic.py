@@ -289,3 +289,35 @@ def test_share_above_sort_cap_keeps_natural_order():
     assert np.array_equal(bi[:, 1] * nBK + bi[:, 0], np.arange(len(bi)))
     assert np.array_equal(_rows_sorted(fi), _rows_sorted(fl["fwd_items"]))
     assert np.array_equal(_rows_sorted(bi), _rows_sorted(fl["bwd_items"]))
+
+
+def test_random_shapes_and_partitions_lists_bit_exact():
+    """Seeded random configurations: ragged S, every head grouping (bitmap
+    heads 1, Hkv or Hq; odd groups), distinct random row and column block
+    partitions (tiny blocks included), densities from 0 to 1, several base
+    masks.  After each update the device-built lists and items equal the
+    host compiler's (items in full when the host's XCD deal does not depend
+    on costs, as a set otherwise)."""
+    rng = np.random.default_rng(2024)
+    groupings = [(4, 2), (8, 2), (3, 1), (6, 3), (8, 8), (2, 2), (12, 4)]
+    for trial in range(24):
+        S = int(rng.integers(65, 1500))
+        Hq, Hkv = groupings[trial % len(groupings)]
+        G = Hq // Hkv
+        heads = [1, Hkv, Hq][int(rng.integers(0, 3))]
+        lo = int(rng.choice([1, 8, 32, 64]))
+        qo = syn.variable_partition(S, lo, lo + int(rng.integers(0, 200)), seed=int(rng.integers(1 << 30)))
+        ko = syn.variable_partition(S, lo, lo + int(rng.integers(0, 200)), seed=int(rng.integers(1 << 30)))
+        base = [syn.spec_full(S), syn.spec_causal(S), syn.spec_sliding(S, int(rng.integers(16, 400)), True),
+                syn.spec_document(syn.sample_doc_lens(S, 16, 300, int(rng.integers(100))), True)][trial % 4]
+        d = 64 if trial % 2 else 128
+        dens = [0.0, 0.1, 0.5, 0.9, 1.0][trial % 5]
+        b1 = _bits(qo, ko, heads, 0.5, seed=int(rng.integers(1 << 30)), diag_on=False)
+        b2 = _bits(qo, ko, heads, dens, seed=int(rng.integers(1 << 30)), diag_on=False)
+        print(f"trial {trial}: S={S} Hq={Hq} Hkv={Hkv} heads={heads} d={d} blocks {len(qo) - 1}x{len(ko) - 1} "
+              f"density {dens}", flush=True)
+        dyn = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, qo, ko, b1), dynamic=True))
+        dyn.bind()
+        dyn.set_bitmap(_dev_bits(b2))
+        _check_lists_equal(dyn, syn.with_bitmap(base, qo, ko, b2), 1, Hq, Hkv, d, b2)
+        _check_bits_section(dyn, b2)
