@@ -99,6 +99,11 @@ def lib():
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
                 " (there is no fallback path)")
+        # torch ships its own HIP runtime under the same soname as the
+        # system one that libattn.so names.  Loading torch first makes the
+        # library bind to that copy; loaded the other way round, the process
+        # would hold two HIP runtimes and the second to start sees no device.
+        import torch  # noqa: F401
         L = C.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(L, name)

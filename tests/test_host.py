@@ -37,6 +37,23 @@ def _tiny_specs(Hkv=2):
     return syn.config_mask_specs("tiny", Hkv=Hkv)
 
 
+def test_library_shares_torch_hip_runtime():
+    """Loading libattn.so through the binding, with torch not yet imported,
+    still leaves one HIP runtime and one HSA runtime in the process (torch's):
+    two copies would each claim the GPU, and the second to start finds none."""
+    import subprocess
+    import sys
+    code = (
+        "import long_context_masked_amd._lib as L; L.lib()\n"
+        "names = set(l.split()[-1] for l in open('/proc/self/maps')\n"
+        "            if 'libamdhip64' in l or 'libhsa-runtime64' in l)\n"
+        "print(len([n for n in names if 'amdhip64' in n]), len([n for n in names if 'hsa-runtime' in n]))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == ["1", "1"], r.stdout
+
+
 @pytest.mark.parametrize("label,spec", _tiny_specs(), ids=[l for l, _ in _tiny_specs()])
 def test_nnz_matches_oracle_popcount(label, spec):
     Hq, Hkv = 4, 2
