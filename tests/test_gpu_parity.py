@@ -24,17 +24,26 @@ if not torch.cuda.is_available():  # pragma: no cover
 import long_context_masked_amd as lcm  # noqa: E402
 
 
-def run_case(spec, B, Hq, Hkv, d, seed=0, check_bwd=True):
+def run_case(spec, B, Hq, Hkv, d, seed=0, check_bwd=True, x=None, bwd_on_oracle_o=False):
+    """Forward and backward against the oracle.  With bwd_on_oracle_o the
+    backward takes the oracle's bf16 O and fp32 LSE in place of the GPU's,
+    so that D = rowsum(dO * O) comes from the same O on both sides."""
     S = spec["S"]
-    x = syn.attention_inputs(B, S, Hq, Hkv, d, seed)
+    if x is None:
+        x = syn.attention_inputs(B, S, Hq, Hkv, d, seed)
     q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
     plan = lcm.Plan(B, S, Hq, Hkv, d, spec)
     o, lse = lcm.fwd(plan, q, k, v)
-    if check_bwd:
-        dq, dk, dv = lcm.bwd(plan, q, k, v, o, lse, do)
-    torch.cuda.synchronize()
     qf, kf, vf, dof = (f64(x[n]) for n in ("q", "k", "v", "do"))
     ref = ora.backward(qf, kf, vf, dof, spec, o_for_d="bf16", magnitudes=True)
+    if check_bwd:
+        if bwd_on_oracle_o:
+            o_b = torch.from_numpy(ora.round_bf16(ref["o"]).astype(np.float32)).to(torch.bfloat16).cuda()
+            lse_b = torch.from_numpy(ref["lse"].astype(np.float32)).cuda()
+        else:
+            o_b, lse_b = o, lse
+        dq, dk, dv = lcm.bwd(plan, q, k, v, o_b, lse_b, do)
+    torch.cuda.synchronize()
     gate("O", to_f64(o), ref["o"], ref["m_o"])
     lg = lse.cpu().numpy().astype(np.float64)
     lr = ref["lse"]
@@ -127,6 +136,37 @@ def test_empty_rows_and_keys():
     bits = np.array([[[1, 0, 1, 0], [0, 0, 0, 0], [1, 0, 1, 0], [0, 0, 0, 1]]], dtype=np.uint8)
     spec = syn.with_bitmap(syn.spec_full(S), offs, offs, bits)
     run_case(spec, 1, 2, 1, 64, seed=9)
+
+
+def _bf16_bits(a):
+    return syn.bf16_bits_from_f32(np.asarray(a, dtype=np.float32))
+
+
+@pytest.mark.parametrize("label,spec,Hq,Hkv,d", [
+    ("full_gqa", syn.spec_full(700), 8, 1, 128), ("causal_gqa", syn.spec_causal(700), 8, 1, 128),
+    ("full_mha", syn.spec_full(333), 2, 2, 128), ("causal_d64", syn.spec_causal(512), 4, 2, 64)])
+def test_forward_rescales_when_later_keys_score_far_higher(label, spec, Hq, Hkv, d):
+    """Rows whose later keys score tens to hundreds of log2 units above
+    everything in the first key tile they read, so that the forward's running
+    maximum moves past its slack and O and the row sum are rescaled (N(0, 1)
+    inputs never get there).  Two constructions: keys late in the sequence
+    along the sign pattern of one query row, and a first key tile that scores
+    far below the rest for every row.  O and LSE are checked; the backward
+    does not use the running maximum."""
+    S = spec["S"]
+    x = syn.attention_inputs(1, S, Hq, Hkv, d, seed=21)
+    q, k = f64(x["q"]), f64(x["k"])
+    for j, r in ((S - 5, 3), (S // 2 + 7, S - 1)):
+        k[0, j] = 4.0 * np.sign(q[0, r, 0] + 1e-3)
+    x["k"] = _bf16_bits(k)
+    run_case(spec, 1, Hq, Hkv, d, x=x, check_bwd=False)
+    rng = np.random.default_rng(22)
+    u = np.sign(rng.standard_normal(d)) * 2.0
+    q2 = u + 0.25 * rng.standard_normal((1, S, Hq, d))
+    k2 = f64(x["k"]).copy()
+    k2[0, :64] = -4.0 * np.sign(u) + 0.5 * rng.standard_normal((64, Hkv, d))
+    x2 = dict(x, q=_bf16_bits(q2), k=_bf16_bits(k2))
+    run_case(spec, 1, Hq, Hkv, d, x=x2, check_bwd=False)
 
 
 def test_forward_is_deterministic():
