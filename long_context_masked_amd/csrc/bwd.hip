@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   constexpr int OFF_DO = T::BYTES, OFF_L = 2 * T::BYTES, OFF_D = OFF_L + 256;
   constexpr int STAGE = 2 * T::BYTES + 1024;
   constexpr int NBUF = 3;
+  constexpr int PF = KS < 4 ? KS : 4;  // k-steps of A operands read ahead
   static_assert(16 % KS == 0 && 8 % KS == 0 && 16 % NC == 0 && 8 % NC == 0, "chunking");
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
 
@@ -297,15 +298,16 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   // The first operand rows and the LSE rows of a stage's phase 1 are read
   // during the previous stage's phase 3b (stage 0: here).
   f32x4 l0n[4];
-  bf16x8 aqn[2], aon[2];
+  bf16x8 aqn[PF], aon[PF];
   {
     const float *sl0 = reinterpret_cast<const float *>(smem + OFF_L) + 4 * hh;
 #pragma unroll
     for (int c = 0; c < 4; ++c) l0n[c] = *reinterpret_cast<const f32x4 *>(sl0 + 8 * c);
-    aqn[0] = rows_q(smem, 1, 0);
-    aon[0] = rows_o(smem, 1, 0);
-    aqn[1] = rows_q(smem, 1, 1);
-    aon[1] = rows_o(smem, 1, 1);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      aqn[i] = rows_q(smem, 1, i);
+      aon[i] = rows_o(smem, 1, i);
+    }
   }
   for (int st = 0; st < nst; ++st) {
     const uint32_t ent2 = st + 2 < nst ? list[(st + 2) / G] : 0u;  // stage st + 2
@@ -335,10 +337,11 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) l0[c] = l0n[c];
     bf16x8 aq[KS], ao[KS];
-    aq[0] = aqn[0];
-    ao[0] = aon[0];
-    aq[1] = aqn[1];
-    ao[1] = aon[1];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      aq[i] = aqn[i];
+      ao[i] = aon[i];
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- phase 1: A(st, 1) with the exponentials of B(st, 0)
@@ -347,9 +350,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     s16x4 xa[4 * DB], xb[4 * DB];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 2 < KS) {
-        aq[ks + 2] = rows_q(buf, 1, ks + 2);
-        ao[ks + 2] = rows_o(buf, 1, ks + 2);
+      if (ks + PF < KS) {
+        aq[ks + PF] = rows_q(buf, 1, ks + PF);
+        ao[ks + PF] = rows_o(buf, 1, ks + PF);
       }
       if (ks == KS / 2) {
 #pragma unroll
@@ -402,10 +405,11 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     dma_wait();
     __syncthreads();
     if (st + 2 < nst) load_stage(st + 2, smem + fre * STAGE, ent2);
-    aq[0] = rows_q(nbuf, 0, 0);
-    ao[0] = rows_o(nbuf, 0, 0);
-    aq[1] = rows_q(nbuf, 0, 1);
-    ao[1] = rows_o(nbuf, 0, 1);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      aq[i] = rows_q(nbuf, 0, i);
+      ao[i] = rows_o(nbuf, 0, i);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- phase 3a: A(st + 1, 0) with the exponentials of B(st, 1) rows 8-15
@@ -413,9 +417,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     f32x16 sa0 = s_first(aq[0], pn, mwn[0]), dpa0 = neg_d(nbuf, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 2 < KS) {
-        aq[ks + 2] = rows_q(nbuf, 0, ks + 2);
-        ao[ks + 2] = rows_o(nbuf, 0, ks + 2);
+      if (ks + PF < KS) {
+        aq[ks + PF] = rows_q(nbuf, 0, ks + PF);
+        ao[ks + PF] = rows_o(nbuf, 0, ks + PF);
       }
       if (ks > 0) sa0 = mfma32(aq[ks], kv[ks], sa0);
       dpa0 = mfma32(ao[ks], vv[ks], dpa0);
@@ -450,10 +454,11 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
         const float *sln = reinterpret_cast<const float *>(nbuf + OFF_L) + 4 * hh;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) l0n[q4] = *reinterpret_cast<const f32x4 *>(sln + 8 * q4);
-        aqn[0] = rows_q(nbuf, 1, 0);
-        aon[0] = rows_o(nbuf, 1, 0);
-        aqn[1] = rows_q(nbuf, 1, 1);
-        aon[1] = rows_o(nbuf, 1, 1);
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+          aqn[i] = rows_q(nbuf, 1, i);
+          aon[i] = rows_o(nbuf, 1, i);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
