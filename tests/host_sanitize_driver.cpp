@@ -6,10 +6,13 @@
 // buffer with memcpy, the launches only check their plan.  Exit status 0 and
 // no sanitizer report mean that every plan lifecycle below ran clean.
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <string>
+#include <thread>
 #include <vector>
 
 #include "attn.h"
@@ -36,7 +39,7 @@ extern "C" attn_status attn_bwd(const attn_plan *plan, const void *, const void 
 
 namespace {
 
-int g_fail = 0;
+std::atomic<int> g_fail{0};
 volatile uint64_t g_sink = 0;  // keeps the blob reads below from being optimised away
 #define EXPECT(c)                                                         \
   do {                                                                    \
@@ -259,9 +262,63 @@ void desc_cache() {
   attn_desc_release(nullptr);
 }
 
+// Several threads share the descriptor cache: lookups, uploads into their
+// own buffers, launches, releases and (one thread) cache clears, plus plan
+// creation and the thread-local error string.  Run under ThreadSanitizer.
+void threads() {
+  constexpr int NT = 4, IT = 150, NMASK = 40;
+  std::vector<std::thread> ts;
+  std::vector<int> fails(NT, 0);
+  for (int t = 0; t < NT; ++t)
+    ts.emplace_back([t, &fails] {
+      uint64_t r = 0x1234567ull + (uint64_t)t * 0x9e3779b97f4a7c15ull;
+      auto next = [&r] {
+        r = r * 6364136223846793005ull + 1442695040888963407ull;
+        return (uint32_t)(r >> 33);
+      };
+      alignas(256) static thread_local uint8_t qkv[4096];
+      std::vector<uint8_t> buf_store, ws_store;
+      for (int it = 0; it < IT; ++it) {
+        const int i = (int)(next() % NMASK);
+        attn_shape sh{1, 150 + i, 4, 2, 64, 0.f};
+        attn_mask_desc m = blank(ATTN_MASK_SLIDING);
+        m.causal = 1;
+        m.window_left = 9 + i;
+        size_t pb = 0, wb = 0;
+        if (attn_desc_plan_bytes(&sh, &m, &pb, &wb, nullptr) != ATTN_OK) { ++fails[t]; continue; }
+        buf_store.assign(pb + 256, 0);
+        ws_store.assign(wb + 512, 0);
+        uint8_t *buf = buf_store.data() + ((256 - ((uintptr_t)buf_store.data() & 255)) & 255);
+        uint8_t *w = ws_store.data() + ((256 - ((uintptr_t)ws_store.data() & 255)) & 255);
+        if (attn_fwd_desc(&sh, &m, qkv, qkv, qkv, qkv, (float *)qkv, buf, pb, nullptr) != ATTN_OK) ++fails[t];
+        if (attn_bwd_desc(&sh, &m, qkv, qkv, qkv, qkv, (const float *)qkv, qkv, qkv, qkv, qkv, w, wb,
+                          buf, pb, nullptr) != ATTN_OK)
+          ++fails[t];
+        attn_desc_release(buf);  // the buffer is freed or reused next
+        // an invalid call sets this thread's error string only
+        attn_shape bad{1, 100, 4, 3, 64, 0.f};
+        attn_plan *p = nullptr;
+        if (attn_plan_create(&bad, &m, &p) != ATTN_ERR_INVALID) ++fails[t];
+        const std::string e = attn_last_error();
+        if (e.empty()) ++fails[t];
+        if (make(1, 64 + i, 4, 2, 64, blank(ATTN_MASK_CAUSAL), false) != ATTN_OK) ++fails[t];
+        if (t == 0 && it % 37 == 36) attn_desc_cache_clear();
+      }
+    });
+  for (auto &th : ts) th.join();
+  for (int t = 0; t < NT; ++t) EXPECT(fails[t] == 0);
+  attn_desc_cache_clear();
+}
+
 }  // namespace
 
-int main() {
+int main(int argc, char **argv) {
+  if (argc > 1 && std::string(argv[1]) == "threads") {
+    threads();
+    if (g_fail) return 1;
+    std::printf("host sanitizer driver: threads clean\n");
+    return 0;
+  }
   EXPECT(attn_version() != nullptr);
   const int64_t shapes[][4] = {{1, 2, 2, 64},   {65, 4, 2, 64},  {128, 3, 1, 64},
                                {333, 2, 2, 128}, {700, 8, 1, 128}, {1024, 8, 2, 128},
@@ -270,7 +327,7 @@ int main() {
   errors();
   desc_cache();
   if (g_fail) {
-    std::fprintf(stderr, "%d expectation(s) failed\n", g_fail);
+    std::fprintf(stderr, "%d expectation(s) failed\n", g_fail.load());
     return 1;
   }
   std::printf("host sanitizer driver: all plan lifecycles clean\n");
