@@ -1,4 +1,5 @@
-"""HIP graph capture of the forward and backward (GPU).
+"""HIP graph capture of the forward and backward, and one plan shared by two
+streams (GPU).
 
 Once a plan is bound, attn_fwd and attn_bwd only launch kernels on the given
 stream (no allocation, no memset, no synchronisation), so a caller can
@@ -80,3 +81,36 @@ def test_captured_forward_backward_replays_match_eager(label, spec, Hq, Hkv, d):
     torch.cuda.synchronize()
     for n, got, want in zip(names, outs, ref2):
         assert torch.equal(got, want), f"replay on new inputs: {n} differs from the eager result"
+
+
+def test_one_plan_on_two_streams_at_once():
+    """A bound plan is read-only on the device, so two streams may use it at
+    the same time: forward + backward on two streams concurrently, each
+    against its own sequential result."""
+    S, Hq, Hkv, d = 1024, 8, 2, 128
+    spec = syn.spec_causal(S)
+    plan = lcm.Plan(1, S, Hq, Hkv, d, spec)
+    ins = []
+    for seed in (41, 42):
+        x = syn.attention_inputs(1, S, Hq, Hkv, d, seed=seed)
+        ins.append(tuple(to_dev(x[n], torch) for n in ("q", "k", "v", "do")))
+    plan.bind(ins[0][0].device)
+
+    def step(q, k, v, do):
+        o, lse = lcm.fwd(plan, q, k, v)
+        return (o, lse) + tuple(lcm.bwd(plan, q, k, v, o, lse, do))
+
+    ref = [[t.clone() for t in step(*x)] for x in ins]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        for s, x in zip(streams, ins):
+            with torch.cuda.stream(s):
+                outs.append((step(*x), s))
+    torch.cuda.synchronize()
+    for i, (got, s) in enumerate(outs):
+        for n, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), got, ref[i % 2]):
+            assert torch.equal(a, b), f"launch {i}: {n} differs from the sequential result"
