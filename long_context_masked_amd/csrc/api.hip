@@ -7,10 +7,11 @@
 #include "plan.hpp"
 
 namespace lcm {
-hipError_t launch_fwd(const FwdArgs &a, int d, int HG, int n_items, int B, hipStream_t st);
+hipError_t launch_fwd(const FwdArgs &a, int d, int HG, bool masked, int n_items, int B,
+                      hipStream_t st);
 hipError_t launch_bwd_pre(const BwdArgs &a, int d, int B, hipStream_t st);
 hipError_t launch_dkdv(const BwdArgs &a, int d, int B, hipStream_t st);
-hipError_t launch_dq(const BwdArgs &a, int d, int HG, int B, hipStream_t st);
+hipError_t launch_dq(const BwdArgs &a, int d, int HG, bool masked, int B, hipStream_t st);
 hipError_t launch_merge(const float *o1, const float *lse1, const float *o2, const float *lse2,
                         void *o, bool o_bf16, float *lse, int64_t B, int S, int Hq, int d,
                         hipStream_t st);
@@ -57,6 +58,10 @@ bool forced_device_error() {
   const char *e = std::getenv("ATTN_FORCE_DEVICE_ERROR");
   return e && e[0] == '1';
 }
+
+// Whether the forward / dQ lists can hold partial tiles: those of a dynamic
+// plan change with every bitmap, the others are fixed at creation.
+bool masked_lists(const attn_plan *p) { return p->dyn.on || p->stats.fwd_tiles_partial > 0; }
 
 attn_status check_plan(const attn_plan *p) {
   if (!p) return fail(ATTN_ERR_INVALID, "plan is NULL");
@@ -169,7 +174,7 @@ attn_status fwd_impl(const attn_plan *p, const void *q, const void *k, const voi
   a.list = sect<uint32_t>(p, p->lay.fwd_list);
   a.m = mask_args(p);
   (void)hipGetLastError();
-  const hipError_t e = launch_fwd(a, (int)p->shape.d, p->HG, (int)p->lay.n_fwd_items,
+  const hipError_t e = launch_fwd(a, (int)p->shape.d, p->HG, masked_lists(p), (int)p->lay.n_fwd_items,
                                   (int)p->shape.B, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;
@@ -304,7 +309,7 @@ extern "C" attn_status attn_bwd_dq(const attn_plan *p, const void *q, const void
   if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
   const BwdArgs a = bwd_args(p, q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, ws);
   (void)hipGetLastError();
-  return launched(launch_dq(a, (int)p->shape.d, p->HG, (int)p->shape.B,
+  return launched(launch_dq(a, (int)p->shape.d, p->HG, masked_lists(p), (int)p->shape.B,
                             reinterpret_cast<hipStream_t>(stream)), "dQ");
 }
 
@@ -331,7 +336,7 @@ extern "C" attn_status attn_bwd(const attn_plan *p, const void *q, const void *k
   (void)hipGetLastError();
   LCM_CHECK(launched(launch_bwd_pre(a, d, B, st), "backward preprocess"));
   LCM_CHECK(launched(launch_dkdv(a, d, B, st), "dK/dV"));
-  return launched(launch_dq(a, d, p->HG, B, st), "dQ");
+  return launched(launch_dq(a, d, p->HG, masked_lists(p), B, st), "dQ");
 }
 
 extern "C" attn_status attn_merge(const float *o1, const float *lse1, const float *o2,

@@ -539,7 +539,8 @@ __global__ __launch_bounds__(256) void attn_dkdv_reduce_kernel(BwdArgs a) {
 // transposed reads.  Each K-tile is processed as two 32-key halves:
 //   S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - D),  dQ^T += K^T dS^T
 // ---------------------------------------------------------------------------
-template <int D, int HG>
+// MASKED = false drops the partial-tile path (plans without partial tiles).
+template <int D, int HG, bool MASKED>
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -624,7 +625,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
     constexpr int BUF = decltype(bufc)::value;
     const uint32_t ent = list[e];
     const int kt = (int)(ent & 0x7fffffffu);
-    const bool partial = (ent >> 31) != 0;
+    const bool partial = MASKED && (ent >> 31) != 0;
     char *stage = smem + BUF * STAGE;
     if (e + 1 < n) {
       const int nkt = (int)(list[e + 1] & 0x7fffffffu);
@@ -727,10 +728,14 @@ template __global__ void attn_dkdv_kernel<128>(BwdArgs);
 template __global__ void attn_dkdv_kernel<64>(BwdArgs);
 template __global__ void attn_dkdv_reduce_kernel<128>(BwdArgs);
 template __global__ void attn_dkdv_reduce_kernel<64>(BwdArgs);
-template __global__ void attn_dq_kernel<128, 2>(BwdArgs);
-template __global__ void attn_dq_kernel<128, 1>(BwdArgs);
-template __global__ void attn_dq_kernel<64, 2>(BwdArgs);
-template __global__ void attn_dq_kernel<64, 1>(BwdArgs);
+#define LCM_DQ(D, HG)                                             \
+  template __global__ void attn_dq_kernel<D, HG, true>(BwdArgs);  \
+  template __global__ void attn_dq_kernel<D, HG, false>(BwdArgs);
+LCM_DQ(128, 2)
+LCM_DQ(128, 1)
+LCM_DQ(64, 2)
+LCM_DQ(64, 1)
+#undef LCM_DQ
 
 hipError_t launch_bwd_pre(const BwdArgs &a, int d, int B, hipStream_t st) {
   const int64_t nrows = (int64_t)B * a.S64 * a.Hq;
@@ -759,12 +764,18 @@ hipError_t launch_dkdv(const BwdArgs &a, int d, int B, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_dq(const BwdArgs &a, int d, int HG, int B, hipStream_t st) {
-  const dim3 grid((unsigned)a.n_fitems, (unsigned)B), block(256);
-  if (d == 128 && HG == 2) hipLaunchKernelGGL((attn_dq_kernel<128, 2>), grid, block, 0, st, a);
-  else if (d == 128 && HG == 1) hipLaunchKernelGGL((attn_dq_kernel<128, 1>), grid, block, 0, st, a);
-  else if (d == 64 && HG == 2) hipLaunchKernelGGL((attn_dq_kernel<64, 2>), grid, block, 0, st, a);
-  else if (d == 64 && HG == 1) hipLaunchKernelGGL((attn_dq_kernel<64, 1>), grid, block, 0, st, a);
+template <int D, int HG>
+static void launch_dq_masked(const BwdArgs &a, bool masked, dim3 grid, hipStream_t st) {
+  if (masked) hipLaunchKernelGGL((attn_dq_kernel<D, HG, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_dq_kernel<D, HG, false>), grid, dim3(256), 0, st, a);
+}
+
+hipError_t launch_dq(const BwdArgs &a, int d, int HG, bool masked, int B, hipStream_t st) {
+  const dim3 grid((unsigned)a.n_fitems, (unsigned)B);
+  if (d == 128 && HG == 2) launch_dq_masked<128, 2>(a, masked, grid, st);
+  else if (d == 128 && HG == 1) launch_dq_masked<128, 1>(a, masked, grid, st);
+  else if (d == 64 && HG == 2) launch_dq_masked<64, 2>(a, masked, grid, st);
+  else if (d == 64 && HG == 1) launch_dq_masked<64, 1>(a, masked, grid, st);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -32,7 +32,9 @@
 
 namespace lcm {
 
-template <int D, int HG>
+// MASKED = false drops the partial-tile path, for plans whose lists hold no
+// partial tile (the code and registers it takes cost full tiles 1-2%).
+template <int D, int HG, bool MASKED>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int KS = D / 16;   // k-steps of QK^T
   constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     const uint32_t ent = list[e];
     mw[0] = 0xffffffffu;
     mw[1] = 0xffffffffu;
-    const bool part = (ent >> 31) != 0;
+    const bool part = MASKED && (ent >> 31) != 0;
     if (part) {
       const uint64_t mk = row_ok ? row_mask(a.m, rb, qb, hm, (int)(ent & 0x7fffffffu) * 64, S) : 0ull;
       const uint64_t sh = mk >> (4 * hh);
@@ -432,17 +434,28 @@ hipError_t launch_merge(const float *o1, const float *lse1, const float *o2, con
 
 // Every variant is instantiated explicitly: implicit instantiation from the
 // launcher alone has left some host-side launch stubs unemitted.
-template __global__ void attn_fwd_kernel<128, 2>(FwdArgs);
-template __global__ void attn_fwd_kernel<128, 1>(FwdArgs);
-template __global__ void attn_fwd_kernel<64, 2>(FwdArgs);
-template __global__ void attn_fwd_kernel<64, 1>(FwdArgs);
+#define LCM_FWD(D, HG)                                              \
+  template __global__ void attn_fwd_kernel<D, HG, true>(FwdArgs);  \
+  template __global__ void attn_fwd_kernel<D, HG, false>(FwdArgs);
+LCM_FWD(128, 2)
+LCM_FWD(128, 1)
+LCM_FWD(64, 2)
+LCM_FWD(64, 1)
+#undef LCM_FWD
 
-hipError_t launch_fwd(const FwdArgs &a, int d, int HG, int n_items, int B, hipStream_t st) {
-  const dim3 grid((unsigned)n_items, (unsigned)B), block(256);
-  if (d == 128 && HG == 2) hipLaunchKernelGGL((attn_fwd_kernel<128, 2>), grid, block, 0, st, a);
-  else if (d == 128 && HG == 1) hipLaunchKernelGGL((attn_fwd_kernel<128, 1>), grid, block, 0, st, a);
-  else if (d == 64 && HG == 2) hipLaunchKernelGGL((attn_fwd_kernel<64, 2>), grid, block, 0, st, a);
-  else if (d == 64 && HG == 1) hipLaunchKernelGGL((attn_fwd_kernel<64, 1>), grid, block, 0, st, a);
+template <int D, int HG>
+static void launch_fwd_masked(const FwdArgs &a, bool masked, dim3 grid, hipStream_t st) {
+  if (masked) hipLaunchKernelGGL((attn_fwd_kernel<D, HG, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, HG, false>), grid, dim3(256), 0, st, a);
+}
+
+hipError_t launch_fwd(const FwdArgs &a, int d, int HG, bool masked, int n_items, int B,
+                      hipStream_t st) {
+  const dim3 grid((unsigned)n_items, (unsigned)B);
+  if (d == 128 && HG == 2) launch_fwd_masked<128, 2>(a, masked, grid, st);
+  else if (d == 128 && HG == 1) launch_fwd_masked<128, 1>(a, masked, grid, st);
+  else if (d == 64 && HG == 2) launch_fwd_masked<64, 2>(a, masked, grid, st);
+  else if (d == 64 && HG == 1) launch_fwd_masked<64, 1>(a, masked, grid, st);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
