@@ -49,6 +49,8 @@ class Plan:
         self._dev = None
         self._dev_index = None
         self._dev_off = 0
+        # bumped by set_bitmap: a backward must see the mask its forward saw
+        self.bitmap_generation = 0
 
     @property
     def handle(self):
@@ -92,6 +94,7 @@ class Plan:
         stream = torch.cuda.current_stream(bits.device).cuda_stream
         L.check(L.lib().attn_plan_set_bitmap(self._h, C.c_void_p(bits.data_ptr()),
                                              C.c_void_p(stream)))
+        self.bitmap_generation += 1
         return self
 
     def layout(self):
@@ -341,13 +344,17 @@ def desc_cache_clear():
 
 def attention(q, k, v, plan):
     """Differentiable masked attention through torch.autograd; ``plan`` is a
-    Plan or a mask spec / MaskDescriptor (then the plan cache is used)."""
+    Plan or a mask spec / MaskDescriptor (then the plan cache is used).  A
+    dynamic plan whose bitmap is replaced between the forward and the
+    backward raises in the backward instead of differentiating another
+    mask."""
     import torch
 
     class _Attn(torch.autograd.Function):
         @staticmethod
         def forward(ctx, q_, k_, v_):
             if isinstance(plan, Plan):
+                ctx.generation = plan.bitmap_generation
                 o, lse = fwd(plan, q_, k_, v_)
             else:
                 o, lse = fwd_desc(q_, k_, v_, plan)
@@ -358,6 +365,9 @@ def attention(q, k, v, plan):
         def backward(ctx, do):
             q_, k_, v_, o, lse = ctx.saved_tensors
             if isinstance(plan, Plan):
+                if plan.bitmap_generation != ctx.generation:
+                    raise RuntimeError("the plan's bitmap was replaced (set_bitmap) after the forward; "
+                                       "the backward would differentiate another mask")
                 return bwd(plan, q_, k_, v_, o, lse, do.contiguous())
             return bwd_desc(q_, k_, v_, o, lse, do.contiguous(), plan)
 

@@ -3,9 +3,11 @@ mask compiler, one shared library next to this file."""
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
+import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -40,8 +42,69 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
+# Sources whose kernels issue transposed LDS reads as inline assembly.
+TR_READ_SOURCES = ["fwd.hip", "bwd.hip"]
+
+
+def _vregs(operand):
+    m = re.match(r"v\[(\d+):(\d+)\]$", operand)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", operand)
+    return {int(m.group(1))} if m else set()
+
+
+def uses_of_pending_reads(asm_text):
+    """(kernel, line, instruction) for every instruction that names a register
+    whose transposed LDS read has not yet been waited for.
+
+    The kernels issue ds_read_b64_tr_b16 as inline assembly and wait for it
+    with an explicit s_waitcnt lgkmcnt(0) that names the destination
+    registers.  The compiler takes an asm output as written when the
+    instruction issues, so under register pressure it may spill such a
+    register, copy it or reuse it as a temporary before the data has
+    arrived; the read then lands on other values or the kernel consumes
+    stale data.  Nothing in the source prevents this: it depends on each
+    build's register allocation.  A linear scan of each kernel's text (the
+    reads and their waits sit in straight-line code)."""
+    found, pending, kernel = [], set(), None
+    for n, line in enumerate(asm_text.split("\n"), 1):
+        t = line.strip()
+        m = re.match(r"^(_Z\w+):", t)
+        if m:
+            kernel, pending = m.group(1), set()
+            continue
+        if not t or t.startswith((";", ".")):
+            continue
+        parts = t.split(None, 1)
+        op = parts[0]
+        operands = [a.strip().split()[0] for a in parts[1].split(",") if a.strip()] if len(parts) > 1 else []
+        if op == "ds_read_b64_tr_b16":
+            pending |= _vregs(operands[0])
+            continue
+        if op == "s_endpgm" or (op == "s_waitcnt" and "lgkmcnt(0)" in t):
+            pending = set()
+            continue
+        if pending and any(_vregs(a) & pending for a in operands):
+            found.append((kernel, n, t))
+    return found
+
+
+def scan_transposed_reads(asm_by_source):
+    """Raise if a compiled kernel touches a register of an in-flight
+    transposed read (see uses_of_pending_reads)."""
+    for src, text in asm_by_source.items():
+        if "ds_read_b64_tr_b16" not in text:
+            raise RuntimeError(f"{src}: no transposed reads compiled")
+        found = uses_of_pending_reads(text)
+        if found:
+            raise RuntimeError(f"{src}: {len(found)} uses of in-flight transposed reads, e.g. "
+                               + "; ".join(f"{k} line {n}: {i}" for k, n, i in found[:3]))
+
+
 def build(verbose: bool = False, extra_hip_flags=()) -> str:
-    """Compile every source and link libattn.so; returns the library path."""
+    """Compile every source, check the compiled transposed LDS reads, and link
+    libattn.so; returns the library path."""
     os.makedirs(OUT_DIR, exist_ok=True)
     jobs = []
     for s in HIP_SOURCES:
@@ -51,8 +114,18 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
     for s in CXX_SOURCES:
         o = os.path.join(OUT_DIR, s + ".o")
         jobs.append([cxx, *CXX_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
-    with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
-        list(ex.map(lambda c: _run(c, verbose), jobs))
+    with tempfile.TemporaryDirectory() as tmp:
+        asm = {s: os.path.join(tmp, s + ".s") for s in TR_READ_SOURCES}
+        for s, out in asm.items():
+            jobs.append([HIPCC, *HIP_FLAGS, *extra_hip_flags, "--cuda-device-only", "-S",
+                         os.path.join(CSRC, s), "-o", out])
+        with ThreadPoolExecutor(max_workers=min(6, len(jobs))) as ex:
+            list(ex.map(lambda c: _run(c, verbose), jobs))
+        texts = {}
+        for s, out in asm.items():
+            with open(out) as f:
+                texts[s] = f.read()
+    scan_transposed_reads(texts)
     objs = [os.path.join(OUT_DIR, s + ".o") for s in HIP_SOURCES + CXX_SOURCES]
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)

@@ -121,6 +121,68 @@ def round_bf16(x):
     return np.ldexp(r / 256.0, e)
 
 
+def _sensitivities(p, ds, o, do, q, k, v, scale, cols=None, rows=True):
+    """First-order sensitivities of one row block's outputs to relative
+    perturbations of the intermediate values that a tiled kernel rounds.
+
+    Rows i of the block (one query head), keys j of the whole sequence.  The
+    perturbations, each a relative change of one value (|.| <= u when the
+    value is rounded to a format with unit roundoff u):
+
+      delta_ij  the unnormalised probability p~_ij whose sum normalises the
+                forward: O_i = sum_j p~_ij v_j / sum_j p~_ij, and
+                LSE_i = m_i + ln sum_j p~_ij (so LSE_i moves by
+                sum_j p_ij delta_ij and the backward's P_ij = exp(S_ij - LSE_i)
+                by minus that);
+      eps_id    the element O_id handed to the backward, which forms
+                D_i = sum_d dO_id O_id from it;
+      eta_ij    P_ij where it enters dV_j = sum_i P_ij dO_i;
+      eta'_ij   dS_ij where it enters dK_j = scale sum_i dS_ij q_i;
+      eta''_ij  dS_ij where it enters dQ_i = scale sum_j dS_ij k_j.
+
+    To first order every output x moves by sum_t c_t e_t over these
+    perturbations e_t; this returns the 2-norm sqrt(sum_t c_t^2) of the
+    coefficient vector of every output element: for O (delta only), LSE,
+    dQ, and the squared norms of this block's contributions to dK and dV
+    (summed over row blocks and query heads by the caller; over every key,
+    or over the key indices ``cols`` when given, False for none; the row
+    outputs are left out when ``rows`` is False).  The
+    closed forms below follow from D' = D + sum_j dS_ij delta_ij + sum_d dO_id O_id eps_id
+    (since p_ij sum_d dO_id (v_jd - O_id) = dS_ij) and
+    dS'_ij = P'_ij (dP_ij - D'_i); with the row sums
+      A_i = sum_j p_ij^2, B_i = sum_j p_ij dS_ij, C_i = sum_j dS_ij^2,
+      E_i = sum_d (dO_id O_id)^2, kbar_i = sum_j p_ij k_j:
+      |c(O_id)|^2   = sum_j p_ij^2 (v_jd - O_id)^2
+      |c(LSE_i)|^2  = A_i
+      |c(dQ_id)|^2  = dQ_id^2 A_i + 2 scale dQ_id kbar_id B_i
+                      + scale^2 kbar_id^2 (C_i + E_i) + scale^2 sum_j dS_ij^2 k_jd^2
+      |c(dK_jd)|^2  = scale^2 sum_i q_id^2 (dS_ij^2 (A_i + 1) + 2 dS_ij p_ij B_i
+                                             + p_ij^2 (C_i + E_i))
+      |c(dV_jd)|^2  = sum_i p_ij^2 dO_id^2 (1 + A_i).
+    """
+    p2 = p * p
+    A = p2.sum(axis=1)
+    B = (p * ds).sum(axis=1)
+    C = (ds * ds).sum(axis=1)
+    E = ((do * o) ** 2).sum(axis=1)
+    out = {"lse": np.sqrt(A)}
+    if rows:
+        m_o2 = p2 @ (v * v) - 2.0 * o * (p2 @ v) + o * o * A[:, None]
+        dq = (ds @ k) * scale
+        kbar = p @ k
+        m_dq2 = (dq * dq * A[:, None] + 2.0 * scale * dq * kbar * B[:, None]
+                 + scale * scale * kbar * kbar * (C + E)[:, None]
+                 + scale * scale * ((ds * ds) @ (k * k)))
+        out["o"] = np.sqrt(np.maximum(m_o2, 0.0))
+        out["dq"] = np.sqrt(np.maximum(m_dq2, 0.0))
+    if cols is not False:
+        pc, dsc = (p, ds) if cols is None else (p[:, cols], ds[:, cols])
+        w = dsc * dsc * (A + 1.0)[:, None] + 2.0 * dsc * pc * B[:, None] + pc * pc * (C + E)[:, None]
+        out["dk2"] = np.maximum((w.T @ (q * q)) * scale * scale, 0.0)
+        out["dv2"] = (pc * pc * (1.0 + A)[:, None]).T @ (do * do)
+    return out
+
+
 def backward(q, k, v, do, spec, scale=None, kv_heads=None, row_block=512,
              o_for_d="exact", magnitudes=False):
     """dQ, dK, dV (and O, LSE) for the selected KV heads and their groups.
@@ -130,14 +192,12 @@ def backward(q, k, v, do, spec, scale=None, kv_heads=None, row_block=512,
     and ``heads``, the query head indices covered.
 
     ``o_for_d``: the O entering D_i = dO_i . O_i.  "exact" uses the exact
-    output; "bf16" uses it rounded to bfloat16, i.e. the O a caller holds when
-    the forward returns bf16 and the backward receives that O back.
+    output; "bf16" uses it rounded to bfloat16.
 
-    ``magnitudes``: also return, per output element x = sum_t a_t b_t of each
-    product (O = P V, dV = P^T dO, dQ = scale dS K, dK = scale dS^T Q), the
-    quadratic magnitude sqrt(sum_t (a_t b_t)^2) under keys "m_o", "m_dv",
-    "m_dq", "m_dk".  It sets the size of the error a product makes when one
-    of its operands is rounded to a narrower format term by term.
+    ``magnitudes``: also return the first-order sensitivity of every output
+    element to relative perturbations of the intermediate values a tiled
+    kernel rounds (see ``_sensitivities``): "m_o", "m_dq", "m_dk", "m_dv"
+    (same shapes as the outputs) and "m_lse" ([B, G*n, S]).
     """
     B, S, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -158,6 +218,7 @@ def backward(q, k, v, do, spec, scale=None, kv_heads=None, row_block=512,
         m_dq = np.zeros_like(dq)
         m_dk2 = np.zeros_like(dk)
         m_dv2 = np.zeros_like(dv)
+        m_lse = np.zeros_like(lse)
     for b in range(B):
         for hi, h in enumerate(heads):
             kvi = hi // G
@@ -182,14 +243,15 @@ def backward(q, k, v, do, spec, scale=None, kv_heads=None, row_block=512,
                 dk[b, :, kvi, :] += (ds.T @ qi) * scale
                 dv[b, :, kvi, :] += p.T @ doi
                 if magnitudes:
-                    p2, ds2 = p * p, ds * ds
-                    m_o[b, i0:i1, hi, :] = np.sqrt(p2 @ (vv * vv))
-                    m_dq[b, i0:i1, hi, :] = np.sqrt(ds2 @ (kk * kk)) * scale
-                    m_dk2[b, :, kvi, :] += (ds2.T @ (qi * qi)) * scale * scale
-                    m_dv2[b, :, kvi, :] += p2.T @ (doi * doi)
+                    sv = _sensitivities(p, ds, oi, doi, qi, kk, vv, scale)
+                    m_o[b, i0:i1, hi, :] = sv["o"]
+                    m_dq[b, i0:i1, hi, :] = sv["dq"]
+                    m_lse[b, hi, i0:i1] = sv["lse"]
+                    m_dk2[b, :, kvi, :] += sv["dk2"]
+                    m_dv2[b, :, kvi, :] += sv["dv2"]
     out = {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": lse, "heads": heads}
     if magnitudes:
-        out.update(m_o=m_o, m_dq=m_dq, m_dk=np.sqrt(m_dk2), m_dv=np.sqrt(m_dv2))
+        out.update(m_o=m_o, m_dq=m_dq, m_dk=np.sqrt(m_dk2), m_dv=np.sqrt(m_dv2), m_lse=m_lse)
     return out
 
 
@@ -219,8 +281,8 @@ def grad_rows(q, k, v, do, spec, h, rows, scale=None, o_for_d="exact"):
     """dQ, O and LSE of query head ``h`` for an arbitrary set of rows only
     (batch 0).  Every quantity a row's dQ needs is local to the row: its
     probabilities p_ij, D_i = dO_i . O_i and dP_ij = dO_i . v_j.  Returns
-    dq [len(rows), d], o [len(rows), d], lse [len(rows)] and the quadratic
-    magnitudes m_dq, m_o of the two products (see ``backward``)."""
+    dq [len(rows), d], o [len(rows), d], lse [len(rows)] and the
+    sensitivities m_dq, m_o, m_lse (see ``backward``)."""
     B, S, Hq, d = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
@@ -231,18 +293,77 @@ def grad_rows(q, k, v, do, spec, h, rows, scale=None, o_for_d="exact"):
     vv = v[0, :, kv, :]
     out = {n: np.zeros((len(rows), d)) for n in ("dq", "o", "m_dq", "m_o")}
     out["lse"] = np.zeros(len(rows))
+    out["m_lse"] = np.zeros(len(rows))
     for r, i in enumerate(rows):
         s = (kk @ q[0, i, h, :]) * scale
         p, l = _probs(s[None, :], masks.allowed(spec, i, i + 1, hm))
-        p = p[0]
         oi = p @ vv
         od = oi if o_for_d == "exact" else round_bf16(oi)
-        Di = float(do[0, i, h, :] @ od)
-        dp = vv @ do[0, i, h, :]
+        doi = do[0, i:i + 1, h, :]
+        Di = float(doi[0] @ od[0])
+        dp = doi @ vv.T
         ds = p * (dp - Di)
-        out["dq"][r] = (ds @ kk) * scale
-        out["o"][r] = oi
+        out["dq"][r] = (ds @ kk)[0] * scale
+        out["o"][r] = oi[0]
         out["lse"][r] = l[0]
-        out["m_dq"][r] = np.sqrt((ds * ds) @ (kk * kk)) * scale
-        out["m_o"][r] = np.sqrt((p * p) @ (vv * vv))
+        sv = _sensitivities(p, ds, oi, doi, q[0, i:i + 1, h, :], kk, vv, scale, cols=False)
+        out["m_dq"][r] = sv["dq"][0]
+        out["m_o"][r] = sv["o"][0]
+        out["m_lse"][r] = sv["lse"][0]
+    return out
+
+
+def grad_cols(q, k, v, do, spec, kv_head, cols, scale=None, row_block=512, heads=None):
+    """dK and dV of KV head ``kv_head`` for chosen key columns only (batch 0),
+    with their sensitivities m_dk, m_dv (see ``backward``).
+
+    dK_j = scale sum_{h, i} dS_ij q_i and dV_j = sum_{h, i} P_ij dO_i over the
+    query heads h of the group and the rows i allowed to attend to j.  Such a
+    row's P_ij, D_i = dO_i . O_i and the row sums of the sensitivities need
+    its whole score row, so exactly those rows are formed in full, in row
+    blocks, each over the keys that some row of the block may attend to
+    (P is zero on every other key); only the chosen columns' terms are
+    accumulated.  ``heads``: only these query heads of the group contribute
+    (default: all of them; squared sensitivities add over heads).  Returns
+    dk, dv, m_dk, m_dv [len(cols), d] and ``pairs``, the number of (row, key)
+    scores formed."""
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    cols = np.asarray(cols, dtype=np.int64)
+    out = {n: np.zeros((len(cols), d)) for n in ("dk", "dv", "m_dk", "m_dv")}
+    all_j = np.arange(S, dtype=np.int64)[None, :]
+    pairs = 0
+    for h in (range(kv_head * G, kv_head * G + G) if heads is None else heads):
+        assert h // G == kv_head
+        hm = masks.mask_head(spec, h, Hq, Hkv)
+        rows = np.nonzero(masks.pred(spec, np.arange(S)[:, None], cols[None, :], hm).any(axis=1))[0]
+        for r0 in range(0, len(rows), row_block):
+            ri = rows[r0:r0 + row_block]
+            a = masks.pred(spec, ri[:, None], all_j, hm)
+            keys = np.nonzero(a.any(axis=0))[0]      # keys some row of the block sees
+            a = a[:, keys]
+            pairs += a.size
+            kk = k[0, keys, kv_head, :]
+            vv = v[0, keys, kv_head, :]
+            qi = q[0, ri, h, :]
+            doi = do[0, ri, h, :]
+            p, _ = _probs((qi @ kk.T) * scale, a)
+            oi = p @ vv
+            D = (doi * oi).sum(axis=1)
+            ds = p * (doi @ vv.T - D[:, None])
+            at = np.searchsorted(keys, cols)          # chosen columns among the block's keys
+            seen = (at < len(keys)) & (keys[np.minimum(at, len(keys) - 1)] == cols)
+            if not seen.any():
+                continue
+            sel = at[seen]
+            out["dk"][seen] += (ds[:, sel].T @ qi) * scale
+            out["dv"][seen] += p[:, sel].T @ doi
+            sv = _sensitivities(p, ds, oi, doi, qi, kk, vv, scale, cols=sel, rows=False)
+            out["m_dk"][seen] += sv["dk2"]
+            out["m_dv"][seen] += sv["dv2"]
+    out["m_dk"] = np.sqrt(out["m_dk"])
+    out["m_dv"] = np.sqrt(out["m_dv"])
+    out["pairs"] = pairs
     return out

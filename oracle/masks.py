@@ -11,8 +11,9 @@ DOCUMENT, BLOCK CAUSAL DOCUMENT) and two dynamic block masks (uniform, e.g.
 below states the reading it takes.  ``i`` is the query row, ``j`` the key
 column, both in [0, S) of one packed sequence (Sq = Sk = S).
 
-Every function returns a boolean array ``allowed[i - i0, j]`` for the rows
-[i0, i1) and all S columns.
+``pred`` evaluates the predicate on any broadcastable integer arrays of rows
+``i`` and columns ``j``; ``allowed`` returns ``allowed[i - i0, j]`` for the
+rows [i0, i1) and all S columns.
 """
 from __future__ import annotations
 
@@ -27,16 +28,17 @@ def _doc_starts(doc_lens):
     return np.concatenate([[0], np.cumsum(doc_lens)[:-1]]).astype(np.int64)
 
 
-def base_allowed(spec, i0, i1):
-    """allowed[i-i0, j] for the base family of ``spec`` (no bitmap)."""
+def base_pred(spec, i, j):
+    """mask(i, j) of the base family of ``spec`` (no bitmap), for int64
+    arrays of rows i and columns j that broadcast against each other."""
     S = int(spec["S"])
-    i = np.arange(i0, i1, dtype=np.int64)[:, None]
-    j = np.arange(S, dtype=np.int64)[None, :]
+    i = np.asarray(i, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
     fam = spec["family"]
 
     if fam == "full":
         # FULL: every key is visible.
-        return np.ones((i1 - i0, S), dtype=bool)
+        return np.ones(np.broadcast_shapes(i.shape, j.shape), dtype=bool)
 
     if fam == "causal":
         # CAUSAL with Sq = Sk: keys up to and including the query position.
@@ -54,7 +56,7 @@ def base_allowed(spec, i0, i1):
         # DOCUMENT (packed variable-length sequences): a token sees only its
         # own document; CAUSAL DOCUMENT additionally requires j <= i.
         doc = _doc_ids(spec["doc_lens"])
-        same = doc[i0:i1][:, None] == doc[None, :]
+        same = doc[i] == doc[j]
         return same & (j <= i) if spec["causal"] else same
 
     if fam == "prefix_lm_causal":
@@ -70,7 +72,7 @@ def base_allowed(spec, i0, i1):
         q = int(spec["question"])
         lens = [q] + list(spec["answers"])
         seg = _doc_ids(lens)            # 0 = question, k = answer k
-        same = seg[i0:i1][:, None] == seg[None, :]
+        same = seg[i] == seg[j]
         return (j <= i) & ((j < q) | same)
 
     if fam == "global_sliding":
@@ -102,8 +104,8 @@ def base_allowed(spec, i0, i1):
         doc = _doc_ids(lens)
         start = _doc_starts(lens)
         pre = np.asarray(spec["prefix_lens"], dtype=np.int64)
-        di = doc[i0:i1][:, None]
-        same = di == doc[None, :]
+        di = doc[i]
+        same = di == doc[j]
         return same & ((j < start[di] + pre[di]) | (j <= i))
 
     if fam == "block_causal_document":
@@ -115,8 +117,8 @@ def base_allowed(spec, i0, i1):
         start = _doc_starts(lens)
         pos = np.arange(S, dtype=np.int64) - start[doc]
         blk = pos // b
-        same = doc[i0:i1][:, None] == doc[None, :]
-        return same & (blk[None, :] <= blk[i0:i1][:, None])
+        same = doc[i] == doc[j]
+        return same & (blk[j] <= blk[i])
 
     if fam == "task_batch":
         # TASK BATCH: token-level core-attention tasks fused into one launch
@@ -133,25 +135,25 @@ def base_allowed(spec, i0, i1):
         start = _doc_starts(lens)
         end = start + np.asarray(lens, dtype=np.int64)
         ql = np.asarray(spec["q_lens"], dtype=np.int64)
-        si = seg[i0:i1][:, None]
-        same = si == seg[None, :]
+        si = seg[i]
+        same = si == seg[j]
         return same & (j <= i) & (i >= end[si] - ql[si])
 
     raise ValueError(f"unknown mask family {fam!r}")
 
 
-def bitmap_allowed(bitmap, hm, i0, i1, S):
-    """allowed[i-i0, j] = bits[hm][qblk(i)][kblk(j)] for a block bitmap.
+def bitmap_pred(bitmap, hm, i, j):
+    """bits[hm][qblk(i)][kblk(j)] of a block bitmap, for broadcastable int64
+    arrays of rows i and columns j.
 
     Uniform or variable-size blocks (page 1 section 3, dynamic masks): the
     block of a position is the b with offsets[b] <= x < offsets[b+1].
     """
     qo = np.asarray(bitmap["q_offsets"], dtype=np.int64)
     ko = np.asarray(bitmap["k_offsets"], dtype=np.int64)
-    qb = np.searchsorted(qo, np.arange(i0, i1), side="right") - 1
-    kb = np.searchsorted(ko, np.arange(S), side="right") - 1
-    bits = bitmap["bits"][hm]
-    return bits[qb][:, kb].astype(bool)
+    qb = np.searchsorted(qo, np.asarray(i, dtype=np.int64), side="right") - 1
+    kb = np.searchsorted(ko, np.asarray(j, dtype=np.int64), side="right") - 1
+    return bitmap["bits"][hm][qb, kb].astype(bool)
 
 
 def mask_head(spec, h, Hq, Hkv):
@@ -168,12 +170,20 @@ def mask_head(spec, h, Hq, Hkv):
     raise ValueError("bitmap head count must be 1, Hkv or Hq")
 
 
-def allowed(spec, i0, i1, hm=0):
-    """Full predicate rows [i0, i1): base family AND the optional bitmap."""
-    a = base_allowed(spec, i0, i1)
+def pred(spec, i, j, hm=0):
+    """The full predicate, base family AND the optional bitmap, for
+    broadcastable int64 arrays of rows i and columns j."""
+    a = base_pred(spec, i, j)
     if "bitmap" in spec:
-        a = a & bitmap_allowed(spec["bitmap"], hm, i0, i1, int(spec["S"]))
+        a = a & bitmap_pred(spec["bitmap"], hm, i, j)
     return a
+
+
+def allowed(spec, i0, i1, hm=0):
+    """Full predicate rows [i0, i1) over all S columns."""
+    i = np.arange(i0, i1, dtype=np.int64)[:, None]
+    j = np.arange(int(spec["S"]), dtype=np.int64)[None, :]
+    return pred(spec, i, j, hm)
 
 
 def dense_mask(spec, hm=0):

@@ -115,15 +115,15 @@ def L_layout(plan):
 
 
 def _oracle_check(plan, spec, B, Hq, Hkv, d, seed, x=None):
-    """Forward against the oracle's O and LSE; backward run on the oracle's
-    bf16 O and fp32 LSE (so that D = rowsum(dO * O) is formed from the same
-    O on both sides) against the oracle's gradients."""
+    """Forward, then the backward chained on the forward's own O and LSE (the
+    product path), against the oracle's O, LSE and gradients."""
     S = spec["S"]
     x = syn.attention_inputs(B, S, Hq, Hkv, d, seed) if x is None else x
     q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
     qf, kf, vf, dof = (f64(x[n]) for n in ("q", "k", "v", "do"))
-    ref = ora.backward(qf, kf, vf, dof, spec, o_for_d="bf16", magnitudes=True)
+    ref = ora.backward(qf, kf, vf, dof, spec, magnitudes=True)
     o, lse = lcm.fwd(plan, q, k, v)
+    dq, dk, dv = lcm.bwd(plan, q, k, v, o, lse, do)
     torch.cuda.synchronize()
     gate("O", to_f64(o), ref["o"], ref["m_o"])
     lg = lse.cpu().numpy().astype(np.float64)
@@ -131,14 +131,10 @@ def _oracle_check(plan, spec, B, Hq, Hkv, d, seed, x=None):
     assert (np.isneginf(lg) == ~fin).all()
     if fin.any():
         assert np.abs(lg[fin] - ref["lse"][fin]).max() <= 5e-3
-    o_r = torch.from_numpy(ora.round_bf16(ref["o"]).astype(np.float32)).to(torch.bfloat16).cuda()
-    lse_r = torch.from_numpy(ref["lse"].astype(np.float32)).cuda()
-    dq, dk, dv = lcm.bwd(plan, q, k, v, o_r, lse_r, do)
-    torch.cuda.synchronize()
     gate("dQ", to_f64(dq), ref["dq"], ref["m_dq"])
     gate("dK", to_f64(dk), ref["dk"], ref["m_dk"])
     gate("dV", to_f64(dv), ref["dv"], ref["m_dv"])
-    return (q, k, v, do), (o, lse, o_r, lse_r, dq)
+    return (q, k, v, do), (o, lse, dq, dk, dv)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -154,16 +150,13 @@ def test_set_bitmap_rebuilds_host_lists_and_matches_oracle(case):
     dyn.set_bitmap(_dev_bits(b2, scale=5))          # any nonzero byte is "on"
     static2 = _check_lists_equal(dyn, spec2, B, Hq, Hkv, d, b2)
     _check_bits_section(dyn, b2)
-    (q, k, v, do), (o, lse, o_r, lse_r, dq) = _oracle_check(dyn, spec2, B, Hq, Hkv, d, seed=3)
-    # same lists and per-item arithmetic as the ordinary plan for b2, also
-    # with the backward chained on the forward's own O and LSE
+    (q, k, v, do), (o, lse, dq, dk, dv) = _oracle_check(dyn, spec2, B, Hq, Hkv, d, seed=3)
+    # same lists and per-item arithmetic as the ordinary plan for b2 (whose
+    # dK/dV items may be split, so dK/dV may differ in the last bits)
     o2, lse2 = lcm.fwd(static2, q, k, v)
-    dq2, _, _ = lcm.bwd(static2, q, k, v, o_r, lse_r, do)
-    dq3, _, _ = lcm.bwd(dyn, q, k, v, o, lse, do)
-    dq4, _, _ = lcm.bwd(static2, q, k, v, o2, lse2, do)
+    dq2, _, _ = lcm.bwd(static2, q, k, v, o2, lse2, do)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(dq, dq2)
-    assert torch.equal(dq3, dq4)
 
 
 @pytest.mark.parametrize("case", CASES[:3], ids=[c[0] for c in CASES[:3]])
@@ -222,6 +215,24 @@ def test_set_bitmap_argument_errors():
     inside = dyn._dev.data_ptr() + dyn._dev_off   # the plan's own buffer
     assert L.lib().attn_plan_set_bitmap(dyn.handle, C.c_void_p(inside), None) == L.ATTN_ERR_INVALID
     assert b"overlaps" in L.lib().attn_last_error()
+
+
+def test_autograd_refuses_a_bitmap_replaced_after_the_forward():
+    """attention() on a dynamic plan: the backward raises if set_bitmap ran
+    after the forward, and runs when the bitmap is the forward's."""
+    label, base, qo, ko, Hq, Hkv, d, heads = CASES[0]
+    b1 = _bits(qo, ko, heads, 0.5, seed=51)
+    b2 = _bits(qo, ko, heads, 0.5, seed=52)
+    dyn = lcm.Plan(1, base["S"], Hq, Hkv, d, dict(syn.with_bitmap(base, qo, ko, b1), dynamic=True))
+    x = syn.attention_inputs(1, base["S"], Hq, Hkv, d, 53)
+    q, k, v, do = (to_dev(x[n], torch).requires_grad_(n != "do") for n in ("q", "k", "v", "do"))
+    o = lcm.attention(q, k, v, dyn)
+    o.backward(do)
+    torch.cuda.synchronize()
+    o = lcm.attention(q, k, v, dyn)
+    dyn.set_bitmap(_dev_bits(b2))
+    with pytest.raises(RuntimeError, match="set_bitmap"):
+        o.backward(do)
 
 
 @pytest.mark.parametrize("blk,heads", [(64, 8), (128, 64)], ids=["block64_per_kv_head", "block128_per_query_head"])

@@ -11,8 +11,14 @@ At these sizes the fp64 oracle cannot run whole tensors, so the tests check:
   from the oracle's predicate) and O_i the mean of the allowed v_j (beyond
   S = 64K on sampled blocks of rows, and with more than 2 bitmap heads on
   the first and last, to keep the oracle's count within seconds);
-* the identity sum_j dV_j = sum over query rows of the group of dO_i, which
-  holds at any size because every probability row sums to one;
+* sampled key columns of dK and dV, which the oracle computes from the full
+  score rows of only the rows that see those keys (tests/fullsize_cases.py
+  picks them within a cost budget), against the same gate, on both the
+  unsplit dK/dV items (bf16 written by the pass itself) and the split ones
+  (fp32 partials summed by the reduce pass);
+* the identities sum_j dV_j = sum over query rows of the group of dO_i and
+  sum_j dK_j = 0 per KV head, which hold at any size because every
+  probability row sums to one (softmax is invariant to a shift of the keys);
 * uniform V: O = v, dQ = dK = 0.
 """
 import numpy as np
@@ -23,6 +29,7 @@ from oracle import attention as ora
 from oracle import masks as om
 
 from gpu_util import f64, gate, to_dev, to_f64
+from fullsize_cases import Lazy64, col_cases, grad_cols_parallel, pick_cols
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -41,17 +48,6 @@ def inputs(S, Hkv):
         x = syn.attention_inputs(1, S, HQ, Hkv, D, seed=0)
         _INPUTS[(S, Hkv)] = (x, {n: to_dev(x[n], torch) for n in x})
     return _INPUTS[(S, Hkv)]
-
-
-class Lazy64:
-    """Array view that widens bf16 bits to float64 only where indexed."""
-
-    def __init__(self, bits):
-        self.bits = bits
-        self.shape = bits.shape
-
-    def __getitem__(self, idx):
-        return f64(self.bits[idx])
 
 
 def _cases():
@@ -116,7 +112,7 @@ def test_sampled_rows(label, spec, Hkv):
     got = {"o": [], "dq": [], "lse": []}
     ref = {"o": [], "dq": [], "lse": [], "m_o": [], "m_dq": []}
     for h in (0, 7, 33, 63):
-        r = ora.grad_rows(lz["q"], lz["k"], lz["v"], lz["do"], spec, h, rows, o_for_d="bf16")
+        r = ora.grad_rows(lz["q"], lz["k"], lz["v"], lz["do"], spec, h, rows)
         for n in ref:
             ref[n].append(r[n])
         got["o"].append(to_f64(o[0, rows, h]))
@@ -137,6 +133,10 @@ def test_sampled_rows(label, spec, Hkv):
     err = (dvs - dos).abs().max().item()
     assert err <= 1e-2 * np.sqrt(S * HQ / Hkv), err
     assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    # sum_j dK_j = 0 per KV head: softmax is invariant to adding one vector
+    # to every key, so the loss has zero derivative along that direction
+    dks = dk[0].to(torch.float64).sum(dim=0).abs().max().item()
+    assert dks <= 1e-2 * np.sqrt(S * HQ / Hkv), dks
 
 
 @pytest.mark.parametrize("label,spec,Hkv", CASES, ids=IDS)
@@ -192,3 +192,37 @@ def test_uniform_v_closed_form(label, spec, Hkv):
     assert (o[0].to(torch.float32) - want[None]).abs().max().item() <= 2.0 ** -7 * want.abs().max().item()
     assert dq.abs().max().item() <= 1e-3
     assert dk.abs().max().item() <= 1e-3
+
+
+COLS = col_cases()
+
+
+@pytest.mark.parametrize("label,spec,Hkv,kvs,budget,extra,row_block", COLS, ids=[c[0] for c in COLS])
+def test_sampled_key_columns(label, spec, Hkv, kvs, budget, extra, row_block):
+    """dK and dV of sampled key columns, chained on the forward's own O and
+    LSE, against the oracle; the columns cover unsplit dK/dV items and, where
+    the plan splits items, split ones."""
+    S = spec["S"]
+    x, t = inputs(S, Hkv)
+    plan = lcm.Plan(1, S, HQ, Hkv, D, spec)
+    o, lse = lcm.fwd(plan, t["q"], t["k"], t["v"])
+    dq, dk, dv = lcm.bwd(plan, t["q"], t["k"], t["v"], o, lse, t["do"])
+    torch.cuda.synchronize()
+    cols = {kv: pick_cols(spec, HQ, Hkv, kv, budget, extra=extra) for kv in kvs}
+    assert all(len(c) > 0 for c in cols.values()), cols
+    lay = plan.layout()
+    items, slots = lay["bwd_items"], lay["bwd_slot"]
+    paths = set()
+    for kv, cs in cols.items():
+        for c in cs:
+            sel = (items[:, 0] == c // 128) & (items[:, 1] == kv)
+            paths.add("split" if (slots[sel] >= 0).any() else "direct")
+    assert "direct" in paths or slots.max() >= 0, paths
+    print(f"{label}: columns {cols}, dK/dV paths {sorted(paths)}", flush=True)
+    ref = grad_cols_parallel(x, spec, HQ, Hkv, kvs, cols, row_block)
+    got = {n: np.concatenate([to_f64(g[0, cols[kv], kv]) for kv in kvs]) for n, g in (("dk", dk), ("dv", dv))}
+    rf = {n: np.concatenate([ref[kv][n] for kv in kvs]) for n in ("dk", "dv", "m_dk", "m_dv")}
+    gate("dK", got["dk"], rf["dk"], rf["m_dk"], quiet=False)
+    gate("dV", got["dv"], rf["dv"], rf["m_dv"], quiet=False)
+    if label == "hetero32K_global_sliding":
+        assert "split" in paths, paths

@@ -58,7 +58,7 @@ def test_merged_forward_matches_whole_mask(label, base, cuts, B, Hq, Hkv, d):
     x, t, plans, o, lse = _run(base, cuts, B, Hq, Hkv, d)
     torch.cuda.synchronize()
     qf, kf, vf, dof = (f64(x[n]) for n in ("q", "k", "v", "do"))
-    ref = ora.backward(qf, kf, vf, dof, base, o_for_d="bf16", magnitudes=True)
+    ref = ora.backward(qf, kf, vf, dof, base, magnitudes=True)
     gate("O", to_f64(o), ref["o"], ref["m_o"])
     lg = lse.cpu().numpy().astype(np.float64)
     fin = np.isfinite(ref["lse"])
@@ -96,7 +96,7 @@ def test_chunked_backward_sums_to_whole_mask(label, base, cuts, B, Hq, Hkv, d):
         dq, dk, dv = (g if dq is None else (dq + g[0], dk + g[1], dv + g[2]))
     torch.cuda.synchronize()
     qf, kf, vf, dof = (f64(x[n]) for n in ("q", "k", "v", "do"))
-    ref = ora.backward(qf, kf, vf, dof, base, o_for_d="bf16", magnitudes=True)
+    ref = ora.backward(qf, kf, vf, dof, base, magnitudes=True)
     tf = lambda a: a.cpu().numpy().astype(np.float64)
     gate("dQ", tf(dq), ref["dq"], ref["m_dq"])
     gate("dK", tf(dk), ref["dk"], ref["m_dk"])
