@@ -44,8 +44,11 @@ COPY_KERNEL_HINT = "copy"
 
 # Algorithmic work per allowed (i, j) pair per query head, in units of d
 # flops, of each kernel: forward = Q K^T + P V; dK/dV pass = Q K^T, dO V^T,
-# P^T dO, dS^T Q; dQ pass = Q K^T, dO V^T, dS K.
+# P^T dO, dS^T Q; dQ pass = Q K^T, dO V^T, dS K.  With dQ accumulated in the
+# dK/dV pass (attn_bwd_atomic_dq) the whole backward is timed as one
+# interval of five products (the "dkdv" entry).
 KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dkdv": 8, "dq": 6}
+KERNEL_FLOPS_PER_PAIR_FUSED = {"fwd": 4, "dkdv": 10, "dq": 0}
 # MFMA-busy fraction and shader clock of the three main kernels, from one
 # rocprofv3 --pmc pass (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE) over a bench
 # step, stored in MFMA_FILE with a hash of the kernels' sources, as for traffic.
@@ -96,14 +99,16 @@ def workload(name, seqs):
             for Hkv, heads in ((8, "gqa"), (64, "mha")):
                 for label, spec in syn.config_mask_specs("sparse", S, Hq=64, Hkv=Hkv):
                     out.append((f"S{S // 1024}K_{heads}_{label}", S, 64, Hkv, spec))
-        # one bitmap per query head under GQA
-        offs, bits = syn.uniform_block_bitmap(seqs[0], 128, 64, 0.5, 1)
-        out.append((f"S{seqs[0] // 1024}K_gqa_perhead_block128_50", seqs[0], 64, 8,
-                    syn.with_bitmap(syn.spec_full(seqs[0]), offs, offs, bits)))
         desc = ("block-sparse masks: B=1, d=128, S in {" + ", ".join(f"{s // 1024}K" for s in seqs)
                 + "} x {GQA 64:8, MHA 64:64}, bitmap per KV head at 50% density, uniform 64/128 and "
-                  f"variable blocks; plus a bitmap per query head under GQA (128 blocks, "
-                  f"{seqs[0] // 1024}K), fwd+bwd")
+                  "variable blocks")
+        if seqs[0] <= 32768:
+            # one bitmap per query head under GQA
+            offs, bits = syn.uniform_block_bitmap(seqs[0], 128, 64, 0.5, 1)
+            out.append((f"S{seqs[0] // 1024}K_gqa_perhead_block128_50", seqs[0], 64, 8,
+                        syn.with_bitmap(syn.spec_full(seqs[0]), offs, offs, bits)))
+            desc += f"; plus a bitmap per query head under GQA (128 blocks, {seqs[0] // 1024}K)"
+        desc += ", fwd+bwd"
     else:
         raise SystemExit(f"unknown workload {name}")
     return out, desc
@@ -293,10 +298,23 @@ def traffic_for(desc):
     return t.get("bytes_per_launch")
 
 
-def summarize_mfma(csv_path, workload_desc, commands):
-    """Per main kernel: the MFMA-busy fraction (busy cycles over all SIMDs
-    divided by the active clocks of one XCD times the SIMD count) and the
-    shader clock (active clocks of one XCD over the dispatch durations)."""
+def _workload_nnz(name, seqs):
+    """nnz per case of a workload, from host-only plan creation (no GPU)."""
+    import long_context_masked_amd as lcm
+    cases, _ = workload(name, seqs)
+    return [(label, lcm.Plan(1, S, Hq, Hkv, 128, spec).stats["nnz_total"]) for label, S, Hq, Hkv, spec in cases]
+
+
+def summarize_mfma(csv_path, workload_name, seqs, workload_desc, commands):
+    """Per main kernel, all from one counter run of one bench step: the
+    MFMA-busy fraction (busy cycles over all SIMDs divided by the active
+    clocks of one XCD times the SIMD count), the shader clock (active clocks
+    of one XCD over the dispatch durations), the algorithmic rate of the same
+    dispatches (their cases' nnz times the kernel's flops per pair, over the
+    summed dispatch durations) and that rate as a fraction of the MFMA peak
+    at the measured clock.  Dispatch k of a kernel belongs to case k mod n
+    (the bench launches the cases in order, once per step)."""
+    nnz = [n for _, n in _workload_nnz(workload_name, seqs)]
     disp = {}
     with open(csv_path) as f:
         for r in csv.DictReader(f):
@@ -305,15 +323,26 @@ def summarize_mfma(csv_path, workload_desc, commands):
             e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     out = {"workload": workload_desc, "commands": commands, "sources": MFMA_SOURCES,
            "source_sha256": sources_sha256(MFMA_SOURCES), "kernels": {}}
+    # the separate dQ pass ran only if its kernel was dispatched
+    fused = not any(MFMA_KERNELS["dq"] in k for (k, _) in disp)
+    fpp = KERNEL_FLOPS_PER_PAIR_FUSED if fused else KERNEL_FLOPS_PER_PAIR
+    out["backward"] = "fused" if fused else "separate"
     for short, name in MFMA_KERNELS.items():
-        rows = [e for (k, _), e in disp.items() if name in k]
+        rows = [e for (k, did), e in sorted(disp.items(), key=lambda kv: kv[0][1])
+                if name in k and "reduce" not in k]
         if not rows:
+            if short == "dq" and fused:
+                continue
             raise SystemExit(f"{csv_path}: no {name} dispatches")
         clk = sum(e["GRBM_GUI_ACTIVE"] for e in rows) / N_XCD   # cycles, per XCD
         busy = sum(e["SQ_VALU_MFMA_BUSY_CYCLES"] for e in rows)
         ns = sum(e["t"] for e in rows)
+        flops = sum(fpp[short] * 128 * nnz[i % len(nnz)] for i in range(len(rows)))
+        ghz = clk / ns
+        rate = flops / ns / 1e3                                 # TFLOP/s
         out["kernels"][short] = {"dispatches": len(rows), "mfma_busy_frac": round(busy / (clk * N_SIMD), 4),
-                                 "clock_GHz": round(clk / ns, 3),
+                                 "clock_GHz": round(ghz, 3), "alg_tflops": round(rate, 1),
+                                 "frac_at_clock": round(rate / (N_CU * BF16_FLOP_PER_CLK_CU * ghz / 1e3), 4),
                                  "mfma_insts": sum(e.get("SQ_INSTS_MFMA", 0.0) for e in rows)}
     return out
 
@@ -331,96 +360,75 @@ def mfma_for(desc):
     return t["kernels"]
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="dense", choices=["dense", "document", "hetero", "sparse", "variants", "tasks"])
-    ap.add_argument("--seqs", default=None,
-                    help="comma-separated sequence lengths (dense: default 1024,8192,16384,49152; "
-                         "sparse: default 32768,131072; ignored by document and hetero)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dynamic", action="store_true",
-                    help="sparse workload: skip the dynamic block-sparse (device list rebuild) figures")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="run one plain device copy of this size before warmup (counter scale)")
-    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the traffic file from two counter runs and exit (no GPU)")
-    ap.add_argument("--traffic-commands", default="", help="commands recorded in the traffic file")
-    ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
-                    help="write the MFMA counter file from one counter run and exit (no GPU)")
-    args = ap.parse_args()
-    if args.summarize_mfma:
-        seqs = [int(x) for x in args.seqs.split(",") if x] if args.seqs else []
-        _, desc = workload(args.workload, seqs)
-        t = summarize_mfma(args.summarize_mfma, desc, args.traffic_commands)
-        with open(MFMA_FILE, "w") as f:
-            json.dump(t, f, indent=1)
-        print(json.dumps(t))
-        return
-    if args.summarize_traffic:
-        seqs = [int(x) for x in args.seqs.split(",") if x] if args.seqs else []
-        _, desc = workload(args.workload, seqs)
-        t = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
-                              args.copy_calibration_mib, desc, args.traffic_commands)
-        with open(TRAFFIC_FILE, "w") as f:
-            json.dump(t, f, indent=1)
-        print(json.dumps(t))
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
+# Every configuration of the target under the same clock as the headline:
+# (workload, sequence lengths, warmup steps, timed steps).
+WORKLOADS = [
+    ("document", None, 1, 3),
+    ("hetero", None, 1, 3),
+    ("sparse", [32768], 1, 3),
+    ("sparse", [131072], 1, 2),
+    ("dense", [131072], 1, 2),
+]
 
-    import numpy as np
-    import torch
 
-    import long_context_masked_amd as lcm
-    import synthetic as syn
+class Runner:
+    """Plans, device tensors and timed steps of one workload's cases."""
 
-    dev = torch.device("cuda:0")
-    seqs = [int(x) for x in args.seqs.split(",") if x] if args.seqs else []
-    cases, desc = workload(args.workload, seqs)
-    d = 128
+    def __init__(self, lcm, torch, dev, cases, device_inputs=False, fused=False):
+        import ctypes
+        self.lcm, self.torch, self.dev = lcm, torch, dev
+        self.fused = fused
+        self.fpp = KERNEL_FLOPS_PER_PAIR_FUSED if fused else KERNEL_FLOPS_PER_PAIR
+        self.tensors, self.runs, self.plan_secs = {}, [], 0.0
+        self.L = lcm._lib
+        self.lib = self.L.lib()
+        self.P = ctypes.c_void_p
+        self.stream = torch.cuda.current_stream(dev)
+        d = 128
+        for label, S, Hq, Hkv, spec in cases:
+            if (S, Hkv) not in self.tensors:
+                log(f"inputs S={S} Hkv={Hkv}")
+                self.tensors[(S, Hkv)] = self._inputs(S, Hq, Hkv, d, device_inputs)
+            t0 = time.perf_counter()
+            plan = lcm.Plan(1, S, Hq, Hkv, d, spec)
+            self.plan_secs += time.perf_counter() - t0
+            plan.bind(dev)
+            nws = plan.atomic_workspace_bytes() if fused else plan.workspace_bytes()
+            ws = torch.empty(nws + 256, dtype=torch.uint8, device=dev)
+            self.runs.append(dict(label=label, S=S, Hq=Hq, Hkv=Hkv, plan=plan, ws=ws,
+                                  nnz=plan.stats["nnz_total"], events=[]))
+            log(f"plan {label}: nnz {plan.stats['nnz_total']:.4g}, fwd partial tiles "
+                f"{plan.stats['fwd_tiles_partial']}, full {plan.stats['fwd_tiles_full']}")
 
-    def t(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    tensors = {}
-    runs = []
-    plan_secs = 0.0
-    for label, S, Hq, Hkv, spec in cases:
-        if (S, Hkv) not in tensors:
-            log(f"inputs S={S} Hkv={Hkv}")
+    def _inputs(self, S, Hq, Hkv, d, on_device):
+        """Q, K, V, dO ~ N(0, 1) rounded to bf16: from the seeded numpy
+        generator the tests use, or (large shapes) torch's seeded generator
+        on the GPU, which gives the same distribution without the host's
+        minutes of sampling."""
+        torch, dev = self.torch, self.dev
+        if on_device:
+            g = torch.Generator(device=dev).manual_seed(0)
+            mk = lambda h: torch.randn((1, S, h, d), generator=g, device=dev).to(torch.bfloat16)
+            q, k, v, do = mk(Hq), mk(Hkv), mk(Hkv), mk(Hq)
+        else:
+            import numpy as np
+            import synthetic as syn
             x = syn.attention_inputs(1, S, Hq, Hkv, d, seed=0)
+            t = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
             q, k, v, do = t(x["q"]), t(x["k"]), t(x["v"]), t(x["do"])
-            del x
-            tensors[(S, Hkv)] = dict(q=q, k=k, v=v, do=do, o=torch.empty_like(q),
-                              lse=torch.empty((1, Hq, S), dtype=torch.float32, device=dev),
-                              dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
-        t0 = time.perf_counter()
-        plan = lcm.Plan(1, S, Hq, Hkv, d, spec)
-        plan_secs += time.perf_counter() - t0
-        plan.bind(dev)
-        ws = torch.empty(plan.workspace_bytes() + 256, dtype=torch.uint8, device=dev)
-        runs.append(dict(label=label, S=S, Hkv=Hkv, plan=plan, ws=ws, nnz=plan.stats["nnz_total"]))
-        log(f"plan {label}: nnz {plan.stats['nnz_total']:.4g}, fwd partial tiles "
-            f"{plan.stats['fwd_tiles_partial']}, full {plan.stats['fwd_tiles_full']}")
+        return dict(q=q, k=k, v=v, do=do, o=torch.empty_like(q),
+                    lse=torch.empty((1, Hq, S), dtype=torch.float32, device=dev),
+                    dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
 
-    L = lcm._lib
-    lib = L.lib()
-    P = lambda x: __import__("ctypes").c_void_p(x)
-    stream = torch.cuda.current_stream(dev)
-    sp = P(stream.cuda_stream)
-
-    def one_step(record):
-        for r in runs:
-            tt = tensors[(r["S"], r["Hkv"])]
+    def step(self, record):
+        L, lib, P, torch, stream = self.L, self.lib, self.P, self.torch, self.stream
+        sp = P(stream.cuda_stream)
+        for r in self.runs:
+            tt = self.tensors[(r["S"], r["Hkv"])]
             h = r["plan"].handle
             wptr = r["ws"].data_ptr()
             wptr += (-wptr) % 256
-            nws = r["plan"].workspace_bytes()
+            nws = r["plan"].atomic_workspace_bytes() if self.fused else r["plan"].workspace_bytes()
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
             if record:
                 ev[0].record(stream)
@@ -428,6 +436,21 @@ def main():
                                  P(tt["o"].data_ptr()), P(tt["lse"].data_ptr()), sp))
             if record:
                 ev[1].record(stream)
+            if self.fused:
+                # the whole backward with dQ accumulated in the dK/dV pass, timed
+                # as one interval (the "dkdv" split)
+                if record:
+                    ev[2].record(stream)
+                L.check(lib.attn_bwd_atomic_dq(h, P(tt["q"].data_ptr()), P(tt["k"].data_ptr()),
+                                               P(tt["v"].data_ptr()), P(tt["o"].data_ptr()),
+                                               P(tt["lse"].data_ptr()), P(tt["do"].data_ptr()),
+                                               P(tt["dq"].data_ptr()), P(tt["dk"].data_ptr()),
+                                               P(tt["dv"].data_ptr()), P(wptr), nws, sp))
+                if record:
+                    ev[3].record(stream)
+                    ev[4].record(stream)
+                    r["events"].append(ev)
+                continue
             L.check(lib.attn_bwd_preprocess(h, P(tt["o"].data_ptr()), P(tt["lse"].data_ptr()),
                                             P(tt["do"].data_ptr()), P(wptr), nws, sp))
             if record:
@@ -442,7 +465,120 @@ def main():
                                     P(wptr), nws, sp))
             if record:
                 ev[4].record(stream)
-                r.setdefault("events", []).append(ev)
+                r["events"].append(ev)
+
+    def measure(self, steps, warmup):
+        """Warmup steps, then `steps` timed steps between two device
+        synchronisations; kernel splits from the HIP events on the launch
+        stream."""
+        import numpy as np
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        d = 128
+        kern = {"fwd": 0.0, "pre": 0.0, "dkdv": 0.0, "dq": 0.0}
+        alg = {"fwd": 0.0, "dkdv": 0.0, "dq": 0.0}
+        launches = {k: 0 for k in kern}
+        pre_bytes = eff_fwd = eff_bwd = 0.0
+        detail = {}
+        for r in self.runs:
+            ms = np.zeros(4)
+            for ev in r["events"]:
+                ms += [ev[j].elapsed_time(ev[j + 1]) for j in range(4)]
+            n = len(r["events"])
+            for j, key in enumerate(("fwd", "pre", "dkdv", "dq")):
+                kern[key] += ms[j] / 1e3
+                launches[key] += n
+            for key in alg:
+                alg[key] += self.fpp[key] * d * r["nnz"] * n
+            pre_bytes += 2.0 * r["S"] * r["Hq"] * d * 2 * n + 3.0 * r["S"] * r["Hq"] * 4 * n
+            ffl, bfl = 4.0 * d * r["nnz"], 10.0 * d * r["nnz"]
+            eff_fwd += ffl * n
+            eff_bwd += bfl * n
+            detail[r["label"]] = {"fwd_tflops": round(ffl * n / (ms[0] / 1e3) / 1e12, 1),
+                                  "bwd_tflops": round(bfl * n / (ms[1:].sum() / 1e3) / 1e12, 1),
+                                  "fwd_ms": round(ms[0] / n, 3), "bwd_ms": round(ms[1:].sum() / n, 3)}
+            r["events"] = []
+        t_fwd, t_bwd = kern["fwd"], kern["pre"] + kern["dkdv"] + kern["dq"]
+        value = (eff_fwd + eff_bwd) / wall / 1e12
+        return {
+            "value": value, "wall": wall, "kern": kern, "alg": alg, "launches": launches,
+            "fwd_tflops": eff_fwd / t_fwd / 1e12, "bwd_tflops": eff_bwd / t_bwd / 1e12,
+            "kernel_tflops": {k: alg[k] / kern[k] / 1e12 for k in alg if alg[k] > 0},
+            "preprocess_GBps": None if self.fused else pre_bytes / kern["pre"] / 1e9, "detail": detail,
+        }
+
+    def free(self):
+        self.tensors.clear()
+        self.runs.clear()
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def _frac(x):
+    return round(x / PEAK_BF16_TFLOPS, 4)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="dense", choices=["dense", "document", "hetero", "sparse", "variants", "tasks"])
+    ap.add_argument("--seqs", default=None,
+                    help="comma-separated sequence lengths (dense: default 1024,8192,16384,49152; "
+                         "sparse: default 32768,131072; ignored by document and hetero)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd", default="separate", choices=["separate", "atomic"],
+                    help="backward: the separate dQ pass (attn_bwd), or dQ accumulated in the "
+                         "dK/dV pass with fp32 atomics (attn_bwd_atomic_dq, timed as one interval)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="default dense run: skip the timing of the other configurations")
+    ap.add_argument("--no-dynamic", action="store_true",
+                    help="sparse workload: skip the dynamic block-sparse (device list rebuild) figures")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size before warmup (counter scale)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic file from two counter runs and exit (no GPU)")
+    ap.add_argument("--traffic-commands", default="", help="commands recorded in the traffic file")
+    ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
+                    help="write the MFMA counter file from one counter run of one step and exit (no GPU)")
+    args = ap.parse_args()
+    seqs = [int(x) for x in args.seqs.split(",") if x] if args.seqs else []
+    if args.summarize_mfma:
+        _, desc = workload(args.workload, seqs)
+        t = summarize_mfma(args.summarize_mfma, args.workload, seqs, desc, args.traffic_commands)
+        with open(MFMA_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return
+    if args.summarize_traffic:
+        _, desc = workload(args.workload, seqs)
+        t = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
+                              args.copy_calibration_mib, desc, args.traffic_commands)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_masked_amd as lcm
+
+    dev = torch.device("cuda:0")
+    cases, desc = workload(args.workload, seqs)
+    fused = args.bwd == "atomic"
+    run = Runner(lcm, torch, dev, cases, fused=fused)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -454,105 +590,84 @@ def main():
         log(f"calibration copy of {args.copy_calibration_mib} MiB done")
         del src, dst
 
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        one_step(False)
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    kern = {"fwd": 0.0, "pre": 0.0, "dkdv": 0.0, "dq": 0.0}
-    alg = {"fwd": 0.0, "dkdv": 0.0, "dq": 0.0}
-    launches = {"fwd": 0, "dkdv": 0, "dq": 0, "pre": 0}
-    pre_bytes = 0.0
-    detail = {}
-    eff_fwd = eff_bwd = 0.0
-    for r in runs:
-        ms = np.zeros(4)
-        for ev in r["events"]:
-            ms += [ev[j].elapsed_time(ev[j + 1]) for j in range(4)]
-        n = len(r["events"])
-        for j, key in enumerate(("fwd", "pre", "dkdv", "dq")):
-            kern[key] += ms[j] / 1e3
-            launches[key] += n
-        for key in alg:
-            alg[key] += KERNEL_FLOPS_PER_PAIR[key] * d * r["nnz"] * n
-        Hq = 64
-        pre_bytes += 2.0 * r["S"] * Hq * d * 2 * n + 3.0 * r["S"] * Hq * 4 * n
-        ffl, bfl = 4.0 * d * r["nnz"], 10.0 * d * r["nnz"]
-        eff_fwd += ffl * n
-        eff_bwd += bfl * n
-        detail[r["label"]] = {"fwd_tflops": round(ffl * n / (ms[0] / 1e3) / 1e12, 1),
-                              "bwd_tflops": round(bfl * n / (ms[1:].sum() / 1e3) / 1e12, 1),
-                              "fwd_ms": round(ms[0] / n, 3), "bwd_ms": round(ms[1:].sum() / n, 3)}
-    total_flops = eff_fwd + eff_bwd
-    value = total_flops / wall / 1e12
-    t_fwd = kern["fwd"]
-    t_bwd = kern["pre"] + kern["dkdv"] + kern["dq"]
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    m = run.measure(args.steps, args.warmup)
+    kern, alg = m["kern"], m["alg"]
     dom = max(("fwd", "dkdv", "dq"), key=lambda k: kern[k])
     achieved = alg[dom] / kern[dom] / 1e12
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(m["value"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "ms_per_step": round(m["wall"] / args.steps * 1e3, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": desc, "global_batch": 1, "seq_len": max(r["S"] for r in runs),
-                   "cases": [r["label"] for r in runs]},
-        "fraction_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd": {"tflops": round(eff_fwd / t_fwd / 1e12, 2),
-                "fraction_of_peak": round(eff_fwd / t_fwd / 1e12 / PEAK_BF16_TFLOPS, 4)},
-        "bwd": {"tflops": round(eff_bwd / t_bwd / 1e12, 2),
-                "fraction_of_peak": round(eff_bwd / t_bwd / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "preprocess_GBps": round(pre_bytes / kern["pre"] / 1e9, 1)},
-        "kernel_ms_per_launch": {k: round(kern[k] / launches[k] * 1e3, 4) for k in kern},
+        "config": {"workload": desc, "global_batch": 1, "seq_len": max(r["S"] for r in run.runs),
+                   "cases": [r["label"] for r in run.runs]},
+        "fraction_of_peak": _frac(m["value"]),
+        "fwd": {"tflops": round(m["fwd_tflops"], 2), "fraction_of_peak": _frac(m["fwd_tflops"])},
+        "bwd": {"tflops": round(m["bwd_tflops"], 2), "fraction_of_peak": _frac(m["bwd_tflops"]),
+                "preprocess_GBps": m["preprocess_GBps"] and round(m["preprocess_GBps"], 1)},
+        "backward": ("dQ accumulated in the dK/dV pass with fp32 atomics, then converted "
+                     "(attn_bwd_atomic_dq)" if fused else "separate dQ pass (attn_bwd)"),
+        "kernel_ms_per_launch": {k: round(kern[k] / m["launches"][k] * 1e3, 4) for k in kern},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "frac": _frac(achieved),
                      "traffic": traffic_for(desc) if dom == "dkdv" else None},
-        "kernel_tflops": {k: round(alg[k] / kern[k] / 1e12, 2) for k in alg},
-        "plan_build_s": round(plan_secs, 3),
-        "detail": detail,
+        "kernel_tflops": {k: round(v, 2) for k, v in m["kernel_tflops"].items()},
+        "plan_build_s": round(run.plan_secs, 3),
+        "detail": m["detail"],
     }
     mf = mfma_for(desc)
     if mf:
-        # the same kernels against the MFMA peak at the clock they ran at,
-        # beside the counters' MFMA-busy fraction
-        mcnt = {}
-        for key, m in mf.items():
-            peak_clk = N_CU * BF16_FLOP_PER_CLK_CU * m["clock_GHz"] / 1e3
-            ach = alg[key] / kern[key] / 1e12
-            mcnt[key] = {"mfma_busy_frac": m["mfma_busy_frac"], "clock_GHz": m["clock_GHz"],
-                         "peak_at_clock_tflops": round(peak_clk, 1),
-                         "frac_at_clock": round(ach / peak_clk, 4)}
-        out["mfma_counters"] = mcnt
-        out["roofline"]["mfma_busy_frac"] = mcnt[dom]["mfma_busy_frac"]
-        out["roofline"]["frac_at_measured_clock"] = mcnt[dom]["frac_at_clock"]
+        # from one rocprofv3 counter run of one step of this workload (another
+        # process, same sources): MFMA-busy fraction, clock, and that run's
+        # own algorithmic rate against the peak at its clock
+        out["mfma_profile"] = {k: {n: v[n] for n in ("mfma_busy_frac", "clock_GHz", "alg_tflops", "frac_at_clock")
+                                   if n in v} for k, v in mf.items()}
+        out["roofline"]["mfma_busy_frac_profile"] = mf[dom]["mfma_busy_frac"]
+    run.free()
     log("merge of partial results")
     out["merge"] = merge_rate(lcm, torch, dev)
     if args.workload == "sparse" and not args.no_dynamic:
         log("dynamic block-sparse: device list rebuild")
+        dyn_run = Runner(lcm, torch, dev, [])
 
         def tensors_for(S, Hkv):
-            if (S, Hkv) not in tensors:
-                x = syn.attention_inputs(1, S, 64, Hkv, d, seed=0)
-                q, k, v, do = t(x["q"]), t(x["k"]), t(x["v"]), t(x["do"])
-                tensors[(S, Hkv)] = dict(q=q, k=k, v=v, do=do, o=torch.empty_like(q),
-                                         lse=torch.empty((1, 64, S), dtype=torch.float32, device=dev),
-                                         dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
-            return tensors[(S, Hkv)]
+            if (S, Hkv) not in dyn_run.tensors:
+                dyn_run.tensors[(S, Hkv)] = dyn_run._inputs(S, 64, Hkv, 128, True)
+            return dyn_run.tensors[(S, Hkv)]
         out["dynamic"] = dynamic_rebuild(lcm, torch, dev, tensors_for)
+        dyn_run.free()
+    if args.workload == "dense" and not seqs and not args.no_workloads:
+        out["workloads"] = {}
+        for name, wseqs, wwarm, wsteps in WORKLOADS:
+            wcases, wdesc = workload(name, wseqs)
+            key = name + ("_" + "_".join(f"{s // 1024}K" for s in wseqs) if wseqs else "")
+            log(f"workload {key}: {len(wcases)} cases, warmup {wwarm}, {wsteps} timed steps")
+            wr = Runner(lcm, torch, dev, wcases, device_inputs=True, fused=fused)
+            wm = wr.measure(wsteps, wwarm)
+            out["workloads"][key] = {
+                "config": wdesc, "steps": wsteps, "warmup": wwarm,
+                "inputs": "N(0,1) rounded to bf16, torch CUDA generator seed 0",
+                "plan_build_s": round(wr.plan_secs, 2),
+                "tflops": round(wm["value"], 2), "fraction_of_peak": _frac(wm["value"]),
+                "ms_per_step": round(wm["wall"] / wsteps * 1e3, 3),
+                "fwd": {"tflops": round(wm["fwd_tflops"], 2), "fraction_of_peak": _frac(wm["fwd_tflops"])},
+                "bwd": {"tflops": round(wm["bwd_tflops"], 2), "fraction_of_peak": _frac(wm["bwd_tflops"])},
+                "kernel_tflops": {k: round(v, 2) for k, v in wm["kernel_tflops"].items()},
+                "detail": wm["detail"],
+            }
+            log(f"workload {key}: {out['workloads'][key]['tflops']} TFLOP/s "
+                f"(fwd {out['workloads'][key]['fwd']['tflops']}, bwd {out['workloads'][key]['bwd']['tflops']})")
+            wr.free()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline()

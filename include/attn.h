@@ -215,6 +215,10 @@ attn_status attn_plan_get_layout(const attn_plan *plan, attn_plan_layout *out);
  * key columns seen by every row), fp32 partial dK and dV of 128 keys per
  * chunk slot and batch entry. */
 size_t attn_bwd_workspace_bytes(const attn_plan *plan);
+/* Bytes of device workspace attn_bwd_atomic_dq needs: attn_bwd's, then the
+ * fp32 dQ accumulator [B][S rounded up to 64][Hq][d] (4 bytes per element of
+ * dQ: 1.6 GB at S = 48K, Hq = 64, d = 128). */
+size_t attn_bwd_atomic_workspace_bytes(const attn_plan *plan);
 
 /*
  * Forward: O and LSE.  Q-split: one workgroup per (Q-tile, group of query
@@ -226,19 +230,40 @@ attn_status attn_fwd(const attn_plan *plan, const void *q, const void *k,
                      const void *v, void *o, float *lse, attn_stream_t stream);
 
 /*
- * Backward: dQ, dK, dV from Q, K, V, the forward's O and LSE, and dO.
- * Three launches on `stream`: -D, D = rowsum(dO * O), and LSE * log2(e)
- * into `ws`; a KV-split pass
- * (one workgroup per K-tile and KV head) accumulating dK and dV; a Q-split
- * pass accumulating dQ = scale * sum_j dS_ij K_j (the row/column two-axis
- * split of FlashAttention-2, "core optimisations").  dK and dV of a KV head
- * are summed over its query-head group.  `ws` is a device buffer of at least
+ * Backward: dQ, dK, dV from Q, K, V, the forward's O and LSE, and dO.  The
+ * dependency dQ_i = sum_j dS_ij K_j makes the backward parallel over both
+ * rows and columns ("FlashAttention vs. RingAttention", FlashAttention-2
+ * "core optimisations").  Three launches on `stream`: -D, D = rowsum(dO * O),
+ * and LSE * log2(e) into `ws`; a KV-split pass (one workgroup per K-tile and
+ * KV head) accumulating dK and dV in registers; a Q-split pass (one
+ * workgroup per Q-tile and head group) recomputing S and dP and accumulating
+ * dQ = scale * sum_j dS_ij K_j in registers.  dK and dV of a KV head are
+ * summed over its query-head group.  No atomics: every output is the same
+ * bit for bit from run to run.  `ws` is a device buffer of at least
  * attn_bwd_workspace_bytes(plan) bytes, 256-byte aligned.
  */
 attn_status attn_bwd(const attn_plan *plan, const void *q, const void *k,
                      const void *v, const void *o, const float *lse,
                      const void *dout, void *dq, void *dk, void *dv, void *ws,
                      size_t ws_bytes, attn_stream_t stream);
+
+/*
+ * attn_bwd with dQ accumulated inside the KV-split pass instead of a second
+ * pass: every wave writes its bf16 dS to LDS, and after the next stage's
+ * barrier computes dQ of the stage's rows for its own columns of d from the
+ * transposed dS tile and a slice of K in registers, adding it into a zeroed
+ * fp32 accumulator in `ws` with atomics; a last launch writes
+ * dQ = scale * accumulator in bf16.  It saves the recomputation of S and dP,
+ * at the price of one fp32 atomic addition per (row, key) pair at d = 128;
+ * measured on MI355X it is about half as fast as attn_bwd, so attn_bwd is
+ * the default.  The order of the atomic additions varies, so dQ may differ
+ * in its last bit from run to run.  Same arguments as attn_bwd, with `ws` of
+ * at least attn_bwd_atomic_workspace_bytes(plan) bytes.
+ */
+attn_status attn_bwd_atomic_dq(const attn_plan *plan, const void *q, const void *k,
+                               const void *v, const void *o, const float *lse,
+                               const void *dout, void *dq, void *dk, void *dv, void *ws,
+                               size_t ws_bytes, attn_stream_t stream);
 
 /*
  * The three stages of attn_bwd, callable one at a time on the same stream

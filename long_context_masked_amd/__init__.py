@@ -62,6 +62,9 @@ class Plan:
     def workspace_bytes(self):
         return int(L.lib().attn_bwd_workspace_bytes(self._h))
 
+    def atomic_workspace_bytes(self):
+        return int(L.lib().attn_bwd_atomic_workspace_bytes(self._h))
+
     def bind(self, device=None):
         import torch
         dev = torch.device("cuda" if device is None else device)
@@ -179,15 +182,16 @@ def fwd(plan, q, k, v=None, out=None, lse=None):
     return o, lse
 
 
-def bwd(plan, q, k, v, o, lse, do, workspace=None, grads=None):
+def bwd(plan, q, k, v, o, lse, do, workspace=None, grads=None, atomic_dq=False):
     """dQ, dK, dV (bf16) from the forward's O and LSE and the output gradient dO.
 
     ``bwd(plan, q, k, v, o, lse, do)`` runs on a compiled Plan;
     ``bwd(q, k, v, o, lse, do, mask)`` takes the mask and uses the plan cache
-    (bwd_desc)."""
+    (bwd_desc).  ``atomic_dq=True`` accumulates dQ inside the dK/dV pass with
+    fp32 atomics (attn_bwd_atomic_dq) instead of the separate dQ pass."""
     if not isinstance(plan, Plan):
-        if grads is not None:
-            raise ValueError("grads= is only for the Plan form")
+        if grads is not None or atomic_dq:
+            raise ValueError("grads= and atomic_dq= are only for the Plan form")
         return bwd_desc(plan, q, k, v, o, lse, do, workspace=workspace)
     import torch
     B, S, Hq, Hkv, d = plan.shape
@@ -201,16 +205,17 @@ def bwd(plan, q, k, v, o, lse, do, workspace=None, grads=None):
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = grads
-    nws = plan.workspace_bytes()
+    nws = plan.atomic_workspace_bytes() if atomic_dq else plan.workspace_bytes()
     ws = torch.empty(nws + 256, dtype=torch.uint8, device=q.device) if workspace is None else workspace
     wptr = ws.data_ptr()
     wptr += (-wptr) % 256
     stream = torch.cuda.current_stream(q.device).cuda_stream
     P = C.c_void_p
-    L.check(L.lib().attn_bwd(plan.handle, P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
-                             P(o.data_ptr()), P(lse.data_ptr()), P(do.data_ptr()),
-                             P(dq.data_ptr()), P(dk.data_ptr()), P(dv.data_ptr()), P(wptr),
-                             C.c_size_t(nws), P(stream)))
+    fn = L.lib().attn_bwd_atomic_dq if atomic_dq else L.lib().attn_bwd
+    L.check(fn(plan.handle, P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
+               P(o.data_ptr()), P(lse.data_ptr()), P(do.data_ptr()),
+               P(dq.data_ptr()), P(dk.data_ptr()), P(dv.data_ptr()), P(wptr),
+               C.c_size_t(nws), P(stream)))
     return dq, dk, dv
 
 

@@ -10,7 +10,8 @@ namespace lcm {
 hipError_t launch_fwd(const FwdArgs &a, int d, int HG, bool masked, int n_items, int B,
                       hipStream_t st);
 hipError_t launch_bwd_pre(const BwdArgs &a, int d, int B, hipStream_t st);
-hipError_t launch_dkdv(const BwdArgs &a, int d, int B, hipStream_t st);
+hipError_t launch_dkdv(const BwdArgs &a, int d, int B, bool fused_dq, hipStream_t st);
+hipError_t launch_dq_convert(const BwdArgs &a, int d, int B, hipStream_t st);
 hipError_t launch_dq(const BwdArgs &a, int d, int HG, bool masked, int B, hipStream_t st);
 hipError_t launch_merge(const float *o1, const float *lse1, const float *o2, const float *lse2,
                         void *o, bool o_bf16, float *lse, int64_t B, int S, int Hq, int d,
@@ -226,6 +227,9 @@ BwdArgs bwd_args(const attn_plan *p, const void *q, const void *k, const void *v
   a.part = ws ? reinterpret_cast<float *>(static_cast<char *>(const_cast<void *>(ws)) +
                                           ws_stats_bytes(p))
               : nullptr;
+  a.dqacc = ws ? reinterpret_cast<float *>(static_cast<char *>(const_cast<void *>(ws)) +
+                                           ws_stats_bytes(p) + ws_partial_bytes(p))
+               : nullptr;
   a.n_fitems = (int)p->lay.n_fwd_items;
   a.n_bitems = (int)p->lay.n_bwd_items;
   a.n_breduce = (int)p->lay.n_bwd_reduce;
@@ -234,12 +238,18 @@ BwdArgs bwd_args(const attn_plan *p, const void *q, const void *k, const void *v
   return a;
 }
 
-attn_status check_ws(const attn_plan *p, const void *ws, size_t ws_bytes) {
+// Workspace bytes a call uses: the statistics and partial dK/dV slots, and
+// the dQ accumulator when the call zeroes, fills or reads it.
+size_t ws_need(const attn_plan *p, bool dq_acc) {
+  return (size_t)(ws_stats_bytes(p) + ws_partial_bytes(p) + (dq_acc ? ws_dq_bytes(p) : 0));
+}
+
+attn_status check_ws(const attn_plan *p, const void *ws, size_t ws_bytes, bool dq_acc) {
   attn_status s = check_tensor(ws, "ws", 256);
   if (s != ATTN_OK) return s;
-  if (ws_bytes < attn_bwd_workspace_bytes(p))
-    return fail(ATTN_ERR_INVALID, "workspace holds %zu bytes; %zu needed", ws_bytes,
-                attn_bwd_workspace_bytes(p));
+  if (ws_bytes < ws_need(p, dq_acc))
+    return fail(ATTN_ERR_INVALID, "workspace holds %zu bytes; %zu needed%s", ws_bytes, ws_need(p, dq_acc),
+                dq_acc ? " (attn_bwd_atomic_workspace_bytes)" : "");
   return ATTN_OK;
 }
 
@@ -264,10 +274,11 @@ extern "C" attn_status attn_bwd_preprocess(const attn_plan *p, const void *o, co
   LCM_CHECK(check_tensor(o, "o", 16));
   LCM_CHECK(check_tensor(lse, "lse", 4));
   LCM_CHECK(check_tensor(dout, "dout", 16));
-  LCM_CHECK(check_ws(p, ws, ws_bytes));
+  LCM_CHECK(check_ws(p, ws, ws_bytes, false));
   if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
-  const BwdArgs a = bwd_args(p, nullptr, nullptr, nullptr, o, lse, dout, nullptr, nullptr,
-                             nullptr, ws);
+  BwdArgs a = bwd_args(p, nullptr, nullptr, nullptr, o, lse, dout, nullptr, nullptr,
+                       nullptr, ws);
+  a.dqacc = nullptr;
   (void)hipGetLastError();
   return launched(launch_bwd_pre(a, (int)p->shape.d, (int)p->shape.B,
                                  reinterpret_cast<hipStream_t>(stream)), "backward preprocess");
@@ -286,11 +297,11 @@ extern "C" attn_status attn_bwd_dkdv(const attn_plan *p, const void *q, const vo
   LCM_CHECK(check_tensor(dout, "dout", 16));
   LCM_CHECK(check_tensor(dk, "dk", 16));
   LCM_CHECK(check_tensor(dv, "dv", 16));
-  LCM_CHECK(check_ws(p, ws, ws_bytes));
+  LCM_CHECK(check_ws(p, ws, ws_bytes, false));
   if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
   const BwdArgs a = bwd_args(p, q, k, v, nullptr, lse, dout, nullptr, dk, dv, ws);
   (void)hipGetLastError();
-  return launched(launch_dkdv(a, (int)p->shape.d, (int)p->shape.B,
+  return launched(launch_dkdv(a, (int)p->shape.d, (int)p->shape.B, false,
                               reinterpret_cast<hipStream_t>(stream)), "dK/dV");
 }
 
@@ -305,7 +316,7 @@ extern "C" attn_status attn_bwd_dq(const attn_plan *p, const void *q, const void
   LCM_CHECK(check_tensor(lse, "lse", 4));
   LCM_CHECK(check_tensor(dout, "dout", 16));
   LCM_CHECK(check_tensor(dq, "dq", 16));
-  LCM_CHECK(check_ws(p, ws, ws_bytes));
+  LCM_CHECK(check_ws(p, ws, ws_bytes, false));
   if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
   const BwdArgs a = bwd_args(p, q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, ws);
   (void)hipGetLastError();
@@ -313,10 +324,10 @@ extern "C" attn_status attn_bwd_dq(const attn_plan *p, const void *q, const void
                             reinterpret_cast<hipStream_t>(stream)), "dQ");
 }
 
-extern "C" attn_status attn_bwd(const attn_plan *p, const void *q, const void *k, const void *v,
-                                const void *o, const float *lse, const void *dout, void *dq,
-                                void *dk, void *dv, void *ws, size_t ws_bytes,
-                                attn_stream_t stream) {
+namespace {
+attn_status bwd_impl(const attn_plan *p, const void *q, const void *k, const void *v,
+                     const void *o, const float *lse, const void *dout, void *dq, void *dk,
+                     void *dv, void *ws, size_t ws_bytes, attn_stream_t stream, bool fused) {
   clear_error();
   LCM_CHECK(check_plan(p));
   LCM_CHECK(check_tensor(q, "q", 16));
@@ -328,15 +339,35 @@ extern "C" attn_status attn_bwd(const attn_plan *p, const void *q, const void *k
   LCM_CHECK(check_tensor(dq, "dq", 16));
   LCM_CHECK(check_tensor(dk, "dk", 16));
   LCM_CHECK(check_tensor(dv, "dv", 16));
-  LCM_CHECK(check_ws(p, ws, ws_bytes));
+  LCM_CHECK(check_ws(p, ws, ws_bytes, fused));
   if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
-  const BwdArgs a = bwd_args(p, q, k, v, o, lse, dout, dq, dk, dv, ws);
+  BwdArgs a = bwd_args(p, q, k, v, o, lse, dout, dq, dk, dv, ws);
+  if (!fused) a.dqacc = nullptr;  // the recompute pass needs no accumulator
   const int d = (int)p->shape.d, B = (int)p->shape.B;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   LCM_CHECK(launched(launch_bwd_pre(a, d, B, st), "backward preprocess"));
-  LCM_CHECK(launched(launch_dkdv(a, d, B, st), "dK/dV"));
+  if (fused) {
+    LCM_CHECK(launched(launch_dkdv(a, d, B, true, st), "dK/dV with dQ"));
+    return launched(launch_dq_convert(a, d, B, st), "dQ convert");
+  }
+  LCM_CHECK(launched(launch_dkdv(a, d, B, false, st), "dK/dV"));
   return launched(launch_dq(a, d, p->HG, masked_lists(p), B, st), "dQ");
+}
+}  // namespace
+
+extern "C" attn_status attn_bwd(const attn_plan *p, const void *q, const void *k, const void *v,
+                                const void *o, const float *lse, const void *dout, void *dq,
+                                void *dk, void *dv, void *ws, size_t ws_bytes,
+                                attn_stream_t stream) {
+  return bwd_impl(p, q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, stream, false);
+}
+
+extern "C" attn_status attn_bwd_atomic_dq(const attn_plan *p, const void *q, const void *k,
+                                          const void *v, const void *o, const float *lse,
+                                          const void *dout, void *dq, void *dk, void *dv,
+                                          void *ws, size_t ws_bytes, attn_stream_t stream) {
+  return bwd_impl(p, q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, stream, true);
 }
 
 extern "C" attn_status attn_merge(const float *o1, const float *lse1, const float *o2,

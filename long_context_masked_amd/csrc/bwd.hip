@@ -28,15 +28,16 @@ __device__ __forceinline__ int64_t ws_row0(int b, int h, int Hq, int S64) {
 }
 
 // ws <- {lse * log2(e), -D = -sum_d dO * O} per (b, h, row); rows in
-// [S, S64) get zeros.  A row with no allowed key (LSE = -inf) gets a large
+// [S, S64) get zeros.  When dqacc is given, its row (b, s, h) of the fp32 dQ
+// accumulator [B][S64][Hq][D] is zeroed as well.  A row with no allowed key (LSE = -inf) gets a large
 // positive lse2 instead, so that the recomputed P = exp2(S c - lse2) is 0 on
 // every key, masked ones (S = -inf) included, rather than -inf + inf.  D is stored negated so that the dK/dV pass can start
 // the accumulation of dP at -D and get dP - D from the products alone.  One group of D/8 lanes per row; the grid covers B * S64 * Hq
 // rows in [b][s][h] order.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const bf16 *dout,
-                                                           const float *lse, float *ws, int S,
-                                                           int S64, int Hq, int64_t nrows) {
+                                                           const float *lse, float *ws, float *dqacc,
+                                                           int S, int S64, int Hq, int64_t nrows) {
   constexpr int CPR = D / 8;
   constexpr int RPB = 256 / CPR;
   const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
@@ -57,6 +58,11 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
   }
 #pragma unroll
   for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (dqacc && r < nrows) {  // the fp32 dQ accumulator row starts at zero
+    float *z = dqacc + r * D + c * 8;
+    *reinterpret_cast<f32x4 *>(z) = (f32x4){};
+    *reinterpret_cast<f32x4 *>(z + 4) = (f32x4){};
+  }
   if (r < nrows && c == 0) {
     const int64_t w0 = ws_row0(b, h, Hq, S64);
     const float l = real ? lse[((int64_t)b * Hq + h) * S + s] : 0.f;
@@ -96,19 +102,39 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
 // next stage's tiles, so stages rotate through three LDS buffers: the
 // barrier before phase 3 publishes stage st + 1 and frees the buffer of
 // stage st - 1, which then receives stage st + 2.
+//
+// FDQ: the pass also accumulates dQ = dS K (the dependency that makes the
+// backward parallel over both rows and columns, "FlashAttention vs.
+// RingAttention", FlashAttention-2 "core optimisations"), so that no second
+// pass has to recompute S and dP.  dS has one key per lane, but dS K needs
+// one query row per lane, so every wave writes its bf16 dS (the same values
+// that enter dK) into an LDS tile [128 keys][64 rows] (phases 2 and 3b), and
+// after the next stage's barrier each wave reads the whole tile transposed
+// and computes dQ of the stage's 64 rows for its own 32 columns of d, from a
+// slice of K kept in registers (phase 4, 16 products at d = 128).  The fp32
+// result is added into a zeroed accumulator [B][S64][Hq][D] with atomics; a
+// convert pass scales it and rounds it to bf16.  The dS tiles rotate through
+// three LDS buffers: the one of stage st is read in stage st + 1 and written
+// again in stage st + 3, after the barrier of stage st + 2 that every wave
+// reaches only once its reads are done.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool FDQ>
 __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   constexpr int KS = D / 16;    // k-steps of A (two MFMAs each: S and dP)
   constexpr int DB = D / 32;    // 32-row blocks of dK^T / dV^T
   constexpr int NC = 2 * DB;    // chunks of C (two MFMAs each: dV and dK)
   using T = Tile<D>;
+  using T64 = Tile<64>;
   constexpr int OFF_DO = T::BYTES, OFF_L = 2 * T::BYTES, OFF_D = OFF_L + 256;
   constexpr int STAGE = 2 * T::BYTES + 1024;
   constexpr int NBUF = 3;
-  constexpr int PF = KS < 4 ? KS : 4;  // k-steps of A operands read ahead
+  // k-steps of A operands read ahead (the fused pass gives the registers of
+  // two of them to its dQ phase)
+  constexpr int PF = KS < (FDQ ? 2 : 4) ? KS : (FDQ ? 2 : 4);
+  constexpr int DSB = 2 * T64::BYTES;  // dS of a stage: keys 0-63, then 64-127
+  constexpr int RBW = DB / 2;          // 32-row blocks of dQ per wave (d = 128: 2, d = 64: 1)
   static_assert(16 % KS == 0 && 8 % KS == 0 && 16 % NC == 0 && 8 % NC == 0, "chunking");
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE + (FDQ ? 3 * DSB : 0)];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -130,6 +156,24 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       kv[ks] = *reinterpret_cast<const bf16x8 *>(a.k + off + ks * 16);
       vv[ks] = *reinterpret_cast<const bf16x8 *>(a.v + off + ks * 16);
       if (!key_ok) { kv[ks] = (bf16x8){}; vv[ks] = (bf16x8){}; }
+    }
+  }
+  // FDQ: the B operand of dQ = dS K for this wave's 32 columns of d, every
+  // 16-key step t of the tile: lane (ln, hh) holds K[16t + 4hh + {0..3}] and
+  // K[16t + 8 + 4hh + {0..3}] at column 32 (wave % DB) + ln, the key order in
+  // which the transposed reads of the dS tile hand over the k index.
+  const int dqb = wave % DB, rb0 = (wave / DB) * RBW;
+  bf16x8 kq[FDQ ? 8 : 1];
+  if constexpr (FDQ) {
+    const bf16 *kc = a.k + (int64_t)b * S * ldk + (int64_t)kvh * D + dqb * 32 + ln;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kk = item.x * 128 + 16 * t + (i < 4 ? 4 * hh + i : 8 + 4 * hh + i - 4);
+        const bf16 x = kc[(int64_t)(kk < S ? kk : S - 1) * ldk];
+        kq[t][i] = kk < S ? x : (bf16)0.f;
+      }
     }
   }
   const int4 cb = key_ok ? a.m.colb[key] : make_int4(0, S, 0, 0);
@@ -272,6 +316,82 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     return x;
   };
 
+  // FDQ: dS of unit u (two k-steps t of 16 rows, as packed for dK) into the
+  // dS tile of a stage.  Lane (ln, hh) of wave w holds key 32 w + ln, i.e.
+  // row 32 (w % 2) + ln of 64-key tile w / 2, and rows 32 u + 16 t + 4 hh +
+  // {0..3} and 32 u + 16 t + 8 + 4 hh + {0..3} of the stage in dsb[t].
+  auto ds_store = [&](char *dsbuf, int u, const bf16x8 (&dsb)[2]) {
+    char *tile = dsbuf + (wave >> 1) * T64::BYTES;
+    const int kr = 32 * (wave & 1) + ln;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      *reinterpret_cast<bf16x4 *>(tile + T64::off(kr, 64 * u + 32 * t + 8 * hh)) =
+          __builtin_shufflevector(dsb[t], dsb[t], 0, 1, 2, 3);
+      *reinterpret_cast<bf16x4 *>(tile + T64::off(kr, 64 * u + 32 * t + 16 + 8 * hh)) =
+          __builtin_shufflevector(dsb[t], dsb[t], 4, 5, 6, 7);
+    }
+  };
+  // FDQ phase 4: dQ of stage sp (list entry entp, dS tile dsbuf, complete in
+  // LDS for every wave) for rows 32 (rb0 + i) + [0, 32), i < RBW, and this
+  // wave's 32 columns of d: A = dS rows read transposed from the tile (lane:
+  // one query row, 8 keys), B = the K slice; then fp32 atomics into the
+  // accumulator, unscaled.
+  auto dq_phase = [&](int sp, uint32_t entp, const char *dsbuf) {
+    const uint32_t base = lds_addr(dsbuf);
+    const int g = sp % G;
+    const int qt = (int)(entp & 0x7fffffffu);
+    const int rs = a.Hq * D;  // accumulator row stride (floats)
+    // uniform base of the stage's rows for this wave's columns, plus a
+    // 32-bit per-lane byte offset per atomic
+    char *dst = reinterpret_cast<char *>(a.dqacc + ((int64_t)b * a.S64 + qt * 64) * rs +
+                                         (int64_t)(kvh * G + g) * D + dqb * 32);
+    const uint32_t loff = (uint32_t)(4 * hh * rs + ln) * 4u;
+    // one 32-row block at a time; the transposed reads of 16-key step t + 1
+    // (tile t / 4, its rows 16 (t % 4)) are in flight while step t's product
+    // runs
+    auto issue = [&](auto tc, int i, s16x4 (&x)[2]) {
+      constexpr int t = decltype(tc)::value;
+      constexpr int OFF = (t >> 2) * T64::BYTES + (t & 3) * 16 * T64::ROWB;
+      x[0] = tr_issue<OFF>(base + tr_off<64>(lane, rb0 + i, 0));  // keys 16 t + 4 hh + {0..3}
+      x[1] = tr_issue<OFF>(base + tr_off<64>(lane, rb0 + i, 1));  // keys 16 t + 8 + 4 hh + {0..3}
+    };
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+      f32x16 acc = (f32x16){};
+      s16x4 xa[2], xb[2];
+      issue(std::integral_constant<int, 0>{}, i, xa);
+      tr_wait(xa);
+      issue(std::integral_constant<int, 1>{}, i, xb);
+      acc = mfma32(tr_pair(xa[0], xa[1]), kq[0], acc);
+      tr_wait(xb);
+      issue(std::integral_constant<int, 2>{}, i, xa);
+      acc = mfma32(tr_pair(xb[0], xb[1]), kq[1], acc);
+      tr_wait(xa);
+      issue(std::integral_constant<int, 3>{}, i, xb);
+      acc = mfma32(tr_pair(xa[0], xa[1]), kq[2], acc);
+      tr_wait(xb);
+      issue(std::integral_constant<int, 4>{}, i, xa);
+      acc = mfma32(tr_pair(xb[0], xb[1]), kq[3], acc);
+      tr_wait(xa);
+      issue(std::integral_constant<int, 5>{}, i, xb);
+      acc = mfma32(tr_pair(xa[0], xa[1]), kq[4], acc);
+      tr_wait(xb);
+      issue(std::integral_constant<int, 6>{}, i, xa);
+      acc = mfma32(tr_pair(xb[0], xb[1]), kq[5], acc);
+      tr_wait(xa);
+      issue(std::integral_constant<int, 7>{}, i, xb);
+      acc = mfma32(tr_pair(xa[0], xa[1]), kq[6], acc);
+      tr_wait(xb);
+      acc = mfma32(tr_pair(xb[0], xb[1]), kq[7], acc);
+      const int row0 = 32 * (rb0 + i);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t off = loff + (uint32_t)((row0 + 8 * (r >> 2) + (r & 3)) * rs) * 4u;
+        unsafeAtomicAdd(reinterpret_cast<float *>(dst + off), acc[r]);
+      }
+    }
+  };
+
   f32x16 s0, dp0;  // unit (st, 0): S and dP - D in VGPRs
   uint32_t mwc[2], mwn[2];
   bool pc = false, pn = false;  // stages st and st + 1 are partial
@@ -292,6 +412,10 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   }
 
   int cur = 0;  // buffer of stage st
+  // FDQ: dS buffer of stage st and of stage st - 1, list entry of st - 1
+  char *const dsb_base = smem + NBUF * STAGE;
+  int dcur = 0, dprev = 0;
+  uint32_t ent0 = nst > 0 ? list[0] : 0u, entp = 0u;
   // List entries are read a stage before they are needed, so that the
   // latency of the scalar load is covered by the products of a stage.
   uint32_t ent1 = nst > 1 ? list[1 / G] : 0u;  // stage st + 1
@@ -315,6 +439,10 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     for (int i = 0; i < DB; ++i) { in_agpr(dk[i]); in_agpr(dv[i]); }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) { in_agpr(kv[ks]); in_agpr(vv[ks]); }
+    if constexpr (FDQ) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) in_agpr(kq[t]);
+    }
     const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
     const int fre = nxt == NBUF - 1 ? 0 : nxt + 1;  // buffer of stage st - 1 = st + 2
     const char *buf = smem + cur * STAGE;
@@ -382,6 +510,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       if (c == 0) {
         tr_wait(xa);
         issue_tr(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, xb);
+        if constexpr (FDQ) ds_store(dsb_base + dcur * DSB, 0, dsb0);
       }
       if (c == DB) tr_wait(xb);
       if (tt == 0) c_chunk(xa, db, pb0[0], dsb0[0]);
@@ -440,6 +569,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       if (c == 0) {
         tr_wait(xa);
         issue_tr(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, xb);
+        if constexpr (FDQ) ds_store(dsb_base + dcur * DSB, 1, dsb1);
       }
       if (c == DB) tr_wait(xb);
       if (tt == 0) c_chunk(xa, db, pb1[0], dsb1[0]);
@@ -462,11 +592,28 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (FDQ) {
+      // ---- phase 4: dQ of stage st - 1 (its dS tile was completed by every
+      // wave before this stage's barrier)
+      __builtin_amdgcn_sched_barrier(0);
+      if (st >= 1) dq_phase(st - 1, entp, dsb_base + dprev * DSB);
+      __builtin_amdgcn_sched_barrier(0);
+      entp = ent0;
+      ent0 = ent1;
+      dprev = dcur;
+      dcur = dcur == 2 ? 0 : dcur + 1;
+    }
     mwc[0] = mwn[0];
     mwc[1] = mwn[1];
     ent1 = ent2;
     pc = pn;
     cur = nxt;
+  }
+  if constexpr (FDQ) {
+    if (nst > 0) {
+      __syncthreads();  // the last stage's dS tile, from every wave
+      dq_phase(nst - 1, entp, dsb_base + dprev * DSB);
+    }
   }
 
   if (slot >= 0) {
@@ -531,6 +678,29 @@ __global__ __launch_bounds__(256) void attn_dkdv_reduce_kernel(BwdArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// dQ from the fp32 accumulator of the fused dK/dV pass: dQ = scale * acc,
+// rounded to bf16.  One group of D/8 lanes per (b, s, h) row of dQ, s < S;
+// bound by HBM (4 bytes read, 2 written per element).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_dq_convert_kernel(const float *acc, bf16 *dq, int S,
+                                                              int S64, int Hq, float scale,
+                                                              int64_t nrows) {
+  constexpr int CPR = D / 8;
+  constexpr int RPB = 256 / CPR;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
+  if (r >= nrows) return;
+  const int c = threadIdx.x % CPR;
+  const int h = (int)(r % Hq);
+  const int64_t bs = r / Hq;
+  const int64_t b = bs / S, s = bs % S;
+  const float *src = acc + ((b * S64 + s) * Hq + h) * D + c * 8;
+  const f32x4 x0 = *reinterpret_cast<const f32x4 *>(src) * scale;
+  const f32x4 x1 = *reinterpret_cast<const f32x4 *>(src + 4) * scale;
+  *reinterpret_cast<bf16x8 *>(dq + r * D + c * 8) = pack8(x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]);
+}
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per forward work item (Q-tile, head group); same lane
@@ -721,11 +891,15 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdArgs a) {
 // Every variant is instantiated explicitly: implicit instantiation from the
 // launchers alone has left some host-side launch stubs unemitted.
 template __global__ void attn_bwd_pre_kernel<128>(const bf16 *, const bf16 *, const float *,
-                                                  float *, int, int, int, int64_t);
+                                                  float *, float *, int, int, int, int64_t);
 template __global__ void attn_bwd_pre_kernel<64>(const bf16 *, const bf16 *, const float *,
-                                                 float *, int, int, int, int64_t);
-template __global__ void attn_dkdv_kernel<128>(BwdArgs);
-template __global__ void attn_dkdv_kernel<64>(BwdArgs);
+                                                 float *, float *, int, int, int, int64_t);
+template __global__ void attn_dkdv_kernel<128, false>(BwdArgs);
+template __global__ void attn_dkdv_kernel<64, false>(BwdArgs);
+template __global__ void attn_dkdv_kernel<128, true>(BwdArgs);
+template __global__ void attn_dkdv_kernel<64, true>(BwdArgs);
+template __global__ void attn_dq_convert_kernel<128>(const float *, bf16 *, int, int, int, float, int64_t);
+template __global__ void attn_dq_convert_kernel<64>(const float *, bf16 *, int, int, int, float, int64_t);
 template __global__ void attn_dkdv_reduce_kernel<128>(BwdArgs);
 template __global__ void attn_dkdv_reduce_kernel<64>(BwdArgs);
 #define LCM_DQ(D, HG)                                             \
@@ -743,18 +917,34 @@ hipError_t launch_bwd_pre(const BwdArgs &a, int d, int B, hipStream_t st) {
   const dim3 grid((unsigned)((nrows + rpb - 1) / rpb)), block(256);
   if (d == 128)
     hipLaunchKernelGGL((attn_bwd_pre_kernel<128>), grid, block, 0, st, a.o, a.dout, a.lse, a.ws,
-                       a.S, a.S64, a.Hq, nrows);
+                       a.dqacc, a.S, a.S64, a.Hq, nrows);
   else if (d == 64)
     hipLaunchKernelGGL((attn_bwd_pre_kernel<64>), grid, block, 0, st, a.o, a.dout, a.lse, a.ws,
-                       a.S, a.S64, a.Hq, nrows);
+                       a.dqacc, a.S, a.S64, a.Hq, nrows);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_dkdv(const BwdArgs &a, int d, int B, hipStream_t st) {
+hipError_t launch_dq_convert(const BwdArgs &a, int d, int B, hipStream_t st) {
+  const int64_t nrows = (int64_t)B * a.S * a.Hq;
+  const int rpb = 256 / (d / 8);
+  const dim3 grid((unsigned)((nrows + rpb - 1) / rpb)), block(256);
+  if (d == 128)
+    hipLaunchKernelGGL((attn_dq_convert_kernel<128>), grid, block, 0, st, a.dqacc, a.dq, a.S, a.S64,
+                       a.Hq, a.scale, nrows);
+  else if (d == 64)
+    hipLaunchKernelGGL((attn_dq_convert_kernel<64>), grid, block, 0, st, a.dqacc, a.dq, a.S, a.S64,
+                       a.Hq, a.scale, nrows);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_dkdv(const BwdArgs &a, int d, int B, bool fused_dq, hipStream_t st) {
   const dim3 grid((unsigned)a.n_bitems, (unsigned)B), block(256);
-  if (d == 128) hipLaunchKernelGGL((attn_dkdv_kernel<128>), grid, block, 0, st, a);
-  else if (d == 64) hipLaunchKernelGGL((attn_dkdv_kernel<64>), grid, block, 0, st, a);
+  if (d == 128 && fused_dq) hipLaunchKernelGGL((attn_dkdv_kernel<128, true>), grid, block, 0, st, a);
+  else if (d == 128) hipLaunchKernelGGL((attn_dkdv_kernel<128, false>), grid, block, 0, st, a);
+  else if (d == 64 && fused_dq) hipLaunchKernelGGL((attn_dkdv_kernel<64, true>), grid, block, 0, st, a);
+  else if (d == 64) hipLaunchKernelGGL((attn_dkdv_kernel<64, false>), grid, block, 0, st, a);
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_breduce == 0) return e;

@@ -245,8 +245,10 @@ __device__ __forceinline__ s16x4 tr_issue(uint32_t addr) {
 // wait so that no use of them can be scheduled before it.
 template <int N>
 __device__ __forceinline__ void tr_wait(s16x4 (&x)[N]) {
-  static_assert(N == 4 || N == 8 || N == 16, "tr_wait: 4, 8 or 16 operands");
-  if constexpr (N == 4)
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "tr_wait: 2, 4, 8 or 16 operands");
+  if constexpr (N == 2)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]));
+  else if constexpr (N == 4)
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
   else if constexpr (N == 8)
     asm volatile("s_waitcnt lgkmcnt(0)"
@@ -353,6 +355,7 @@ struct BwdArgs {
   const int *bslot;     // per dK/dV item: partial slot, -1 when not split
   const int4 *breduce;  // per split item: K-tile, KV head, first slot, chunks
   float *part;          // partial dK/dV: [B][n_slots][2][128 keys][d] fp32
+  float *dqacc;         // fused dQ accumulator [B][S64][Hq][d] fp32, or null
   int n_fitems, n_bitems, n_breduce, n_slots;
   MaskArgs m;
 };

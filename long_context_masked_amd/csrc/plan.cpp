@@ -839,4 +839,9 @@ extern "C" size_t attn_bwd_workspace_bytes(const attn_plan *plan) {
   return (size_t)(lcm::ws_stats_bytes(plan) + lcm::ws_partial_bytes(plan));
 }
 
+extern "C" size_t attn_bwd_atomic_workspace_bytes(const attn_plan *plan) {
+  if (!plan) return 0;
+  return (size_t)(lcm::ws_stats_bytes(plan) + lcm::ws_partial_bytes(plan) + lcm::ws_dq_bytes(plan));
+}
+
 extern "C" void attn_plan_destroy(attn_plan *plan) { delete plan; }

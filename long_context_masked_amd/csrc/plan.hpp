@@ -89,6 +89,11 @@ inline int64_t ws_stats_bytes(const attn_plan *p) {
 inline int64_t ws_partial_bytes(const attn_plan *p) {
   return p->shape.B * (int64_t)p->n_slots * 2 * kBwdKeyTile * p->shape.d * 4;
 }
+// fp32 dQ accumulator of the fused dK/dV pass: [B][S64][Hq][d].
+inline int64_t ws_dq_bytes(const attn_plan *p) {
+  const int64_t s64 = (p->shape.S + 63) / 64 * 64;
+  return p->shape.B * s64 * p->shape.Hq * p->shape.d * 4;
+}
 
 // Thread-local last error (defined in plan.cpp).
 attn_status fail(attn_status s, const char *fmt, ...);

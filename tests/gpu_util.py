@@ -93,3 +93,16 @@ def gate(name, got, ref, mag=None, rms=None, n=None, quiet=True):
         f"allowance {allow[worst]:.3e}); raw max {mx:.3e}")
     assert mean <= GATE_MEAN, f"{name}: mean-abs {mean:.3e} of rms (raw max {mx:.3e})"
     return mx, mean, used
+
+
+def assert_within_one_ulp(name, a, b):
+    """a and b (bf16 tensors) are equal up to one bf16 unit in the last place,
+    or, for elements near zero where the summed terms cancel, to 1e-4 of the
+    tensor's RMS: what two runs of the atomic dQ accumulation can differ by
+    (fp32 sums in another order, about 2^-24 of the terms each, then one
+    rounding to bf16)."""
+    import torch
+    x, y = a.to(torch.float32), b.to(torch.float32)
+    floor = 1e-4 * float(x.pow(2).mean().sqrt())
+    ok = (x - y).abs() <= 2.0 ** -7 * torch.maximum(x.abs(), y.abs()) + floor
+    assert bool(ok.all()), f"{name}: {int((~ok).sum())} elements differ by more than one bf16 ulp"

@@ -14,7 +14,7 @@ import synthetic as syn
 from oracle import attention as ora
 from oracle import masks as om
 
-from gpu_util import gate, to_dev, to_f64, f64
+from gpu_util import assert_within_one_ulp, gate, to_dev, to_f64, f64
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -177,8 +177,10 @@ def test_forward_is_deterministic():
 
 
 def test_backward_is_deterministic_with_split_items():
-    """The partial dK/dV of split items are summed in a fixed order, so two
-    backward passes give identical bits (S = 1K splits every dK/dV item)."""
+    """The partial dK/dV of split items are summed in a fixed order and dQ
+    has its own pass, so two backward passes give identical bits (S = 1K
+    splits every dK/dV item); with dQ accumulated by atomics, dK and dV keep
+    identical bits and dQ stays within one bf16 ulp, run to run."""
     S = 1024
     spec = syn.spec_causal(S)
     plan = lcm.Plan(1, S, 8, 2, 128, spec)
@@ -188,9 +190,37 @@ def test_backward_is_deterministic_with_split_items():
     o, lse = lcm.fwd(plan, q, k, v)
     g1 = lcm.bwd(plan, q, k, v, o, lse, do)
     g2 = lcm.bwd(plan, q, k, v, o, lse, do)
+    a1 = lcm.bwd(plan, q, k, v, o, lse, do, atomic_dq=True)
+    a2 = lcm.bwd(plan, q, k, v, o, lse, do, atomic_dq=True)
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+    for a, b, c in zip(a1[1:], a2[1:], g1[1:]):
+        assert torch.equal(a, b) and torch.equal(a, c)
+    assert_within_one_ulp("dQ", a1[0], a2[0])
+
+
+def test_atomic_and_separate_dq_paths_both_match_the_oracle():
+    """attn_bwd (separate dQ pass) and attn_bwd_atomic_dq (dQ accumulated in
+    the dK/dV pass) against the oracle on masks with partial tiles, GQA and
+    MHA, both head dims, ragged S and rows without keys."""
+    cases = [(syn.spec_causal(333), 1, 6, 2, 128), (RAGGED_GQA[12][1], 1, 8, 1, 128),
+             (dict(TINY)["varblock_50"], 2, 4, 2, 64)]
+    for spec, B, Hq, Hkv, d in cases:
+        S = spec["S"]
+        print(f"atomic vs separate dQ: {spec['family']} S={S} Hq={Hq} Hkv={Hkv} d={d}", flush=True)
+        x = syn.attention_inputs(B, S, Hq, Hkv, d, 9)
+        q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
+        plan = lcm.Plan(B, S, Hq, Hkv, d, spec)
+        o, lse = lcm.fwd(plan, q, k, v)
+        gs = lcm.bwd(plan, q, k, v, o, lse, do)
+        ga = lcm.bwd(plan, q, k, v, o, lse, do, atomic_dq=True)
+        torch.cuda.synchronize()
+        ref = ora.backward(*(f64(x[n]) for n in ("q", "k", "v", "do")), spec, magnitudes=True)
+        for g in (gs, ga):
+            gate("dQ", to_f64(g[0]), ref["dq"], ref["m_dq"])
+            gate("dK", to_f64(g[1]), ref["dk"], ref["m_dk"])
+            gate("dV", to_f64(g[2]), ref["dv"], ref["m_dv"])
 
 
 def test_forced_device_error_leaves_outputs_untouched(monkeypatch):
