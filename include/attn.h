@@ -266,6 +266,27 @@ attn_status attn_bwd_atomic_dq(const attn_plan *plan, const void *q, const void 
                                size_t ws_bytes, attn_stream_t stream);
 
 /*
+ * attn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same backward, with its workspace in a static device array that the
+ * library holds on every GPU it runs on until the process ends, instead of a
+ * caller buffer.  The caller still passes the bound plan, the inputs and the
+ * outputs.  Plans whose workspace (attn_bwd_workspace_bytes) exceeds
+ * attn_bwd_noalloc_max_workspace_bytes() (128 MiB) are rejected with
+ * ATTN_ERR_INVALID before anything is launched.  Calls no allocation
+ * routine.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and must
+ * be serialised by the caller.  The backward writes every workspace value
+ * it reads, so nothing left by an earlier call is used.  The device is the
+ * current one, which must be the stream's.
+ */
+attn_status attn_bwd_noalloc(const attn_plan *plan, const void *q, const void *k,
+                             const void *v, const void *o, const float *lse,
+                             const void *dout, void *dq, void *dk, void *dv,
+                             attn_stream_t stream);
+size_t attn_bwd_noalloc_max_workspace_bytes(void);
+
+/*
  * The three stages of attn_bwd, callable one at a time on the same stream
  * and in this order (attn_bwd is exactly these three calls).  They exist so
  * that callers can interleave other work between stages and time them.

@@ -74,6 +74,8 @@ SIGNATURES = {
     "attn_bwd_dkdv": (C.c_int, [C.c_void_p] * 9 + [C.c_size_t, C.c_void_p]),
     "attn_bwd_dq": (C.c_int, [C.c_void_p] * 8 + [C.c_size_t, C.c_void_p]),
     "attn_bwd_atomic_dq": (C.c_int, [C.c_void_p] * 11 + [C.c_size_t, C.c_void_p]),
+    "attn_bwd_noalloc": (C.c_int, [C.c_void_p] * 11),
+    "attn_bwd_noalloc_max_workspace_bytes": (C.c_size_t, []),
     "attn_bwd_atomic_workspace_bytes": (C.c_size_t, [C.c_void_p]),
     "attn_fwd_partial": (C.c_int, [C.c_void_p] * 7),
     "attn_merge": (C.c_int, [C.c_void_p] * 5 + [C.c_int, C.c_void_p] + [C.c_int64] * 4 + [C.c_void_p]),

@@ -2,6 +2,7 @@
 // All argument checks run before anything is enqueued.
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "kernels.hpp"
 #include "plan.hpp"
@@ -401,4 +402,59 @@ extern "C" attn_status attn_merge(const float *o1, const float *lse1, const floa
   return launched(launch_merge(o1, lse1, o2, lse2, o, o_bf16 != 0, lse, B, (int)S, (int)Hq, (int)d,
                                reinterpret_cast<hipStream_t>(stream)),
                   "merge");
+}
+
+// ---------------------------------------------------------------------------
+// attn_bwd without a caller workspace, for callers that cannot allocate
+// device memory.  The workspace of the backward (LSE * log2(e), -D and the
+// partial dK/dV of split items) lives in this file-scope array instead; each
+// GPU the library runs on holds one copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, not a device address: the
+// address of each device's copy comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is used.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = size_t(128) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+attn_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(ATTN_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+}  // namespace
+
+extern "C" size_t attn_bwd_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
+
+extern "C" attn_status attn_bwd_noalloc(const attn_plan *p, const void *q, const void *k,
+                                        const void *v, const void *o, const float *lse,
+                                        const void *dout, void *dq, void *dk, void *dv,
+                                        attn_stream_t stream) {
+  clear_error();
+  LCM_CHECK(check_plan(p));
+  const size_t need = ws_need(p, false);
+  if (need > kScratchBytes)
+    return fail(ATTN_ERR_INVALID,
+                "attn_bwd_noalloc: this plan needs %zu bytes of workspace; the library's "
+                "static workspace holds %zu (use attn_bwd with a caller buffer)",
+                need, kScratchBytes);
+  void *ws = nullptr;
+  LCM_CHECK(scratch_of_current_device(&ws));
+  return bwd_impl(p, q, k, v, o, lse, dout, dq, dk, dv, ws, kScratchBytes, stream, false);
 }
