@@ -281,6 +281,12 @@ def summarize_traffic(fetch_csv, write_csv, copy_mib, workload_desc, commands):
         out[name] = {"counter": counter, "copy_kib": round(copy_kib, 1), "factor": round(factor, 4),
                      "kernel_dispatches": len(kern), "kernel_mean_kib_raw": round(mean_kib, 1),
                      "bytes_per_launch": round(mean_kib * factor * 1024.0)}
+        # the other main kernels of the same run, for comparison
+        for short, kname in MFMA_KERNELS.items():
+            vals = [v for (k, _), v in agg.items() if kname in k and "reduce" not in k]
+            if vals:
+                out.setdefault("per_kernel", {}).setdefault(short, {})[name + "_bytes_per_launch"] = \
+                    round(sum(vals) / len(vals) * factor * 1024.0)
     out["bytes_per_launch"] = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
     return out
 
