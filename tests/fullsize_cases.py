@@ -65,7 +65,7 @@ def _doc_ends(spec):
 
 def col_cases():
     """(label, spec, Hkv, KV heads checked, row budget, extra candidates,
-    oracle row block).  About 2.5e9 (row, key) scores in all."""
+    oracle row block).  About 5e9 (row, key) scores in all."""
     out = []
     dense8 = dict(syn.config_mask_specs("dense", 8192))
     dense48 = dict(syn.config_mask_specs("dense", 49152))
@@ -101,6 +101,12 @@ def col_cases():
     # it, each with all earlier keys; at 8K with 2K blocks to bound the cost
     bc = syn.spec_causal_blockwise(8192, 2048, reading="block_causal")
     out.append(("variants8K_causal_blockwise_block_causal", bc, 8, (0,), 2048, (), 512))
+    # the longest configured sequence: S = 128K, keys near the end (few rows)
+    dense128 = dict(syn.config_mask_specs("dense", 131072))
+    out.append(("dense128K_causal", dense128["causal"], 8, (3,), 512,
+                (131072 - 2, 131072 - 64, 131072 - 65), 512))
+    spg = dict(syn.config_mask_specs("sparse", 32768, Hq=HQ, Hkv=8))
+    out.append(("sparse32K_block64_50", spg["block64_50"], 8, (5,), 20000, (), 64))
     spm = dict(syn.config_mask_specs("sparse", 32768, Hq=HQ, Hkv=64))
     out.append(("sparse32K_mha_block64_50", spm["block64_50"], 64, (0, 21, 42, 63), 20000, (), 64))
     out.append(("sparse32K_mha_varblock_50", spm["varblock_50"], 64, (0, 63), 20000, (), 64))
