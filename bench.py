@@ -404,7 +404,8 @@ class Runner:
             self.runs.append(dict(label=label, S=S, Hq=Hq, Hkv=Hkv, plan=plan, ws=ws,
                                   nnz=plan.stats["nnz_total"], events=[]))
             log(f"plan {label}: nnz {plan.stats['nnz_total']:.4g}, fwd partial tiles "
-                f"{plan.stats['fwd_tiles_partial']}, full {plan.stats['fwd_tiles_full']}")
+                f"{plan.stats['fwd_tiles_partial']}, full {plan.stats['fwd_tiles_full']}, "
+                f"dK/dV items of {plan.stats['bwd_tile_cols']} keys")
 
     def _inputs(self, S, Hq, Hkv, d, on_device):
         """Q, K, V, dO ~ N(0, 1) rounded to bf16: from the seeded numpy
@@ -544,6 +545,8 @@ def main():
     ap.add_argument("--bwd", default="separate", choices=["separate", "atomic"],
                     help="backward: the separate dQ pass (attn_bwd), or dQ accumulated in the "
                          "dK/dV pass with fp32 atomics (attn_bwd_atomic_dq, timed as one interval)")
+    ap.add_argument("--bwd-key-tile", type=int, default=0, choices=[0, 64, 128],
+                    help="keys per dK/dV work item for every plan (0: each plan chooses)")
     ap.add_argument("--no-workloads", action="store_true",
                     help="default dense run: skip the timing of the other configurations")
     ap.add_argument("--no-dynamic", action="store_true",
@@ -584,6 +587,10 @@ def main():
     dev = torch.device("cuda:0")
     cases, desc = workload(args.workload, seqs)
     fused = args.bwd == "atomic"
+    key_tile = 128 if fused else args.bwd_key_tile  # the fused dQ pass runs on 128-key items
+    if key_tile:
+        cases = [(label, S, Hq, Hkv, dict(spec, bwd_key_tile=key_tile)) for label, S, Hq, Hkv, spec in cases]
+        desc += f"; dK/dV items of {key_tile} keys"
     run = Runner(lcm, torch, dev, cases, fused=fused)
 
     if args.copy_calibration_mib:

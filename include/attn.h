@@ -116,6 +116,10 @@ typedef struct {
   int32_t dynamic;               /* 0, or 1 (needs block_bitmap): the bitmap
                                     may later be replaced by
                                     attn_plan_set_bitmap                         */
+  int32_t bwd_key_tile;          /* keys per dK/dV work item: 0 lets the plan
+                                    choose, else 128 or 64 (64 needs
+                                    dynamic = 0).  Results do not depend on it
+                                    beyond fp32 summation order.               */
 } attn_mask_desc;
 
 typedef struct attn_plan attn_plan;

@@ -32,7 +32,7 @@ class MaskDesc(C.Structure):
                 ("cu_seqlens", P32), ("prefix_lens", P32), ("col_bounds", P32),
                 ("block_bitmap", PU8), ("bitmap_heads", C.c_int32), ("n_qblk", C.c_int32),
                 ("n_kblk", C.c_int32), ("q_blk_offsets", P32), ("k_blk_offsets", P32),
-                ("dynamic", C.c_int32)]
+                ("dynamic", C.c_int32), ("bwd_key_tile", C.c_int32)]
 
 
 class Stats(C.Structure):

@@ -235,6 +235,7 @@ BwdArgs bwd_args(const attn_plan *p, const void *q, const void *k, const void *v
   a.n_bitems = (int)p->lay.n_bwd_items;
   a.n_breduce = (int)p->lay.n_bwd_reduce;
   a.n_slots = (int)p->lay.n_slots;
+  a.key_tile = p->bwd_keys;
   a.m = mask_args(p);
   return a;
 }
@@ -341,6 +342,9 @@ attn_status bwd_impl(const attn_plan *p, const void *q, const void *k, const voi
   LCM_CHECK(check_tensor(dk, "dk", 16));
   LCM_CHECK(check_tensor(dv, "dv", 16));
   LCM_CHECK(check_ws(p, ws, ws_bytes, fused));
+  if (fused && p->bwd_keys != kBwdKeyTile)
+    return fail(ATTN_ERR_UNSUPPORTED, "the fused dQ pass needs 128-key dK/dV items (this plan has %d)",
+                p->bwd_keys);
   if (forced_device_error()) return fail(ATTN_ERR_DEVICE, "forced device error (ATTN_FORCE_DEVICE_ERROR)");
   BwdArgs a = bwd_args(p, q, k, v, o, lse, dout, dq, dk, dv, ws);
   if (!fused) a.dqacc = nullptr;  // the recompute pass needs no accumulator

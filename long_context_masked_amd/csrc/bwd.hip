@@ -118,8 +118,19 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
 // again in stage st + 3, after the barrier of stage st + 2 that every wave
 // reaches only once its reads are done.
 // ---------------------------------------------------------------------------
-template <int D, bool FDQ>
-__global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
+//
+// NW = 2 (narrow items): 64 keys per work item, two waves, and two LDS stage
+// buffers instead of three, so that two workgroups share a CU (one wave per
+// SIMD either way).  For masks that leave one 64-key half of many 128-key
+// tiles empty (64-wide bitmap blocks), a 128-key item would spend half its
+// products on masked keys in those stages.  With two buffers, stage st + 2
+// can only be loaded once every wave has finished reading stage st, so its
+// loads are issued after a second barrier at the end of stage st, into
+// stage st's buffer.
+template <int D, bool FDQ, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(BwdArgs a) {
+  static_assert(NW == 4 || (NW == 2 && !FDQ), "narrow items have no fused dQ variant");
+  constexpr int KT = 32 * NW;   // keys per work item
   constexpr int KS = D / 16;    // k-steps of A (two MFMAs each: S and dP)
   constexpr int DB = D / 32;    // 32-row blocks of dK^T / dV^T
   constexpr int NC = 2 * DB;    // chunks of C (two MFMAs each: dV and dK)
@@ -127,7 +138,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   using T64 = Tile<64>;
   constexpr int OFF_DO = T::BYTES, OFF_L = 2 * T::BYTES, OFF_D = OFF_L + 256;
   constexpr int STAGE = 2 * T::BYTES + 1024;
-  constexpr int NBUF = 3;
+  constexpr int NBUF = NW == 4 ? 3 : 2;
   // k-steps of A operands read ahead (the fused pass gives the registers of
   // two of them to its dQ phase)
   constexpr int PF = KS < (FDQ ? 2 : 4) ? KS : (FDQ ? 2 : 4);
@@ -144,7 +155,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   const int b = blockIdx.y;
   const int S = a.S, G = a.G;
   const int kvh = item.y;
-  const int key = item.x * 128 + wave * 32 + ln;
+  const int key = item.x * KT + wave * 32 + ln;
   const bool key_ok = key < S;
   const int64_t ldq = (int64_t)a.Hq * D, ldk = (int64_t)a.Hkv * D;
 
@@ -163,7 +174,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
   // K[16t + 8 + 4hh + {0..3}] at column 32 (wave % DB) + ln, the key order in
   // which the transposed reads of the dS tile hand over the k index.
   const int dqb = wave % DB, rb0 = (wave / DB) * RBW;
-  bf16x8 kq[FDQ ? 8 : 1];
+  bf16x8 kq[8];  // unused (and dropped) without FDQ
   if constexpr (FDQ) {
     const bf16 *kc = a.k + (int64_t)b * S * ldk + (int64_t)kvh * D + dqb * 32 + ln;
 #pragma unroll
@@ -194,26 +205,26 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
 
   const auto *list = as_const(a.blist + item.z);
   const int nst = item.w * G;
-  TileDma<D> dma;
+  TileDma<D, NW> dma;
   dma.init(ldq);
 
   // Loads of stage st into `stg`: the Q and dO tiles of head kvh*G + g, and
-  // 64 rows each of lse2 and D (lanes 0..7 of every wave, 16 bytes each), so
-  // that every wave issues the same number of loads per stage.
+  // 64 rows each of lse2 and D (32 / NW lanes of every wave, 16 bytes each),
+  // so that every wave issues the same number of loads per stage.
   auto load_stage = [&](int st, char *stg, uint32_t ent) {
     const int e = st / G, g = st - e * G;
     const int qt = (int)(ent & 0x7fffffffu);
     const int h = kvh * G + g;
     dma.load(stg, a.q + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
     dma.load(stg + OFF_DO, a.dout + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
-    if (lane < 8) {
-      const int q = wave * 8 + lane;
+    if (lane < 32 / NW) {
+      const int q = wave * (32 / NW) + lane;
       const float *src =
           a.ws + ws_row0(b, h, a.Hq, a.S64) + (q >> 4) * a.S64 + qt * 64 + (q & 15) * 4;
       __builtin_amdgcn_global_load_lds(
           src,
           (__attribute__((address_space(3))) void *)((__attribute__((address_space(3))) char *)stg +
-                                                      OFF_L + wave * 128),
+                                                      OFF_L + wave * (512 / NW)),
           16, 0, 0);
     }
   };
@@ -530,10 +541,13 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
     bf16x8 pb1[2], dsb1[2];
     b_pack(s1, dp1, 0, pb1[0], dsb1[0]);
 
-    // stage st + 1 is in LDS for every wave, and stage st - 1's buffer is free
+    // stage st + 1 is in LDS for every wave (three buffers: and stage st - 1's
+    // buffer is free)
     dma_wait();
     __syncthreads();
-    if (st + 2 < nst) load_stage(st + 2, smem + fre * STAGE, ent2);
+    if constexpr (NBUF == 3) {
+      if (st + 2 < nst) load_stage(st + 2, smem + fre * STAGE, ent2);
+    }
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       aq[i] = rows_q(nbuf, 0, i);
@@ -591,6 +605,13 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdArgs a) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NBUF == 2) {
+      // every wave is done with stage st's buffer: it receives stage st + 2
+      if (st + 2 < nst) {
+        __syncthreads();
+        load_stage(st + 2, smem + cur * STAGE, ent2);
+      }
     }
     if constexpr (FDQ) {
       // ---- phase 4: dQ of stage st - 1 (its dS tile was completed by every
@@ -665,8 +686,8 @@ __global__ __launch_bounds__(256) void attn_dkdv_reduce_kernel(BwdArgs a) {
   for (int i = threadIdx.x; i < 2 * PER; i += blockDim.x) {
     const int which = i / PER, j = i - which * PER;
     const int kl = j / (D / 4), d0 = (j - kl * (D / 4)) * 4;
-    const int key = r.x * kDkdvKeys + kl;
-    if (key >= a.S) continue;
+    const int key = r.x * a.key_tile + kl;  // a slot holds 128 keys; narrow items use 64
+    if (kl >= a.key_tile || key >= a.S) continue;
     const float *src = base + (int64_t)which * kDkdvKeys * D + (int64_t)kl * D + d0;
     f32x4 acc = *reinterpret_cast<const f32x4 *>(src);
     for (int c = 1; c < r.w; ++c)
@@ -894,10 +915,12 @@ template __global__ void attn_bwd_pre_kernel<128>(const bf16 *, const bf16 *, co
                                                   float *, float *, int, int, int, int64_t);
 template __global__ void attn_bwd_pre_kernel<64>(const bf16 *, const bf16 *, const float *,
                                                  float *, float *, int, int, int, int64_t);
-template __global__ void attn_dkdv_kernel<128, false>(BwdArgs);
-template __global__ void attn_dkdv_kernel<64, false>(BwdArgs);
-template __global__ void attn_dkdv_kernel<128, true>(BwdArgs);
-template __global__ void attn_dkdv_kernel<64, true>(BwdArgs);
+template __global__ void attn_dkdv_kernel<128, false, 4>(BwdArgs);
+template __global__ void attn_dkdv_kernel<64, false, 4>(BwdArgs);
+template __global__ void attn_dkdv_kernel<128, true, 4>(BwdArgs);
+template __global__ void attn_dkdv_kernel<64, true, 4>(BwdArgs);
+template __global__ void attn_dkdv_kernel<128, false, 2>(BwdArgs);
+template __global__ void attn_dkdv_kernel<64, false, 2>(BwdArgs);
 template __global__ void attn_dq_convert_kernel<128>(const float *, bf16 *, int, int, int, float, int64_t);
 template __global__ void attn_dq_convert_kernel<64>(const float *, bf16 *, int, int, int, float, int64_t);
 template __global__ void attn_dkdv_reduce_kernel<128>(BwdArgs);
@@ -940,11 +963,15 @@ hipError_t launch_dq_convert(const BwdArgs &a, int d, int B, hipStream_t st) {
 }
 
 hipError_t launch_dkdv(const BwdArgs &a, int d, int B, bool fused_dq, hipStream_t st) {
-  const dim3 grid((unsigned)a.n_bitems, (unsigned)B), block(256);
-  if (d == 128 && fused_dq) hipLaunchKernelGGL((attn_dkdv_kernel<128, true>), grid, block, 0, st, a);
-  else if (d == 128) hipLaunchKernelGGL((attn_dkdv_kernel<128, false>), grid, block, 0, st, a);
-  else if (d == 64 && fused_dq) hipLaunchKernelGGL((attn_dkdv_kernel<64, true>), grid, block, 0, st, a);
-  else if (d == 64) hipLaunchKernelGGL((attn_dkdv_kernel<64, false>), grid, block, 0, st, a);
+  const dim3 grid((unsigned)a.n_bitems, (unsigned)B), block(256), narrow(128);
+  if (a.key_tile == 64 && fused_dq) return hipErrorInvalidValue;
+  if (a.key_tile == 64 && d == 128) hipLaunchKernelGGL((attn_dkdv_kernel<128, false, 2>), grid, narrow, 0, st, a);
+  else if (a.key_tile == 64 && d == 64) hipLaunchKernelGGL((attn_dkdv_kernel<64, false, 2>), grid, narrow, 0, st, a);
+  else if (a.key_tile != 128) return hipErrorInvalidValue;
+  else if (d == 128 && fused_dq) hipLaunchKernelGGL((attn_dkdv_kernel<128, true, 4>), grid, block, 0, st, a);
+  else if (d == 128) hipLaunchKernelGGL((attn_dkdv_kernel<128, false, 4>), grid, block, 0, st, a);
+  else if (d == 64 && fused_dq) hipLaunchKernelGGL((attn_dkdv_kernel<64, true, 4>), grid, block, 0, st, a);
+  else if (d == 64) hipLaunchKernelGGL((attn_dkdv_kernel<64, false, 4>), grid, block, 0, st, a);
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_breduce == 0) return e;

@@ -63,6 +63,7 @@ attn_status make_key(const attn_shape *sh, const attn_mask_desc *d, std::string 
   std::memcpy(&sc, &sh->scale, 4);
   put(k, sc);
   put(k, d->kind); put(k, d->causal); put(k, d->window_left); put(k, d->window_right);
+  put(k, d->bwd_key_tile);
   if (d->kind == ATTN_MASK_DOCUMENT || d->kind == ATTN_MASK_PREFIX_LM) {
     if (d->num_docs < 1 || !d->cu_seqlens) return fail(ATTN_ERR_INVALID, "num_docs must be >= 1 with cu_seqlens");
     put(k, d->num_docs);

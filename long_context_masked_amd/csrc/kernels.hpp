@@ -356,6 +356,7 @@ struct BwdArgs {
   const int4 *breduce;  // per split item: K-tile, KV head, first slot, chunks
   float *part;          // partial dK/dV: [B][n_slots][2][128 keys][d] fp32
   float *dqacc;         // fused dQ accumulator [B][S64][Hq][d] fp32, or null
+  int key_tile;         // keys per dK/dV item: 128 (four waves) or 64 (two waves)
   int n_fitems, n_bitems, n_breduce, n_slots;
   MaskArgs m;
 };

@@ -391,6 +391,11 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   if (desc->dynamic != 0 && desc->dynamic != 1) return fail(ATTN_ERR_INVALID, "dynamic must be 0 or 1");
   const bool dynamic = desc->dynamic == 1;
   if (dynamic && !has_bm) return fail(ATTN_ERR_INVALID, "dynamic = 1 needs a block_bitmap");
+  const int want_keys = desc->bwd_key_tile;
+  if (want_keys != 0 && want_keys != 64 && want_keys != 128)
+    return fail(ATTN_ERR_INVALID, "bwd_key_tile must be 0, 64 or 128");
+  if (want_keys == 64 && dynamic)
+    return fail(ATTN_ERR_UNSUPPORTED, "bwd_key_tile = 64 needs dynamic = 0");
   if (has_bm) {
     const int nh = desc->bitmap_heads;
     if (nh != 1 && nh != sh.Hkv && nh != sh.Hq)
@@ -435,21 +440,46 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   const int64_t nM = (S + kMicro - 1) / kMicro;
   const int MR = p->fwd_rows / kMicro;                     // micro rows per fwd tile
   const int64_t nFQ = (S + p->fwd_rows - 1) / p->fwd_rows;  // fwd Q tiles
-  const int MC = kBwdKeyTile / kMicro;                     // micro cols per bwd tile
-  const int64_t nBK = (S + kBwdKeyTile - 1) / kBwdKeyTile;  // bwd K tiles
   const int n_mask_heads = has_bm ? bm.heads : 1;
   auto hm_of = [&](int64_t h) -> int {
     if (!has_bm || bm.heads == 1) return 0;
     if (bm.heads == sh.Hkv) return (int)(h / G);
     return (int)h;
   };
+  const bool per_qhead = has_bm && bm.heads == sh.Hq && G > 1;
+  // Keys per dK/dV item.  A 128-key item runs both 64-key halves of every
+  // listed Q-tile; where one half is empty (bitmap blocks 64 keys wide) its
+  // products are masked work.  Narrow 64-key items skip such halves at the
+  // price of fetching each Q/dO tile for 64 keys instead of 128, so the
+  // plan takes them when, on the mask heads of the first dK/dV item group,
+  // more than a quarter of the listed 128-key stages have an empty half.
+  p->bwd_keys = kBwdKeyTile;
+  if (want_keys != 0) {
+    p->bwd_keys = want_keys;
+  } else if (has_bm && !dynamic && nM > 1) {
+    std::vector<std::vector<uint8_t>> cls0(per_qhead ? (size_t)G : 1);
+    for (size_t g = 0; g < cls0.size(); ++g) classify_bitmap(S, base, bm, (int)g, cls0[g]);
+    int64_t listed = 0, half = 0;
+    for (int64_t I = 0; I < nM; ++I)
+      for (int64_t J = 0; J + 1 < nM; J += 2) {
+        bool a0 = false, a1 = false;
+        for (const auto &c : cls0) {
+          a0 |= c[(size_t)(I * nM + J)] != kEmpty;
+          a1 |= c[(size_t)(I * nM + J + 1)] != kEmpty;
+        }
+        listed += a0 || a1;
+        half += a0 != a1;
+      }
+    if (4 * half > listed) p->bwd_keys = 64;
+  }
+  const int MC = p->bwd_keys / kMicro;                       // micro cols per bwd tile
+  const int64_t nBK = (S + p->bwd_keys - 1) / p->bwd_keys;  // bwd K tiles
   // Work lists are built per list group: the mask heads one work item covers.
   // With one bitmap per query head under GQA, a forward item covers the HG
   // mask heads of its query heads and a dK/dV item the G heads of its KV
   // head; a tile is listed if any of them allows a pair in it, and full only
   // if it is full for all of them (the kernels mask per query head).
   // Otherwise every item covers a single mask head and a group is that head.
-  const bool per_qhead = has_bm && bm.heads == sh.Hq && G > 1;
   const int n_fgroups = per_qhead ? (int)(sh.Hq / p->HG) : n_mask_heads;
   const int n_bgroups = per_qhead ? (int)sh.Hkv : n_mask_heads;
   auto fgroup_of = [&](int64_t h0) -> int { return per_qhead ? (int)(h0 / p->HG) : hm_of(h0); };
@@ -617,7 +647,8 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   {
     double total = 0.0;
     for (const Item &x : bi) total += x.cost;
-    const double share = total * (double)sh.B / kSplitTarget;
+    // two narrow workgroups are resident per CU
+    const double share = total * (double)sh.B / (kSplitTarget * (kBwdKeyTile / p->bwd_keys));
     std::vector<Item> split;
     std::vector<int32_t> sl;
     int32_t slots = 0;
@@ -783,7 +814,7 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   s.fwd_tile_rows = p->fwd_rows;
   s.fwd_tile_cols = kFwdKeyTile;
   s.bwd_tile_rows = kBwdRowTile;
-  s.bwd_tile_cols = kBwdKeyTile;
+  s.bwd_tile_cols = p->bwd_keys;
   s.heads_per_item = p->HG;
   s.device_bytes = L.total;
   *out = p;

@@ -14,7 +14,7 @@ namespace lcm {
 // tile is a whole number of them.
 constexpr int kMicro = 64;
 constexpr int kFwdKeyTile = 64;   // forward / dQ: keys per K-tile
-constexpr int kBwdKeyTile = 128;  // dK/dV: keys per workgroup (4 waves x 32)
+constexpr int kBwdKeyTile = 128;  // dK/dV: keys per workgroup (4 waves x 32); narrow items: 64
 constexpr int kBwdRowTile = 64;   // dK/dV: query rows per Q-tile
 constexpr int kWgRowsHeads = 128; // forward / dQ: (rows x heads) per workgroup
 
@@ -69,6 +69,7 @@ struct attn_plan {
   int G = 1;            // query heads per KV head
   int HG = 1;           // query heads per forward / dQ workgroup
   int fwd_rows = 128;   // query rows per forward / dQ workgroup
+  int bwd_keys = 128;   // keys per dK/dV work item: 128, or 64 (two waves)
   int bitmap_heads = 0; // 0 = no bitmap
   int nqb = 0, nkb = 0;
   std::vector<uint8_t> blob;  // host copy of the device blob

@@ -155,6 +155,7 @@ class MaskDescriptor:
             d.q_blk_offsets = self._ptr32(_i32(bm["q_offsets"]))
             d.k_blk_offsets = self._ptr32(_i32(bm["k_offsets"]))
         d.dynamic = 1 if spec.get("dynamic") else 0
+        d.bwd_key_tile = int(spec.get("bwd_key_tile", 0))
         d._arrays = self._keep   # the struct keeps the arrays it points to alive
         self.c = d
 

@@ -88,7 +88,8 @@ def _check_items(dl, fresh_layout, Hkv):
 
 
 def _check_lists_equal(dyn, spec_new, B, Hq, Hkv, d, bits_new):
-    ref = lcm.Plan(B, spec_new["S"], Hq, Hkv, d, spec_new)
+    # dynamic plans run 128-key dK/dV items; so does the ordinary plan here
+    ref = lcm.Plan(B, spec_new["S"], Hq, Hkv, d, dict(spec_new, bwd_key_tile=128))
     fs, bs = lists_by_item(ref.layout())
     dl = dyn.device_layout()
     fd, bd = lists_by_item(dl)
@@ -249,7 +250,7 @@ def test_fullsize_sparse_32k_gqa(blk, heads):
     _, b2 = syn.uniform_block_bitmap(S, blk, heads, 0.5, seed=2)
     base = syn.spec_full(S)
     dyn = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b1), dynamic=True))
-    static = lcm.Plan(1, S, Hq, Hkv, d, syn.with_bitmap(base, offs, offs, b2))
+    static = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b2), bwd_key_tile=128))
     dyn.bind()
     dyn.set_bitmap(_dev_bits(b2))
     dl = dyn.device_layout()

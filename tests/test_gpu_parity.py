@@ -23,6 +23,7 @@ if not torch.cuda.is_available():  # pragma: no cover
     pytest.skip("no GPU", allow_module_level=True)
 
 import long_context_masked_amd as lcm  # noqa: E402
+from long_context_masked_amd import _lib as L  # noqa: E402
 
 
 def run_case(spec, B, Hq, Hkv, d, seed=0, check_bwd=True, x=None):
@@ -207,6 +208,7 @@ def test_atomic_and_separate_dq_paths_both_match_the_oracle():
     cases = [(syn.spec_causal(333), 1, 6, 2, 128), (RAGGED_GQA[12][1], 1, 8, 1, 128),
              (dict(TINY)["varblock_50"], 2, 4, 2, 64)]
     for spec, B, Hq, Hkv, d in cases:
+        spec = dict(spec, bwd_key_tile=128)  # the fused dQ pass runs on 128-key items
         S = spec["S"]
         print(f"atomic vs separate dQ: {spec['family']} S={S} Hq={Hq} Hkv={Hkv} d={d}", flush=True)
         x = syn.attention_inputs(B, S, Hq, Hkv, d, 9)
@@ -221,6 +223,59 @@ def test_atomic_and_separate_dq_paths_both_match_the_oracle():
             gate("dQ", to_f64(g[0]), ref["dq"], ref["m_dq"])
             gate("dK", to_f64(g[1]), ref["dk"], ref["m_dk"])
             gate("dV", to_f64(g[2]), ref["dv"], ref["m_dv"])
+
+
+def _narrow_cases():
+    S1, S2, S3 = 1000, 1500, 900
+    uo, ub = syn.uniform_block_bitmap(S2, 64, 2, 0.5, seed=31)
+    vo, vb = syn.variable_block_bitmap(S3, 32, 224, 2, 0.5, seed=32)
+    po, pb = syn.uniform_block_bitmap(700, 64, 8, 0.5, seed=33)
+    return [
+        ("causal_ragged_d64", dict(syn.spec_causal(S1), bwd_key_tile=64), 1, 4, 2, 64),
+        ("block64_gqa_auto", syn.with_bitmap(syn.spec_full(S2), uo, uo, ub), 1, 8, 2, 128),
+        ("varblock_mha", dict(syn.with_bitmap(syn.spec_causal(S3), vo, vo, vb), bwd_key_tile=64), 1, 2, 2, 128),
+        ("per_query_head_gqa", dict(syn.with_bitmap(syn.spec_causal(700), po, po, pb), bwd_key_tile=64),
+         1, 8, 2, 128),
+        ("global_sliding_split", dict(syn.spec_global_sliding(2048, 64, 256), bwd_key_tile=64), 1, 16, 2, 128),
+        ("document_batch2", dict(syn.spec_document(syn.sample_doc_lens(640, 8, 200, 5), True), bwd_key_tile=64),
+         2, 4, 2, 64),
+    ]
+
+
+@pytest.mark.parametrize("label,spec,B,Hq,Hkv,d", _narrow_cases(), ids=[c[0] for c in _narrow_cases()])
+def test_narrow_dkdv_items(label, spec, B, Hq, Hkv, d):
+    """64-key dK/dV items (two waves, two stage buffers): ragged S, both head
+    dims, GQA and MHA, bitmaps per KV head and per query head, split items
+    and a batch of two, against the oracle."""
+    p = lcm.Plan(B, spec["S"], Hq, Hkv, d, spec)
+    assert p.stats["bwd_tile_cols"] == 64
+    if label == "global_sliding_split":
+        assert p.layout()["n_slots"] > 0
+    run_case(spec, B, Hq, Hkv, d, seed=34)
+
+
+@pytest.mark.parametrize("label,spec", [
+    ("full", syn.spec_full(8192)), ("causal_sw1024", syn.spec_sliding(8192, 1024, True))])
+def test_narrow_and_wide_dkdv_items_agree(label, spec):
+    """Without split items, a key's dK and dV sum the same products in the
+    same order whether its item spans 64 or 128 keys (a listed tile that a
+    64-key item skips adds exact zeros to the 128-key item's sums), so the
+    two plans give equal dK and dV; dQ has its own pass and equal bits."""
+    S, Hq, Hkv, d = spec["S"], 16, 8, 128
+    x = syn.attention_inputs(1, S, Hq, Hkv, d, 35)
+    q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
+    wide = lcm.Plan(1, S, Hq, Hkv, d, dict(spec, bwd_key_tile=128))
+    narrow = lcm.Plan(1, S, Hq, Hkv, d, dict(spec, bwd_key_tile=64))
+    assert wide.layout()["n_slots"] == 0 and narrow.layout()["n_slots"] == 0
+    o, lse = lcm.fwd(wide, q, k, v)
+    gw = lcm.bwd(wide, q, k, v, o, lse, do)
+    gn = lcm.bwd(narrow, q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), gw, gn):
+        assert torch.equal(a, b), name
+    with pytest.raises(lcm.AttnError) as ei:
+        lcm.bwd(narrow, q, k, v, o, lse, do, atomic_dq=True)
+    assert ei.value.status == L.ATTN_ERR_UNSUPPORTED
 
 
 def test_forced_device_error_leaves_outputs_untouched(monkeypatch):

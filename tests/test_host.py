@@ -208,6 +208,58 @@ def test_work_lists_ragged_and_head_groupings(Hq, Hkv):
         _check_lists(lcm.Plan(1, S, Hq, Hkv, 128, spec), spec, Hq, Hkv)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (3, 1), (8, 2)])
+def test_narrow_dkdv_items_cover_mask_exactly(Hq, Hkv):
+    """Forced 64-key dK/dV items (bwd_key_tile = 64): the same exact-cover
+    checks, over 64-key columns, for static families, ragged S and the
+    bitmap head groupings."""
+    S = 200
+    specs = [dict(s, bwd_key_tile=64) for s in _family_specs(S, 4)[:12]]
+    offs, bits = syn.variable_block_bitmap(S, 20, 90, Hkv, 0.5, seed=8)
+    specs.append(dict(syn.with_bitmap(syn.spec_causal(S), offs, offs, bits), bwd_key_tile=64))
+    offs, bits = syn.uniform_block_bitmap(S, 64, Hq, 0.5, seed=9)
+    specs.append(dict(syn.with_bitmap(syn.spec_full(S), offs, offs, bits), bwd_key_tile=64))
+    for spec in specs:
+        p = lcm.Plan(1, S, Hq, Hkv, 128, spec)
+        assert p.stats["bwd_tile_cols"] == 64
+        _check_lists(p, spec, Hq, Hkv)
+
+
+def _empty_half_fraction(spec, S):
+    """Of the 128-key (64-row, 128-key) tiles with an allowed pair, the
+    fraction whose 64-key halves are not both non-empty: brute force over
+    the oracle's dense mask of mask head 0."""
+    m = om.dense_mask(spec, 0)
+    listed = half = 0
+    for r in range(0, S, 64):
+        for c in range(0, S - 127, 128):
+            a0, a1 = m[r:r + 64, c:c + 64].any(), m[r:r + 64, c + 64:c + 128].any()
+            listed += a0 or a1
+            half += a0 != a1
+    return half / listed
+
+
+@pytest.mark.parametrize("label,block,density,narrow", [
+    ("block64_50", 64, 0.5, True), ("block64_90", 64, 0.9, False),
+    ("block128_50", 128, 0.5, False), ("block256_30", 256, 0.3, False),
+])
+def test_dkdv_key_tile_choice(label, block, density, narrow):
+    """With bwd_key_tile = 0 the plan takes 64-key dK/dV items exactly when
+    more than a quarter of the listed 128-key tiles of mask head 0 have an
+    empty 64-key half; masks without a bitmap, dynamic plans and an explicit
+    128 keep 128-key items."""
+    S = 2048
+    offs, bits = syn.uniform_block_bitmap(S, block, 1, density, 3)
+    spec = syn.with_bitmap(syn.spec_full(S), offs, offs, bits)
+    frac = _empty_half_fraction(spec, S)
+    assert (frac > 0.25) == narrow, frac
+    assert lcm.Plan(1, S, 8, 2, 128, spec).stats["bwd_tile_cols"] == (64 if narrow else 128)
+    assert lcm.Plan(1, S, 8, 2, 128, dict(spec, bwd_key_tile=128)).stats["bwd_tile_cols"] == 128
+    assert lcm.Plan(1, S, 8, 2, 128, dict(spec, dynamic=True)).stats["bwd_tile_cols"] == 128
+    assert lcm.Plan(1, S, 8, 2, 128, syn.spec_causal(S)).stats["bwd_tile_cols"] == 128
+    assert lcm.Plan(1, S, 8, 2, 128, dict(syn.spec_causal(S), bwd_key_tile=64)).stats["bwd_tile_cols"] == 64
+
+
 def _lpt_makespan(costs, m):
     loads = np.zeros(m)
     for c in costs:
@@ -366,6 +418,12 @@ def test_plan_create_errors():
     bad_offs = np.array([0, 64, 64, 192, 256], dtype=np.int32)
     d.c.q_blk_offsets = bad_offs.ctypes.data_as(L.P32)
     assert _create((1, S, 4, 4, 64, 0.0), d.c) == L.ATTN_ERR_INVALID
+    # keys per dK/dV item: 0, 64 or 128; 64 only on static plans
+    for tile, want in ((64, L.ATTN_OK), (128, L.ATTN_OK), (32, L.ATTN_ERR_INVALID), (-1, L.ATTN_ERR_INVALID)):
+        assert _create((1, S, 4, 2, 64, 0.0), desc(syn.spec_causal(S), bwd_key_tile=tile).c) == want
+    offs, bits = syn.uniform_block_bitmap(S, 64, 1, 0.5, 0)
+    d = desc(dict(syn.with_bitmap(syn.spec_full(S), offs, offs, bits), dynamic=True), bwd_key_tile=64)
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_UNSUPPORTED
 
 
 def test_launch_entry_points_validate_before_touching_the_gpu():
@@ -453,10 +511,11 @@ def _dynamic_cases():
 @pytest.mark.parametrize("label,spec,Hq,Hkv", _dynamic_cases(), ids=[c[0] for c in _dynamic_cases()])
 def test_dynamic_plan_lists_equal_static(label, spec, Hq, Hkv):
     """A dynamic plan lists the same tiles, entry for entry, as the ordinary
-    plan for its creation bitmap; each list sits at slot * nM (room for every
-    tile of its row or column) and no dK/dV item is split."""
+    plan for its creation bitmap (with 128-key dK/dV items, the only width
+    of dynamic plans); each list sits at slot * nM (room for every tile of
+    its row or column) and no dK/dV item is split."""
     S = spec["S"]
-    static = lcm.Plan(1, S, Hq, Hkv, 64, spec)
+    static = lcm.Plan(1, S, Hq, Hkv, 64, dict(spec, bwd_key_tile=128))
     dyn = lcm.Plan(1, S, Hq, Hkv, 64, dict(spec, dynamic=True))
     ls, ld = static.layout(), dyn.layout()
     fs, bs = lists_by_item(ls)
