@@ -117,9 +117,9 @@ typedef struct {
                                     may later be replaced by
                                     attn_plan_set_bitmap                         */
   int32_t bwd_key_tile;          /* keys per dK/dV work item: 0 lets the plan
-                                    choose, else 128 or 64 (64 needs
-                                    dynamic = 0).  Results do not depend on it
-                                    beyond fp32 summation order.               */
+                                    choose, else 128 or 64.  Results do not
+                                    depend on it beyond fp32 summation
+                                    order.                                     */
 } attn_mask_desc;
 
 typedef struct attn_plan attn_plan;
@@ -140,7 +140,13 @@ typedef struct {
  * Compile the mask for `shape`: validate, classify every (Q-tile, K-tile)
  * pair as empty, full or partial, build the per-Q-tile (forward, dQ) and
  * per-K-tile (dK/dV) work lists and order them longest-first.  Host only: no
- * HIP call is made.  On success *out owns host memory only.
+ * HIP call is made.  On success *out owns host memory only.  A dK/dV work
+ * item spans 128 keys, or 64 (two waves) when desc->bwd_key_tile = 64 or,
+ * with bwd_key_tile = 0, when more than a quarter of the listed 128-key
+ * tiles of the first item group have an empty 64-key half (bitmap blocks 64
+ * keys wide; a dynamic plan decides on its creation bitmap);
+ * stats.bwd_tile_cols reports it.  bwd_key_tile outside {0, 64, 128} is
+ * ATTN_ERR_INVALID.
  */
 attn_status attn_plan_create(const attn_shape *shape, const attn_mask_desc *desc,
                              attn_plan **out);
@@ -262,7 +268,9 @@ attn_status attn_bwd(const attn_plan *plan, const void *q, const void *k,
  * measured on MI355X it is about half as fast as attn_bwd, so attn_bwd is
  * the default.  The order of the atomic additions varies, so dQ may differ
  * in its last bit from run to run.  Same arguments as attn_bwd, with `ws` of
- * at least attn_bwd_atomic_workspace_bytes(plan) bytes.
+ * at least attn_bwd_atomic_workspace_bytes(plan) bytes.  Needs 128-key dK/dV
+ * items: a plan with 64-key items returns ATTN_ERR_UNSUPPORTED before any
+ * launch.
  */
 attn_status attn_bwd_atomic_dq(const attn_plan *plan, const void *q, const void *k,
                                const void *v, const void *o, const float *lse,

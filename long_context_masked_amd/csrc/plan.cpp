@@ -394,8 +394,6 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   const int want_keys = desc->bwd_key_tile;
   if (want_keys != 0 && want_keys != 64 && want_keys != 128)
     return fail(ATTN_ERR_INVALID, "bwd_key_tile must be 0, 64 or 128");
-  if (want_keys == 64 && dynamic)
-    return fail(ATTN_ERR_UNSUPPORTED, "bwd_key_tile = 64 needs dynamic = 0");
   if (has_bm) {
     const int nh = desc->bitmap_heads;
     if (nh != 1 && nh != sh.Hkv && nh != sh.Hq)
@@ -452,11 +450,13 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   // products are masked work.  Narrow 64-key items skip such halves at the
   // price of fetching each Q/dO tile for 64 keys instead of 128, so the
   // plan takes them when, on the mask heads of the first dK/dV item group,
-  // more than a quarter of the listed 128-key stages have an empty half.
+  // more than a quarter of the listed 128-key stages have an empty half.  A
+  // dynamic plan decides on its creation bitmap: the block geometry, which
+  // makes the halves empty, stays when the bits change.
   p->bwd_keys = kBwdKeyTile;
   if (want_keys != 0) {
     p->bwd_keys = want_keys;
-  } else if (has_bm && !dynamic && nM > 1) {
+  } else if (has_bm && nM > 1) {
     std::vector<std::vector<uint8_t>> cls0(per_qhead ? (size_t)G : 1);
     for (size_t g = 0; g < cls0.size(); ++g) classify_bitmap(S, base, bm, (int)g, cls0[g]);
     int64_t listed = 0, half = 0;

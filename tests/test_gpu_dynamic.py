@@ -88,14 +88,16 @@ def _check_items(dl, fresh_layout, Hkv):
 
 
 def _check_lists_equal(dyn, spec_new, B, Hq, Hkv, d, bits_new):
-    # dynamic plans run 128-key dK/dV items; so does the ordinary plan here
-    ref = lcm.Plan(B, spec_new["S"], Hq, Hkv, d, dict(spec_new, bwd_key_tile=128))
+    # the ordinary plan for the new bitmap, with the dynamic plan's dK/dV item
+    # width (chosen from its creation bitmap)
+    ref = lcm.Plan(B, spec_new["S"], Hq, Hkv, d, dict(spec_new, bwd_key_tile=dyn.stats["bwd_tile_cols"]))
     fs, bs = lists_by_item(ref.layout())
     dl = dyn.device_layout()
     fd, bd = lists_by_item(dl)
     assert fd == fs, "forward / dQ lists differ from the host compiler's"
     assert bd == bs, "dK/dV lists differ from the host compiler's"
-    fresh = lcm.Plan(B, spec_new["S"], Hq, Hkv, d, dict(spec_new, dynamic=True))
+    fresh = lcm.Plan(B, spec_new["S"], Hq, Hkv, d,
+                     dict(spec_new, dynamic=True, bwd_key_tile=dyn.stats["bwd_tile_cols"]))
     _check_items(dl, fresh.layout(), Hkv)
     return ref
 
@@ -250,7 +252,8 @@ def test_fullsize_sparse_32k_gqa(blk, heads):
     _, b2 = syn.uniform_block_bitmap(S, blk, heads, 0.5, seed=2)
     base = syn.spec_full(S)
     dyn = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b1), dynamic=True))
-    static = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b2), bwd_key_tile=128))
+    static = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b2),
+                                             bwd_key_tile=dyn.stats["bwd_tile_cols"]))
     dyn.bind()
     dyn.set_bitmap(_dev_bits(b2))
     dl = dyn.device_layout()
@@ -258,7 +261,8 @@ def test_fullsize_sparse_32k_gqa(blk, heads):
     (gk, gl, ge), (ck, cl, ce) = concat_lists(static.layout())
     assert np.array_equal(fk, gk) and np.array_equal(fl, gl) and np.array_equal(fe, ge)
     assert np.array_equal(bk, ck) and np.array_equal(bl, cl) and np.array_equal(be, ce)
-    fresh = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b2), dynamic=True))
+    fresh = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b2), dynamic=True,
+                                            bwd_key_tile=dyn.stats["bwd_tile_cols"]))
     _check_items(dl, fresh.layout(), Hkv)   # longest first, as a fresh plan
     del fresh
     x = syn.attention_inputs(1, S, Hq, Hkv, d, 7)
@@ -291,7 +295,8 @@ def test_share_above_sort_cap_keeps_natural_order():
     dyn.set_bitmap(_dev_bits(b2))
     from plan_util import concat_lists
     dl = dyn.device_layout()
-    fresh = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b2), dynamic=True))
+    fresh = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b2), dynamic=True,
+                                            bwd_key_tile=dyn.stats["bwd_tile_cols"]))
     fl = fresh.layout()
     for (a, b) in zip(concat_lists(dl), concat_lists(fl)):
         assert all(np.array_equal(x, y) for x, y in zip(a, b))

@@ -246,8 +246,8 @@ def _empty_half_fraction(spec, S):
 def test_dkdv_key_tile_choice(label, block, density, narrow):
     """With bwd_key_tile = 0 the plan takes 64-key dK/dV items exactly when
     more than a quarter of the listed 128-key tiles of mask head 0 have an
-    empty 64-key half; masks without a bitmap, dynamic plans and an explicit
-    128 keep 128-key items."""
+    empty 64-key half (dynamic plans likewise, on their creation bitmap);
+    masks without a bitmap and an explicit 128 keep 128-key items."""
     S = 2048
     offs, bits = syn.uniform_block_bitmap(S, block, 1, density, 3)
     spec = syn.with_bitmap(syn.spec_full(S), offs, offs, bits)
@@ -255,7 +255,7 @@ def test_dkdv_key_tile_choice(label, block, density, narrow):
     assert (frac > 0.25) == narrow, frac
     assert lcm.Plan(1, S, 8, 2, 128, spec).stats["bwd_tile_cols"] == (64 if narrow else 128)
     assert lcm.Plan(1, S, 8, 2, 128, dict(spec, bwd_key_tile=128)).stats["bwd_tile_cols"] == 128
-    assert lcm.Plan(1, S, 8, 2, 128, dict(spec, dynamic=True)).stats["bwd_tile_cols"] == 128
+    assert lcm.Plan(1, S, 8, 2, 128, dict(spec, dynamic=True)).stats["bwd_tile_cols"] == (64 if narrow else 128)
     assert lcm.Plan(1, S, 8, 2, 128, syn.spec_causal(S)).stats["bwd_tile_cols"] == 128
     assert lcm.Plan(1, S, 8, 2, 128, dict(syn.spec_causal(S), bwd_key_tile=64)).stats["bwd_tile_cols"] == 64
 
@@ -423,7 +423,7 @@ def test_plan_create_errors():
         assert _create((1, S, 4, 2, 64, 0.0), desc(syn.spec_causal(S), bwd_key_tile=tile).c) == want
     offs, bits = syn.uniform_block_bitmap(S, 64, 1, 0.5, 0)
     d = desc(dict(syn.with_bitmap(syn.spec_full(S), offs, offs, bits), dynamic=True), bwd_key_tile=64)
-    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_ERR_UNSUPPORTED
+    assert _create((1, S, 4, 2, 64, 0.0), d.c) == L.ATTN_OK
 
 
 def test_launch_entry_points_validate_before_touching_the_gpu():
@@ -511,12 +511,12 @@ def _dynamic_cases():
 @pytest.mark.parametrize("label,spec,Hq,Hkv", _dynamic_cases(), ids=[c[0] for c in _dynamic_cases()])
 def test_dynamic_plan_lists_equal_static(label, spec, Hq, Hkv):
     """A dynamic plan lists the same tiles, entry for entry, as the ordinary
-    plan for its creation bitmap (with 128-key dK/dV items, the only width
-    of dynamic plans); each list sits at slot * nM (room for every tile of
-    its row or column) and no dK/dV item is split."""
+    plan for its creation bitmap; each list sits at slot * nM (room for
+    every tile of its row or column) and no dK/dV item is split."""
     S = spec["S"]
-    static = lcm.Plan(1, S, Hq, Hkv, 64, dict(spec, bwd_key_tile=128))
+    static = lcm.Plan(1, S, Hq, Hkv, 64, spec)
     dyn = lcm.Plan(1, S, Hq, Hkv, 64, dict(spec, dynamic=True))
+    assert dyn.stats["bwd_tile_cols"] == static.stats["bwd_tile_cols"]
     ls, ld = static.layout(), dyn.layout()
     fs, bs = lists_by_item(ls)
     fd, bd = lists_by_item(ld)
