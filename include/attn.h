@@ -134,6 +134,10 @@ typedef struct {
   int64_t fwd_tile_rows, fwd_tile_cols, bwd_tile_rows, bwd_tile_cols;
   int64_t heads_per_item;  /* query heads sharing one K/V tile in fwd / dQ   */
   int64_t device_bytes;    /* size of the device blob                        */
+  int64_t bwd_head_entries; /* 1: each dK/dV list entry is one (Q-tile, query
+                              head) stage, the head in bits 24-30 (one bitmap
+                              per query head under GQA, static plans); 0: an
+                              entry is a Q-tile for all heads of the group  */
 } attn_stats;
 
 /*

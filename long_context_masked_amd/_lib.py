@@ -43,7 +43,8 @@ class Stats(C.Structure):
                 ("bwd_tiles_full", C.c_int64), ("bwd_tiles_partial", C.c_int64),
                 ("fwd_tile_rows", C.c_int64), ("fwd_tile_cols", C.c_int64),
                 ("bwd_tile_rows", C.c_int64), ("bwd_tile_cols", C.c_int64),
-                ("heads_per_item", C.c_int64), ("device_bytes", C.c_int64)]
+                ("heads_per_item", C.c_int64), ("device_bytes", C.c_int64),
+                ("bwd_head_entries", C.c_int64)]
 
 
 class Layout(C.Structure):

@@ -23,6 +23,7 @@ hipError_t launch_dyn(const DynArgs &a, hipStream_t st);
 using namespace lcm;
 
 static_assert(kDkdvKeys == kBwdKeyTile, "dK/dV tile width of the kernels and the plan");
+static_assert(kTileBits == (1u << kHeadShift) - 1u, "dK/dV list entry layout of the kernels and the plan");
 
 namespace {
 
@@ -236,6 +237,7 @@ BwdArgs bwd_args(const attn_plan *p, const void *q, const void *k, const void *v
   a.n_breduce = (int)p->lay.n_bwd_reduce;
   a.n_slots = (int)p->lay.n_slots;
   a.key_tile = p->bwd_keys;
+  a.head_entries = p->bwd_head_entries ? 1 : 0;
   a.m = mask_args(p);
   return a;
 }

@@ -204,7 +204,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(BwdArgs a) {
   const float sl2 = a.sl2;
 
   const auto *list = as_const(a.blist + item.z);
-  const int nst = item.w * G;
+  // A list entry is one Q-tile for all G query heads of the group (G stages),
+  // or, with head_entries, one (Q-tile, query head) stage whose head is in
+  // bits 24-30.
+  const int GE = a.head_entries ? 1 : G;
+  const int nst = item.w * GE;
+  auto head_of = [&](int st, uint32_t ent) -> int {
+    return a.head_entries ? (int)((ent >> 24) & 0x7fu) : st % G;
+  };
   TileDma<D, NW> dma;
   dma.init(ldq);
 
@@ -212,8 +219,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(BwdArgs a) {
   // 64 rows each of lse2 and D (32 / NW lanes of every wave, 16 bytes each),
   // so that every wave issues the same number of loads per stage.
   auto load_stage = [&](int st, char *stg, uint32_t ent) {
-    const int e = st / G, g = st - e * G;
-    const int qt = (int)(ent & 0x7fffffffu);
+    const int g = head_of(st, ent);
+    const int qt = (int)(ent & kTileBits);
     const int h = kvh * G + g;
     dma.load(stg, a.q + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
     dma.load(stg + OFF_DO, a.dout + (int64_t)b * S * ldq + (int64_t)h * D, ldq, qt * 64, S);
@@ -232,12 +239,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(BwdArgs a) {
   // Allowed-row words of the lane's key for the two units of stage st (all
   // ones unless the tile is partial); returns whether it is partial.
   auto stage_mask = [&](int st, uint32_t ent, uint32_t (&mw)[2]) -> bool {
-    const int g = st % G;
+    const int g = head_of(st, ent);
     mw[0] = 0xffffffffu;
     mw[1] = 0xffffffffu;
     const bool part = (ent >> 31) != 0;
     if (part) {
-      const int qt = (int)(ent & 0x7fffffffu);
+      const int qt = (int)(ent & kTileBits);
       const int hm = bitmap_head(a.m.bm_heads, kvh * G + g, a.Hq, G);
       const uint64_t mk = key_ok ? col_mask(a.m, cb, kblk, hm, qt * 64, S) : 0ull;
       const uint64_t sh = mk >> (4 * hh);
@@ -349,8 +356,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(BwdArgs a) {
   // accumulator, unscaled.
   auto dq_phase = [&](int sp, uint32_t entp, const char *dsbuf) {
     const uint32_t base = lds_addr(dsbuf);
-    const int g = sp % G;
-    const int qt = (int)(entp & 0x7fffffffu);
+    const int g = head_of(sp, entp);
+    const int qt = (int)(entp & kTileBits);
     const int rs = a.Hq * D;  // accumulator row stride (floats)
     // uniform base of the stage's rows for this wave's columns, plus a
     // 32-bit per-lane byte offset per atomic
@@ -408,7 +415,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(BwdArgs a) {
   bool pc = false, pn = false;  // stages st and st + 1 are partial
   if (nst > 0) {
     load_stage(0, smem, list[0]);
-    if (nst > 1) load_stage(1, smem + STAGE, list[1 / G]);
+    if (nst > 1) load_stage(1, smem + STAGE, list[1 / GE]);
     pc = stage_mask(0, list[0], mwc);
     dma_wait();
     __syncthreads();
@@ -429,7 +436,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(BwdArgs a) {
   uint32_t ent0 = nst > 0 ? list[0] : 0u, entp = 0u;
   // List entries are read a stage before they are needed, so that the
   // latency of the scalar load is covered by the products of a stage.
-  uint32_t ent1 = nst > 1 ? list[1 / G] : 0u;  // stage st + 1
+  uint32_t ent1 = nst > 1 ? list[1 / GE] : 0u;  // stage st + 1
   // The first operand rows and the LSE rows of a stage's phase 1 are read
   // during the previous stage's phase 3b (stage 0: here).
   f32x4 l0n[4];
@@ -445,7 +452,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(BwdArgs a) {
     }
   }
   for (int st = 0; st < nst; ++st) {
-    const uint32_t ent2 = st + 2 < nst ? list[(st + 2) / G] : 0u;  // stage st + 2
+    const uint32_t ent2 = st + 2 < nst ? list[(st + 2) / GE] : 0u;  // stage st + 2
 #pragma unroll
     for (int i = 0; i < DB; ++i) { in_agpr(dk[i]); in_agpr(dv[i]); }
 #pragma unroll

@@ -44,6 +44,9 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kMinit = -1.0e30f;  // finite start value of the running max
 constexpr float kEmptyRowLse2 = 1.0e30f;  // lse2 of a row with no allowed key
+// dK/dV list entry: Q-tile index in bits 0-23, the query head in bits 24-30
+// when the plan lists (Q-tile, head) stages, the partial flag in bit 31.
+constexpr uint32_t kTileBits = 0x00ffffffu;
 constexpr int kDkdvKeys = 128;      // keys per dK/dV workgroup (4 waves x 32)
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -357,6 +360,7 @@ struct BwdArgs {
   float *part;          // partial dK/dV: [B][n_slots][2][128 keys][d] fp32
   float *dqacc;         // fused dQ accumulator [B][S64][Hq][d] fp32, or null
   int key_tile;         // keys per dK/dV item: 128 (four waves) or 64 (two waves)
+  int head_entries;     // 1: dK/dV list entries name their query head (bits 24-30)
   int n_fitems, n_bitems, n_breduce, n_slots;
   MaskArgs m;
 };

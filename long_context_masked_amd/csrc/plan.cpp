@@ -430,7 +430,11 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   p->shape = sh;
   p->scale = sh.scale > 0.f ? sh.scale : (float)(1.0 / std::sqrt((double)sh.d));
   p->G = G;
-  p->HG = (G % 2 == 0) ? 2 : 1;
+  // Two query heads per forward / dQ item under GQA share each staged K/V
+  // tile; with one bitmap per query head an item's list would be the union
+  // of its heads' lists, so there an item takes one head (128 rows).
+  const bool per_qhead = has_bm && bm.heads == sh.Hq && G > 1;
+  p->HG = (G % 2 == 0 && !per_qhead) ? 2 : 1;
   p->fwd_rows = kWgRowsHeads / p->HG;
   p->bitmap_heads = has_bm ? bm.heads : 0;
   p->nqb = bm.nqb; p->nkb = bm.nkb;
@@ -444,7 +448,6 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     if (bm.heads == sh.Hkv) return (int)(h / G);
     return (int)h;
   };
-  const bool per_qhead = has_bm && bm.heads == sh.Hq && G > 1;
   // Keys per dK/dV item.  A 128-key item runs both 64-key halves of every
   // listed Q-tile; where one half is empty (bitmap blocks 64 keys wide) its
   // products are masked work.  Narrow 64-key items skip such halves at the
@@ -472,6 +475,12 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
       }
     if (4 * half > listed) p->bwd_keys = 64;
   }
+  // With one bitmap per query head, a dK/dV list of Q-tiles shared by the
+  // group would run every head of a tile that any head sees; static plans
+  // list (Q-tile, head) stages instead.  (The device list compiler of dynamic
+  // plans builds shared lists.)
+  p->bwd_head_entries = per_qhead && !dynamic && G <= kMaxEntryHeads;
+  const int GE = p->bwd_head_entries ? 1 : G;                // stages per list entry
   const int MC = p->bwd_keys / kMicro;                       // micro cols per bwd tile
   const int64_t nBK = (S + p->bwd_keys - 1) / p->bwd_keys;  // bwd K tiles
   // Work lists are built per list group: the mask heads one work item covers.
@@ -523,6 +532,24 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
         int32_t npart = 0;
         const int64_t J0 = kt * MC, J1 = std::min<int64_t>(nM, J0 + MC);
         for (int64_t I = 0; I < nM; ++I) {
+          const bool ragged = (I + 1) * kBwdRowTile > S || (J1 - J0) < MC;
+          if (p->bwd_head_entries) {
+            // one stage per (Q-tile, query head) that has an allowed pair;
+            // heads in descending order, so that the reversal below leaves
+            // them ascending within a Q-tile
+            for (size_t g = C.size(); g-- > 0;) {
+              bool any = false, all = true;
+              for (int64_t J = J0; J < J1; ++J) {
+                const uint8_t x = (*C[g])[I * nM + J];
+                any |= x != kEmpty; all &= x == kFull;
+              }
+              if (!any) continue;
+              const bool part = !all || ragged;
+              npart += part;
+              bwd_list.push_back((uint32_t)I | ((uint32_t)g << kHeadShift) | (part ? kPartialBit : 0u));
+            }
+            continue;
+          }
           bool any = false, all = true;
           for (const auto *c : C)
             for (int64_t J = J0; J < J1; ++J) {
@@ -530,7 +557,6 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
               any |= x != kEmpty; all &= x == kFull;
             }
           if (!any) continue;
-          const bool ragged = (I + 1) * kBwdRowTile > S || (J1 - J0) < MC;
           const bool part = !all || ragged;
           npart += part;
           bwd_list.push_back((uint32_t)I | (part ? kPartialBit : 0u));
@@ -627,7 +653,7 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
       const size_t slot = (size_t)bg * nBK + kt;
       const int32_t len = bwd_len[slot], np = bwd_npart[slot];
       bi.push_back({(int32_t)kt, (int32_t)kvh, (int32_t)bwd_off[slot], len,
-                    G * ((len - np) + kPartCost * np) + kItemCost});
+                    GE * ((len - np) + kPartCost * np) + kItemCost});
     }
   }
   auto by_cost = [](const Item &a, const Item &b) { return a.cost > b.cost; };
@@ -668,7 +694,7 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
         int32_t np = 0;
         for (int32_t e = a0; e < a1; ++e) np += (bwd_list[(size_t)x.off + e] & kPartialBit) != 0;
         const int32_t len = a1 - a0;
-        split.push_back({x.tile, x.head, x.off + a0, len, G * ((len - np) + kPartCost * np) + kItemCost});
+        split.push_back({x.tile, x.head, x.off + a0, len, GE * ((len - np) + kPartCost * np) + kItemCost});
         sl.push_back(slots + c);
       }
       slots += n;
@@ -809,14 +835,15 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   s.fwd_tiles_full = ffull;
   s.fwd_tiles_partial = fpart;
   s.bwd_items = L.n_bwd_items;
-  s.bwd_tiles_full = bfull * G;
-  s.bwd_tiles_partial = bpart * G;
+  s.bwd_tiles_full = bfull * GE;
+  s.bwd_tiles_partial = bpart * GE;
   s.fwd_tile_rows = p->fwd_rows;
   s.fwd_tile_cols = kFwdKeyTile;
   s.bwd_tile_rows = kBwdRowTile;
   s.bwd_tile_cols = p->bwd_keys;
   s.heads_per_item = p->HG;
   s.device_bytes = L.total;
+  s.bwd_head_entries = p->bwd_head_entries ? 1 : 0;
   *out = p;
   return ATTN_OK;
 }

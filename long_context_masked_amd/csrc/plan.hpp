@@ -19,6 +19,8 @@ constexpr int kBwdRowTile = 64;   // dK/dV: query rows per Q-tile
 constexpr int kWgRowsHeads = 128; // forward / dQ: (rows x heads) per workgroup
 
 constexpr uint32_t kPartialBit = 0x80000000u;
+constexpr int kHeadShift = 24;   // dK/dV (Q-tile, head) entries: head in bits 24-30
+constexpr int kMaxEntryHeads = 128;
 // Class of a 64x64 micro tile (stored as uint8 in a dynamic plan's blob).
 enum : uint8_t { kEmpty = 0, kPartial = 1, kFull = 2 };
 
@@ -70,6 +72,7 @@ struct attn_plan {
   int HG = 1;           // query heads per forward / dQ workgroup
   int fwd_rows = 128;   // query rows per forward / dQ workgroup
   int bwd_keys = 128;   // keys per dK/dV work item: 128, or 64 (two waves)
+  bool bwd_head_entries = false;  // dK/dV lists hold (Q-tile, query head) stages
   int bitmap_heads = 0; // 0 = no bitmap
   int nqb = 0, nkb = 0;
   std::vector<uint8_t> blob;  // host copy of the device blob

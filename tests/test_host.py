@@ -9,7 +9,7 @@ import pytest
 
 import synthetic as syn
 from oracle import masks as om
-from plan_util import lists_by_item
+from plan_util import bwd_as_shared, lists_by_item
 
 lcm = pytest.importorskip("long_context_masked_amd")
 from long_context_masked_amd import _lib as L  # noqa: E402
@@ -171,18 +171,27 @@ def _check_lists(p, spec, Hq, Hkv):
             assert [c[2] for c in ch] == list(range(slot0, slot0 + nch)), "slots follow list order"
             slots_seen.update(c[2] for c in ch)
     assert slots_seen == set(range(lay["n_slots"]))
+    # An entry is a Q-tile for all G heads, or (bwd_head_entries) one
+    # (Q-tile, head) stage with the head in bits 24-30.
+    he = bool(st["bwd_head_entries"])
     seen = set()
     for (kt, kvh), (off, n) in whole.items():
         seen.add((kt, kvh))
         ents = lay["bwd_list"][off:off + n]
-        tiles = (ents & 0x7FFFFFFF).astype(int)
+        tiles = (ents & 0xFFFFFF).astype(int)
+        heads = ((ents >> 24) & 0x7F).astype(int)
+        if he:
+            assert len(set(zip(tiles.tolist(), heads.tolist()))) == len(ents)
+        else:
+            assert (heads == 0).all()
         c0, c1 = kt * BC, min(S, kt * BC + BC)
         for g in range(G):
             a = dm(kvh * G + g)[:, c0:c1]
             cover = np.zeros(S, dtype=bool)
-            for t, e in zip(tiles, ents):
+            sel = heads == g if he else np.ones(len(ents), dtype=bool)
+            for t, e in zip(tiles[sel], ents[sel]):
                 r0, r1 = t * BR, min(S, t * BR + BR)
-                assert a[r0:r1].any() or G > 1
+                assert a[r0:r1].any() or (G > 1 and not he)
                 if not (e >> 31):
                     assert a[r0:r1].all() and r1 - r0 == BR
                 cover[r0:r1] = True
@@ -520,6 +529,8 @@ def test_dynamic_plan_lists_equal_static(label, spec, Hq, Hkv):
     ls, ld = static.layout(), dyn.layout()
     fs, bs = lists_by_item(ls)
     fd, bd = lists_by_item(ld)
+    if static.stats["bwd_head_entries"]:  # dynamic plans share lists across the group
+        bs = bwd_as_shared(bs, Hq // Hkv)
     assert fs == fd and bs == bd
     nM = (S + 63) // 64
     assert (ld["fwd_items"][:, 2] % nM == 0).all() and (ld["bwd_items"][:, 2] % nM == 0).all()
