@@ -15,6 +15,9 @@
 //
 // One wave builds one list.  Lane l classifies tile c + l of a run of 64; a
 // ballot compacts the listed tiles in order; the wave moves to the next 64.
+// Where the plan lists dK/dV (Q-tile, head) stages (one bitmap per query
+// head), each lane classifies its tile for every head of the group and a
+// scan over the lanes places the lane's stages.
 // Forward / dQ lists run over key tiles J ascending, dK/dV lists over
 // Q-tiles I descending (the order the host gives them).
 //
@@ -122,10 +125,46 @@ __global__ __launch_bounds__(256) void attn_dyn_lists_kernel(DynArgs a) {
     const int wb = w - a.n_fslots;
     const int g = wb / a.nBK, kt = wb - g * a.nBK;
     const int J0 = kt * a.MC, J1 = min(nM, J0 + a.MC);
-    uint32_t *out = a.bwd_list + (int64_t)wb * nM;
+    uint32_t *out = a.bwd_list + (int64_t)wb * a.bcap;
     int cnt = 0, npart = 0;
     for (int c = 0; c < nM; c += 64) {
       const int I = nM - 1 - (c + lane);
+      if (a.bhe) {
+        // one entry per (Q-tile, head) with an allowed pair, heads ascending
+        // within a Q-tile: bits of the lane's non-empty and full heads, an
+        // exclusive scan of their counts over the lanes, then the writes
+        uint64_t hany = 0, hfull = 0;
+        if (I >= 0) {
+          for (int hh = 0; hh < a.bheads; ++hh) {
+            bool any = false, all = true;
+            for (int J = J0; J < J1; ++J) {
+              const int x = micro_class(a, g * a.bheads + hh, I, J, key_block_lo(a, J),
+                                        key_block_hi(a, J));
+              any |= x != kEmpty;
+              all &= x == kFull;
+            }
+            hany |= (uint64_t)any << hh;
+            hfull |= (uint64_t)(any && all) << hh;
+          }
+        }
+        const bool ragged = (I + 1) * kBwdRowTile > a.S || (J1 - J0) < a.MC;
+        if (ragged) hfull = 0;
+        const int n = __popcll(hany), np = n - __popcll(hfull);
+        int incl = n, pincl = np;
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(incl, d), py = __shfl_up(pincl, d);
+          if (lane >= d) { incl += y; pincl += py; }
+        }
+        int k = cnt + incl - n;
+        for (uint64_t m = hany; m; m &= m - 1) {
+          const int hh = __builtin_ctzll(m);
+          const bool part = ((hfull >> hh) & 1ull) == 0ull;
+          out[k++] = (uint32_t)I | ((uint32_t)hh << kHeadShift) | (part ? kPartialBit : 0u);
+        }
+        cnt += __shfl(incl, 63);
+        npart += __shfl(pincl, 63);
+        continue;
+      }
       bool any = false, all = true;
       if (I >= 0) {
         for (int hh = 0; hh < a.bheads; ++hh)
@@ -162,10 +201,11 @@ __global__ __launch_bounds__(kSortThreads) void attn_dyn_sort_kernel(DynArgs a) 
   const int4 *nat = (fwd ? a.fnat : a.bnat) + m0;
   int4 *items = fwd ? a.fitems : a.bitems;
   const int2 *len = a.slot_len + (fwd ? 0 : a.n_fslots);
+  const int64_t cap = fwd ? a.nM : a.bcap;  // list capacity per slot
   if (m > kSortCap) {
     for (int i = tid; i < m; i += kSortThreads) {
       int4 it = nat[i];
-      it.w = len[it.z / a.nM].x;
+      it.w = len[it.z / cap].x;
       items[pos[i]] = it;
     }
     return;
@@ -176,7 +216,7 @@ __global__ __launch_bounds__(kSortThreads) void attn_dyn_sort_kernel(DynArgs a) 
   for (int i = tid; i < n; i += kSortThreads) {
     uint64_t k = ~0ull;
     if (i < m) {
-      const int2 ln = len[nat[i].z / a.nM];
+      const int2 ln = len[nat[i].z / cap];
       const uint32_t cost = 4u * (uint32_t)ln.x + (uint32_t)ln.y;
       k = ((uint64_t)(0xffffffffu - cost) << 32) | (uint32_t)i;
     }
@@ -199,7 +239,7 @@ __global__ __launch_bounds__(kSortThreads) void attn_dyn_sort_kernel(DynArgs a) 
     }
   for (int i = tid; i < m; i += kSortThreads) {
     int4 it = nat[(uint32_t)key[i]];
-    it.w = len[it.z / a.nM].x;
+    it.w = len[it.z / cap].x;
     items[pos[i]] = it;
   }
 }

@@ -383,6 +383,8 @@ struct DynArgs {
   int S, nM, MR, MC, nqb, nkb, nFQ, nBK;
   int n_fslots, n_bslots, fheads, bheads;
   int copy_blocks;
+  int bhe;                 // 1: dK/dV entries are (Q-tile, head) stages
+  int64_t bcap;            // dK/dV list capacity per slot (nM, or nM * bheads)
 };
 
 // Zeros over half hh of a D-wide row (the two lane halves split it).

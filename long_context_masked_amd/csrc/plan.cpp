@@ -476,10 +476,9 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     if (4 * half > listed) p->bwd_keys = 64;
   }
   // With one bitmap per query head, a dK/dV list of Q-tiles shared by the
-  // group would run every head of a tile that any head sees; static plans
-  // list (Q-tile, head) stages instead.  (The device list compiler of dynamic
-  // plans builds shared lists.)
-  p->bwd_head_entries = per_qhead && !dynamic && G <= kMaxEntryHeads;
+  // group would run every head of a tile that any head sees; such plans list
+  // (Q-tile, head) stages instead.
+  p->bwd_head_entries = per_qhead && G <= (dynamic ? kMaxDynEntryHeads : kMaxEntryHeads);
   const int GE = p->bwd_head_entries ? 1 : G;                // stages per list entry
   const int MC = p->bwd_keys / kMicro;                       // micro cols per bwd tile
   const int64_t nBK = (S + p->bwd_keys - 1) / p->bwd_keys;  // bwd K tiles
@@ -602,25 +601,27 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     }
   }
   if (dynamic) {
-    // Every list gets room for all nM tiles of its row or column, at
-    // slot * nM, so that the device can rebuild any list in place.
+    // Every list gets room for all tiles of its row or column (dK/dV
+    // (Q-tile, head) lists: for every stage), at slot * capacity, so that the
+    // device can rebuild any list in place.
     const int64_t nfs = (int64_t)n_fgroups * nFQ, nbs = (int64_t)n_bgroups * nBK;
-    if (nfs * nM > 0x7fffffff || nbs * nM > 0x7fffffff) {
+    const int64_t bcap = p->bwd_head_entries ? nM * G : nM;
+    if (nfs * nM > 0x7fffffff || nbs * bcap > 0x7fffffff) {
       delete p;
       return fail(ATTN_ERR_UNSUPPORTED, "dynamic work lists would exceed 2^31 entries");
     }
     auto widen = [&](std::vector<uint32_t> &list, std::vector<int64_t> &offs,
-                     const std::vector<int32_t> &lens) {
-      std::vector<uint32_t> w((size_t)(offs.size() * nM), 0u);
+                     const std::vector<int32_t> &lens, int64_t cap) {
+      std::vector<uint32_t> w((size_t)(offs.size() * cap), 0u);
       for (size_t sl = 0; sl < offs.size(); ++sl) {
         std::copy(list.begin() + offs[sl], list.begin() + offs[sl] + lens[sl],
-                  w.begin() + (int64_t)sl * nM);
-        offs[sl] = (int64_t)sl * nM;
+                  w.begin() + (int64_t)sl * cap);
+        offs[sl] = (int64_t)sl * cap;
       }
       list.swap(w);
     };
-    widen(fwd_list, fwd_off, fwd_len);
-    widen(bwd_list, bwd_off, bwd_len);
+    widen(fwd_list, fwd_off, fwd_len, nM);
+    widen(bwd_list, bwd_off, bwd_len, bcap);
     DynInfo &D = p->dyn;
     D.on = true;
     D.nM = nM; D.nFQ = nFQ; D.nBK = nBK;
@@ -628,6 +629,8 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     D.MR = MR; D.MC = MC;
     D.fheads = per_qhead ? p->HG : 1;
     D.bheads = per_qhead ? G : 1;
+    D.bhe = p->bwd_head_entries;
+    D.bcap = bcap;
   }
   if (fwd_list.size() > 0x7fffffffu || bwd_list.size() > 0x7fffffffu) {
     delete p;

@@ -21,6 +21,7 @@ constexpr int kWgRowsHeads = 128; // forward / dQ: (rows x heads) per workgroup
 constexpr uint32_t kPartialBit = 0x80000000u;
 constexpr int kHeadShift = 24;   // dK/dV (Q-tile, head) entries: head in bits 24-30
 constexpr int kMaxEntryHeads = 128;
+constexpr int kMaxDynEntryHeads = 64;  // the device list compiler keeps a 64-bit head mask
 // Class of a 64x64 micro tile (stored as uint8 in a dynamic plan's blob).
 enum : uint8_t { kEmpty = 0, kPartial = 1, kFull = 2 };
 
@@ -43,8 +44,10 @@ struct Layout {
 // What the device list builder of a dynamic plan needs.  List group g of
 // the forward covers mask heads [g * fheads, (g + 1) * fheads) and owns the
 // forward lists of slots [g * nFQ, (g + 1) * nFQ), one per Q-tile; likewise
-// the dK/dV groups with bheads and nBK.  Every list has room for nM entries
-// at list + slot * nM.  The items of each pass are dealt to XCD shares
+// the dK/dV groups with bheads and nBK.  Every forward list has room for nM
+// entries at list + slot * nM, every dK/dV list for bcap entries at
+// list + slot * bcap: nM, or nM * bheads when its entries are (Q-tile, head)
+// stages (bhe).  The items of each pass are dealt to XCD shares
 // (fixed at creation); a share's items are re-sorted, longest first, within
 // the share's positions of the item array.
 struct DynInfo {
@@ -53,6 +56,8 @@ struct DynInfo {
   int64_t n_fslots = 0, n_bslots = 0;
   int MR = 1, MC = 2, fheads = 1, bheads = 1;
   int n_fshares = 1, n_bshares = 1;
+  bool bhe = false;
+  int64_t bcap = 0;
 };
 
 // dK/dV items whose work exceeds the share of one workgroup are split into

@@ -15,25 +15,6 @@ def lists_by_item(lay):
 
 
 
-def bwd_as_shared(b, G):
-    """dK/dV lists of (Q-tile, query head) stages (plans with
-    stats["bwd_head_entries"]) in the form of lists shared by the G heads of
-    a group, as dynamic plans build them: one entry per Q-tile that has a
-    stage, partial unless all G heads have a full stage of it."""
-    out = {}
-    for key, ents in b.items():
-        tiles, full = [], {}
-        for e in ents:
-            t = e & 0xFFFFFF
-            if t not in full:
-                tiles.append(t)
-                full[t] = 0
-            if not e >> 31:
-                full[t] += 1
-        out[key] = [t | (0 if full[t] == G else 0x80000000) for t in tiles]
-    return out
-
-
 def concat_lists(lay):
     """Numpy form of lists_by_item for large plans: per pass, the (tile, head)
     keys in sorted order, their list lengths, and all their entries joined in

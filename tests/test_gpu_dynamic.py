@@ -20,7 +20,7 @@ import synthetic as syn
 from oracle import attention as ora
 
 from gpu_util import gate, to_dev, to_f64, f64
-from plan_util import bwd_as_shared, lists_by_item
+from plan_util import lists_by_item
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -92,8 +92,6 @@ def _check_lists_equal(dyn, spec_new, B, Hq, Hkv, d, bits_new):
     # width (chosen from its creation bitmap)
     ref = lcm.Plan(B, spec_new["S"], Hq, Hkv, d, dict(spec_new, bwd_key_tile=dyn.stats["bwd_tile_cols"]))
     fs, bs = lists_by_item(ref.layout())
-    if ref.stats["bwd_head_entries"]:  # dynamic plans share lists across the group
-        bs = bwd_as_shared(bs, Hq // Hkv)
     dl = dyn.device_layout()
     fd, bd = lists_by_item(dl)
     assert fd == fs, "forward / dQ lists differ from the host compiler's"
@@ -262,12 +260,7 @@ def test_fullsize_sparse_32k_gqa(blk, heads):
     (fk, fl, fe), (bk, bl, be) = concat_lists(dl)
     (gk, gl, ge), (ck, cl, ce) = concat_lists(static.layout())
     assert np.array_equal(fk, gk) and np.array_equal(fl, gl) and np.array_equal(fe, ge)
-    if static.stats["bwd_head_entries"]:
-        # the ordinary plan lists (Q-tile, head) stages; the dynamic plan
-        # shares its lists across the group
-        assert bwd_as_shared(lists_by_item(static.layout())[1], Hq // Hkv) == lists_by_item(dl)[1]
-    else:
-        assert np.array_equal(bk, ck) and np.array_equal(bl, cl) and np.array_equal(be, ce)
+    assert np.array_equal(bk, ck) and np.array_equal(bl, cl) and np.array_equal(be, ce)
     fresh = lcm.Plan(1, S, Hq, Hkv, d, dict(syn.with_bitmap(base, offs, offs, b2), dynamic=True,
                                             bwd_key_tile=dyn.stats["bwd_tile_cols"]))
     _check_items(dl, fresh.layout(), Hkv)   # longest first, as a fresh plan

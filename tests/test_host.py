@@ -9,7 +9,7 @@ import pytest
 
 import synthetic as syn
 from oracle import masks as om
-from plan_util import bwd_as_shared, lists_by_item
+from plan_util import lists_by_item
 
 lcm = pytest.importorskip("long_context_masked_amd")
 from long_context_masked_amd import _lib as L  # noqa: E402
@@ -529,8 +529,7 @@ def test_dynamic_plan_lists_equal_static(label, spec, Hq, Hkv):
     ls, ld = static.layout(), dyn.layout()
     fs, bs = lists_by_item(ls)
     fd, bd = lists_by_item(ld)
-    if static.stats["bwd_head_entries"]:  # dynamic plans share lists across the group
-        bs = bwd_as_shared(bs, Hq // Hkv)
+    assert dyn.stats["bwd_head_entries"] == static.stats["bwd_head_entries"]
     assert fs == fd and bs == bd
     nM = (S + 63) // 64
     assert (ld["fwd_items"][:, 2] % nM == 0).all() and (ld["bwd_items"][:, 2] % nM == 0).all()
