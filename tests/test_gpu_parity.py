@@ -204,9 +204,13 @@ def test_backward_is_deterministic_with_split_items():
 def test_atomic_and_separate_dq_paths_both_match_the_oracle():
     """attn_bwd (separate dQ pass) and attn_bwd_atomic_dq (dQ accumulated in
     the dK/dV pass) against the oracle on masks with partial tiles, GQA and
-    MHA, both head dims, ragged S and rows without keys."""
+    MHA, both head dims, ragged S, rows without keys and one bitmap per query
+    head."""
+    po, pb = syn.uniform_block_bitmap(333, 64, 6, 0.5, seed=14)
     cases = [(syn.spec_causal(333), 1, 6, 2, 128), (RAGGED_GQA[12][1], 1, 8, 1, 128),
-             (dict(TINY)["varblock_50"], 2, 4, 2, 64)]
+             (dict(TINY)["varblock_50"], 2, 4, 2, 64),
+             # one bitmap per query head: (Q-tile, head) dK/dV stages
+             (syn.with_bitmap(syn.spec_causal(333), po, po, pb), 1, 6, 2, 128)]
     for spec, B, Hq, Hkv, d in cases:
         spec = dict(spec, bwd_key_tile=128)  # the fused dQ pass runs on 128-key items
         S = spec["S"]
