@@ -145,6 +145,8 @@ extern "C" attn_status attn_plan_set_bitmap(attn_plan *plan, const uint8_t *bits
   a.bheads = D.bheads;
   a.bhe = D.bhe ? 1 : 0;
   a.bcap = D.bcap;
+  a.head_major = D.head_major ? 1 : 0;
+  a.fkv = D.fkv;
   (void)hipGetLastError();
   const hipError_t e = launch_dyn(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "list rebuild launch failed: %s", hipGetErrorString(e));

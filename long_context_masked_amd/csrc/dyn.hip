@@ -26,7 +26,8 @@
 // XCD shares at creation (each XCD's workgroups serve a fixed set of heads,
 // so that its L2 holds their tiles); one workgroup re-sorts the items of one
 // share by their new cost, 4 x tiles + partial tiles (a partial tile costs
-// 1.25 full ones), ties in natural order, with a bitonic sort in LDS, and
+// 1.25 full ones), ties in natural order (shares of several KV heads: by
+// head first), with a bitonic sort in LDS, and
 // writes them, with their new lengths, into the share's positions.  That is
 // the host compiler's order whenever its deal does not depend on the costs
 // (Hkv a multiple of 8, or no deal at all).
@@ -188,6 +189,7 @@ __global__ __launch_bounds__(256) void attn_dyn_lists_kernel(DynArgs a) {
 // One workgroup per XCD share of either pass.  A share larger than
 // kSortCap items keeps its items in natural order (lengths updated).
 constexpr int kSortCap = 8192;
+static_assert(kSortCap <= 0x10000, "share_sort_key keeps 16 bits of the natural index");
 constexpr int kSortThreads = 1024;
 
 __global__ __launch_bounds__(kSortThreads) void attn_dyn_sort_kernel(DynArgs a) {
@@ -212,13 +214,17 @@ __global__ __launch_bounds__(kSortThreads) void attn_dyn_sort_kernel(DynArgs a) 
   }
   int n = 1;
   while (n < m) n <<= 1;
-  // ascending order of (0xffffffff - cost) << 32 | natural index
+  // ascending order of share_sort_key: cost descending, ties in natural
+  // order, or, where the share holds several KV heads, the head first (one
+  // head's items together, each head's longest first: the host's order, as
+  // its interleave leaves it)
   for (int i = tid; i < n; i += kSortThreads) {
     uint64_t k = ~0ull;
     if (i < m) {
       const int2 ln = len[nat[i].z / cap];
       const uint32_t cost = 4u * (uint32_t)ln.x + (uint32_t)ln.y;
-      k = ((uint64_t)(0xffffffffu - cost) << 32) | (uint32_t)i;
+      const uint32_t kvh = (uint32_t)(fwd ? nat[i].y / a.fkv : nat[i].y);
+      k = share_sort_key(a.head_major != 0, kvh, cost, (uint32_t)i);
     }
     key[i] = k;
   }
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(kSortThreads) void attn_dyn_sort_kernel(DynArgs a) 
       __syncthreads();
     }
   for (int i = tid; i < m; i += kSortThreads) {
-    int4 it = nat[(uint32_t)key[i]];
+    int4 it = nat[share_sort_index(key[i])];
     it.w = len[it.z / cap].x;
     items[pos[i]] = it;
   }

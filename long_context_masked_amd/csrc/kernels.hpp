@@ -385,6 +385,8 @@ struct DynArgs {
   int copy_blocks;
   int bhe;                 // 1: dK/dV entries are (Q-tile, head) stages
   int64_t bcap;            // dK/dV list capacity per slot (nM, or nM * bheads)
+  int head_major;          // 1: XCD shares hold several KV heads, sorted by head first
+  int fkv;                 // query heads per KV head (forward items carry a query head)
 };
 
 // Zeros over half hh of a D-wide row (the two lane halves split it).

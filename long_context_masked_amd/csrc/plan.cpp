@@ -296,10 +296,24 @@ struct Item { int32_t tile, head, off, len; double cost; };
 // XCD x takes the heads h with h % 8 == x; when Hkv divides 8, each head's
 // items go to the least-loaded of the XCDs congruent to it modulo Hkv (the
 // longest-processing-time rule within that set).  Otherwise the order is
-// left as it is.  Each XCD's share stays in longest-first order.  If `cls`
+// left as it is.  Each XCD's share stays in longest-first order, except that
+// a share of several KV heads (Hkv > 8) runs one head's items after another,
+// each head's longest first: the workgroups then in flight on the XCD walk
+// the tiles of one head together.  With the share's heads mixed (MHA, a
+// random bitmap per head) L2 served a third of the forward's K/V tiles and
+// the rest came from HBM at two thirds of its bandwidth.  If `cls`
 // is given it receives the XCD share (0 when the order is left) of every
 // position of the result.
 constexpr int kXcds = 8;
+// The share sort's key layouts give back the natural index, and order as
+// the host does: by KV head first where asked, then cost descending, then
+// natural index.
+static_assert(share_sort_index(share_sort_key(true, 13, 0xfffffffeu, 8191)) == 8191, "index, head-major");
+static_assert(share_sort_index(share_sort_key(false, 13, 0xfffffffeu, 8191)) == 8191, "index");
+static_assert(share_sort_key(true, 1, 9, 0) < share_sort_key(true, 2, 99, 0), "head first");
+static_assert(share_sort_key(true, 1, 99, 5) < share_sort_key(true, 1, 9, 0), "cost descending");
+static_assert(share_sort_key(false, 7, 99, 5) < share_sort_key(false, 1, 9, 0), "cost descending");
+static_assert(share_sort_key(true, 1, 9, 3) < share_sort_key(true, 1, 9, 4), "natural order on ties");
 void xcd_interleave(std::vector<Item> &v, int64_t Hkv, int64_t heads_per_kv,
                     std::vector<int32_t> *cls = nullptr) {
   const bool by_mod = Hkv % kXcds == 0;
@@ -320,6 +334,11 @@ void xcd_interleave(std::vector<Item> &v, int64_t Hkv, int64_t heads_per_kv,
     q[(size_t)slot].push_back(x);
     load[(size_t)slot] += x.cost;
   }
+  if (by_mod && Hkv > kXcds)
+    for (auto &share : q)
+      std::stable_sort(share.begin(), share.end(), [&](const Item &a, const Item &b) {
+        return a.head / heads_per_kv < b.head / heads_per_kv;
+      });
   v.clear();
   if (cls) cls->clear();
   for (size_t i = 0;; ++i) {
@@ -631,6 +650,8 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     D.bheads = per_qhead ? G : 1;
     D.bhe = p->bwd_head_entries;
     D.bcap = bcap;
+    D.head_major = sh.Hkv % kXcds == 0 && sh.Hkv > kXcds;
+    D.fkv = G;
   }
   if (fwd_list.size() > 0x7fffffffu || bwd_list.size() > 0x7fffffffu) {
     delete p;

@@ -50,6 +50,16 @@ struct Layout {
 // stages (bhe).  The items of each pass are dealt to XCD shares
 // (fixed at creation); a share's items are re-sorted, longest first, within
 // the share's positions of the item array.
+// Sort key of the device's re-sort of an XCD share (ascending order): the
+// item's cost descending, ties by its natural index i < 2^16; or, when the
+// share holds several KV heads, the KV head first.  share_sort_index
+// recovers i from either layout.
+constexpr uint64_t share_sort_key(bool head_major, uint32_t kvh, uint32_t cost, uint32_t i) {
+  return head_major ? ((uint64_t)(kvh & 0xffffu) << 48) | ((uint64_t)(0xffffffffu - cost) << 16) | (i & 0xffffu)
+                    : ((uint64_t)(0xffffffffu - cost) << 32) | (i & 0xffffu);
+}
+constexpr uint32_t share_sort_index(uint64_t key) { return (uint32_t)(key & 0xffffu); }
+
 struct DynInfo {
   bool on = false;
   int64_t nM = 0, nFQ = 0, nBK = 0;
@@ -58,6 +68,8 @@ struct DynInfo {
   int n_fshares = 1, n_bshares = 1;
   bool bhe = false;
   int64_t bcap = 0;
+  bool head_major = false;  // shares sorted by KV head, then cost (several heads per XCD)
+  int fkv = 1;              // query heads per KV head
 };
 
 // dK/dV items whose work exceeds the share of one workgroup are split into

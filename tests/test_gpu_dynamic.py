@@ -55,6 +55,8 @@ def _cases():
     o = syn.uniform_block_bitmap(S, 64, 1, seed=0)[0]
     out.append(("mha8_by_head_deal", syn.spec_causal(S), o, o, 8, 8, 64, 8))
     out.append(("gqa6_3_no_deal", syn.spec_full(S), o, o, 6, 3, 128, 3))
+    # two KV heads per XCD share: the share runs one head's items after the other
+    out.append(("mha16_head_major_shares", syn.spec_causal(S), o, o, 16, 16, 64, 16))
     return out
 
 

@@ -334,6 +334,37 @@ def test_schedule_is_longest_first(family):
                 assert _lpt_makespan(share, m) <= (4.0 / 3.0 - 1.0 / (3.0 * m)) * lower + 1e-9
 
 
+@pytest.mark.parametrize("Hkv,dynamic", [(16, False), (64, False), (16, True)])
+def test_xcd_shares_of_several_heads_run_head_by_head(Hkv, dynamic):
+    """With more than 8 KV heads each XCD share (items b with b % 8 == x)
+    holds the heads h % 8 == x; it runs one head's items after another, in
+    ascending head order, each head's in non-increasing cost order."""
+    S, G = 8192, 2  # items of about equal cost: none split, shares of equal length
+    offs, bits = syn.uniform_block_bitmap(S, 128, Hkv, 0.5, 7)
+    spec = syn.with_bitmap(syn.spec_full(S), offs, offs, bits)
+    if dynamic:
+        spec = dict(spec, dynamic=True)
+    p = lcm.Plan(1, S, Hkv * G, Hkv, 128, spec)
+    lay = p.layout()
+    HG = p.stats["heads_per_item"]
+    for kind, items, lst, per_kv in (("fwd", lay["fwd_items"], lay["fwd_list"], G),
+                                      ("bwd", lay["bwd_items"], lay["bwd_list"], 1)):
+        for x in range(8):
+            share = items[x::8]
+            kvh = share[:, 1] // per_kv
+            assert (kvh % 8 == x).all(), kind
+            assert (np.diff(kvh) >= 0).all(), f"{kind}: share {x} not head by head"
+            for h in np.unique(kvh):
+                run = share[kvh == h]
+                cost = []
+                for _, _, off, n in run:
+                    e = lst[off:off + n]
+                    npart = int((e >> 31).sum())
+                    stages = G if kind == "bwd" else 1
+                    cost.append(stages * ((n - npart) + 1.25 * npart))
+                assert (np.diff(cost) <= 1e-9).all(), f"{kind}: head {h} not longest first"
+
+
 @pytest.mark.parametrize("label,spec,S,splits", [
     ("full1K", syn.spec_full(1024), 1024, True),
     ("causal1K", syn.spec_causal(1024), 1024, True),
