@@ -304,3 +304,62 @@ def test_smoke_entry_point():
     oracle, with the gate above) passes."""
     import __graft_entry__
     __graft_entry__.smoke()
+
+
+def _random_configs(n=14, seed=2026):
+    """Seeded random shapes, masks and plan options: S in [65, 900], KV heads
+    1-16 with groups of 1-4 (16 KV heads put two heads in each XCD share),
+    both head dims, batches of 1-2, every base family, bitmaps per KV head
+    and per query head (uniform 32/64/128 or variable blocks, distinct row
+    and column partitions), and 64-key, 128-key or chosen dK/dV items."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        S = int(rng.integers(65, 901))
+        Hkv = int(rng.choice([1, 2, 4, 16]))
+        G = int(rng.choice([1, 2, 3, 4])) if Hkv < 16 else int(rng.choice([1, 2]))
+        Hq, d, B = Hkv * G, int(rng.choice([64, 128])), int(rng.choice([1, 1, 2]))
+        fam = int(rng.integers(0, 6))
+        s = int(rng.integers(0, 1 << 30))
+        if fam == 0:
+            base = syn.spec_full(S)
+        elif fam == 1:
+            base = syn.spec_causal(S)
+        elif fam == 2:
+            base = syn.spec_sliding(S, int(rng.integers(1, S + 1)), bool(rng.integers(0, 2)))
+        elif fam == 3:
+            base = syn.spec_document(syn.sample_doc_lens(S, 16, max(17, S // 2), s), bool(rng.integers(0, 2)))
+        elif fam == 4:
+            base = syn.spec_global_sliding(S, int(rng.integers(1, 40)), int(rng.integers(8, 200)),
+                                           bool(rng.integers(0, 2)))
+        else:
+            base = syn.spec_causal_blockwise(S, int(rng.integers(16, 300)))
+        spec = base
+        bm = int(rng.integers(0, 4))  # 0: none, 1: per KV head, 2: per query head, 3: distinct partitions
+        heads = {1: Hkv, 2: Hq, 3: 1}.get(bm)
+        if bm in (1, 2):
+            if rng.integers(0, 2):
+                offs, bits = syn.uniform_block_bitmap(S, int(rng.choice([32, 64, 128])), heads, 0.5, s)
+            else:
+                offs, bits = syn.variable_block_bitmap(S, 16, 200, heads, 0.5, s)
+            spec = syn.with_bitmap(base, offs, offs, bits)
+        elif bm == 3:
+            qo = syn.variable_partition(S, 20, 150, s)
+            ko = syn.variable_partition(S, 30, 200, s + 1)
+            spec = syn.with_bitmap(base, qo, ko, syn.partition_bitmap(qo, ko, 1, 0.5, s + 2))
+        tile = int(rng.choice([0, 0, 64, 128]))
+        if tile:
+            spec = dict(spec, bwd_key_tile=tile)
+        out.append((f"r{i}_S{S}_B{B}_{Hq}x{Hkv}_d{d}_{base['family']}_bm{bm}_k{tile}", spec, B, Hq, Hkv, d))
+    return out
+
+
+RANDOM = _random_configs()
+
+
+@pytest.mark.parametrize("label,spec,B,Hq,Hkv,d", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_configurations(label, spec, B, Hq, Hkv, d):
+    """Forward and chained backward against the oracle on seeded random
+    configurations (shape, mask family, bitmap layout, dK/dV item width)."""
+    print(f"random configuration {label}", flush=True)
+    run_case(spec, B, Hq, Hkv, d, seed=int(label[1:label.index("_")]) + 40)
