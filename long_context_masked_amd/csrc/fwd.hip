@@ -111,14 +111,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     dma.load(smem + VOFF + slot * T::BYTES, vbase, ldk, (int)(list[e] & 0x7fffffffu) * 64, S);
   };
   // Allowed-key words of the lane's row for the two key blocks of tile e
-  // (all ones unless the tile is partial); returns whether it is partial.
-  auto tile_mask = [&](int e, uint32_t (&mw)[2]) -> bool {
+  // (all ones unless the tile is partial); returns whether the tile needs the
+  // per-entry bias.  A partial tile in which every row of the wave sees all
+  // 64 keys or none (a bitmap or document edge between rows, not inside the
+  // tile's keys) needs none: `dead` marks the rows that see no key, whose
+  // exponentials then take a -inf offset and whose maxima are left out.
+  auto tile_mask = [&](int e, uint32_t (&mw)[2], bool &dead) -> bool {
     const uint32_t ent = list[e];
     mw[0] = 0xffffffffu;
     mw[1] = 0xffffffffu;
-    const bool part = MASKED && (ent >> 31) != 0;
+    dead = false;
+    bool part = MASKED && (ent >> 31) != 0;
     if (part) {
       const uint64_t mk = row_ok ? row_mask(a.m, rb, qb, hm, (int)(ent & 0x7fffffffu) * 64, S) : 0ull;
+      dead = mk == 0ull;
+      part = __ballot(mk != 0ull && mk != ~0ull) != 0ull;
       const uint64_t sh = mk >> (4 * hh);
       mw[0] = (uint32_t)sh;
       mw[1] = (uint32_t)(sh >> 32);
@@ -141,8 +148,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   // P of accumulator register r of key block kb, pinned where it is
   // computed (the compiler would otherwise sink it next to its use and undo
   // the interleave).
+  float mneg = -m_run;  // -m_run, or -inf on a row that sees no key of the tile
   auto p_exp = [&](f32x16 &s, int r) {
-    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -m_run));
+    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, mneg));
     in_vgpr(p);
     s[r] = p;
   };
@@ -167,12 +175,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 
   // Prologue: K(0), V(0), K(1) in; S^T(0) and its max; then K(2), V(1) out.
   f32x16 sc[2];  // S^T of the current tile, then its P (exponentiated in place)
+  bool dc = false;  // this row sees no key of the current tile (row-uniform tile)
   if (n > 0) {
     load_k(0, 0);
     load_v(0, 0);
     if (n > 1) load_k(1, 1);
     uint32_t mw[2];
-    const bool part = tile_mask(0, mw);
+    const bool part = tile_mask(0, mw, dc);
     dma_wait();
     __syncthreads();
     bf16x8 ak[2][KS];
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     float mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[0][r]), sc[1][r]);
-    m_update(mx);
+    m_update(dc ? kNegInf : mx);
     __syncthreads();  // every wave is done with K slot 0
     if (n > 2) load_k(2, 0);
     if (n > 1) load_v(1, 1);
@@ -204,8 +213,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     constexpr bool NEXT = decltype(nc)::value;  // tile t + 1 exists
     const char *kslot = smem + (1 - P) * T::BYTES;
     uint32_t mw[2] = {0xffffffffu, 0xffffffffu};
-    bool pn = false;
-    if constexpr (NEXT) pn = tile_mask(t + 1, mw);
+    bool pn = false, dn = false;
+    if constexpr (NEXT) pn = tile_mask(t + 1, mw, dn);
+    mneg = dc ? kNegInf : -m_run;
     bf16x8 ak[2][KS];
     if constexpr (NEXT) {
       ak[0][0] = lds_rows(kslot, koff[0]);
@@ -294,9 +304,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NEXT) {
-      m_update(mx);
+      m_update(dn ? kNegInf : mx);
       sc[0] = sn[0];
       sc[1] = sn[1];
+      dc = dn;
     }
 
     // K(t + 2) and V(t + 1) are in LDS for every wave; K slot 1 - P and V
