@@ -29,11 +29,13 @@ __device__ __forceinline__ int64_t ws_row0(int b, int h, int Hq, int S64) {
 
 // ws <- {lse * log2(e), -D = -sum_d dO * O} per (b, h, row); rows in
 // [S, S64) get zeros.  When dqacc is given, its row (b, s, h) of the fp32 dQ
-// accumulator [B][S64][Hq][D] is zeroed as well.  A row with no allowed key (LSE = -inf) gets a large
-// positive lse2 instead, so that the recomputed P = exp2(S c - lse2) is 0 on
-// every key, masked ones (S = -inf) included, rather than -inf + inf.  D is stored negated so that the dK/dV pass can start
-// the accumulation of dP at -D and get dP - D from the products alone.  One group of D/8 lanes per row; the grid covers B * S64 * Hq
-// rows in [b][s][h] order.
+// accumulator [B][S64][Hq][D] is zeroed as well.  A row with no allowed key
+// (LSE = -inf) gets a large positive lse2 instead, so that the recomputed
+// P = exp2(S c - lse2) is 0 on every key, masked ones (S = -inf) included,
+// rather than -inf + inf.  D is stored negated so that the dK/dV pass can
+// start the accumulation of dP at -D and get dP - D from the products alone.
+// One group of D/8 lanes per row; the grid covers B * S64 * Hq rows in
+// [b][s][h] order.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const bf16 *dout,
                                                            const float *lse, float *ws, float *dqacc,
@@ -117,7 +119,10 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
 // three LDS buffers: the one of stage st is read in stage st + 1 and written
 // again in stage st + 3, after the barrier of stage st + 2 that every wave
 // reaches only once its reads are done.
-// ---------------------------------------------------------------------------
+//
+// A list entry names a Q-tile, run for each of the G query heads of the
+// group (G stages); on plans with one bitmap per query head it names one
+// (Q-tile, head) stage, the head in bits 24-30.
 //
 // NW = 2 (narrow items): 64 keys per work item, two waves, and two LDS stage
 // buffers instead of three, so that two workgroups share a CU (one wave per
@@ -127,6 +132,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const bf16 *o, const 
 // can only be loaded once every wave has finished reading stage st, so its
 // loads are issued after a second barrier at the end of stage st, into
 // stage st's buffer.
+// ---------------------------------------------------------------------------
 template <int D, bool FDQ, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void attn_dkdv_kernel(BwdArgs a) {
   static_assert(NW == 4 || (NW == 2 && !FDQ), "narrow items have no fused dQ variant");
