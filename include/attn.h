@@ -219,6 +219,12 @@ typedef struct {
    * dK/dV item split into chunks whose partial results are summed. */
   int64_t off_bwd_reduce, n_bwd_reduce;
   int64_t n_slots;                      /* partial slots per batch entry    */
+  /* uint64 [bitmap heads][n_qblk][ceil(S/64)]: allowed keys of 64-key tile t
+   * for rows of bitmap row block qb (bit c: key 64 t + c), and uint64
+   * [bitmap heads][n_kblk][ceil(S/64)]: allowed rows of 64-row tile t for
+   * keys of column block kb; the bitmap part of the mask only.  Static plans
+   * whose blocks cut 64-wide tiles, up to 4 GiB for both; else -1. */
+  int64_t off_kwords, off_rwords;
 } attn_plan_layout;
 
 attn_status attn_plan_get_layout(const attn_plan *plan, attn_plan_layout *out);

@@ -136,6 +136,14 @@ class Plan:
             "bwd_reduce": i32(lay.off_bwd_reduce, 4 * lay.n_bwd_reduce).reshape(-1, 4),
             "n_slots": int(lay.n_slots),
         }
+        if lay.off_kwords >= 0:
+            # bitmap words: [heads][n_qblk][nM] allowed keys, [heads][n_kblk][nM] allowed rows
+            c, nM = self.desc.c, (S + 63) // 64
+            nk, nr = c.bitmap_heads * c.n_qblk * nM, c.bitmap_heads * c.n_kblk * nM
+            out["kwords"] = raw[lay.off_kwords:lay.off_kwords + 8 * nk].view(np.uint64).reshape(
+                c.bitmap_heads, c.n_qblk, nM)
+            out["rwords"] = raw[lay.off_rwords:lay.off_rwords + 8 * nr].view(np.uint64).reshape(
+                c.bitmap_heads, c.n_kblk, nM)
         return out
 
     def __del__(self):

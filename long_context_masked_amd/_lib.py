@@ -57,7 +57,8 @@ class Layout(C.Structure):
                 ("off_bits", C.c_int64), ("off_qblk", C.c_int64), ("off_kblk", C.c_int64),
                 ("off_qoffs", C.c_int64), ("off_koffs", C.c_int64),
                 ("off_bwd_slot", C.c_int64), ("off_bwd_reduce", C.c_int64),
-                ("n_bwd_reduce", C.c_int64), ("n_slots", C.c_int64)]
+                ("n_bwd_reduce", C.c_int64), ("n_slots", C.c_int64),
+                ("off_kwords", C.c_int64), ("off_rwords", C.c_int64)]
 
 
 # Every symbol include/attn.h declares, with its ctypes signature.

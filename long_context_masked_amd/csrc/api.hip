@@ -45,6 +45,9 @@ MaskArgs mask_args(const attn_plan *p) {
   m.nqb = p->nqb;
   m.nkb = p->nkb;
   m.bm_heads = p->bitmap_heads;
+  m.kwords = sect<uint64_t>(p, p->lay.kwords);
+  m.rwords = sect<uint64_t>(p, p->lay.rwords);
+  m.nM = (int)((p->shape.S + kMicro - 1) / kMicro);
   return m;
 }
 

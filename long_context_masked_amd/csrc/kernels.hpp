@@ -327,6 +327,10 @@ struct MaskArgs {
   const int *qblk, *kblk;  // block of each position
   const int *qoffs, *koffs;
   int nqb, nkb, bm_heads;  // bm_heads 0 = no bitmap
+  // or null: the bitmap part of the mask precomputed per 64-wide tile,
+  // allowed keys [bm_heads][nqb][nM] and allowed rows [bm_heads][nkb][nM]
+  const uint64_t *kwords, *rwords;
+  int nM;
 };
 
 struct FwdArgs {
@@ -402,7 +406,9 @@ __device__ __forceinline__ void zero_half_row(E *row, int hh) {
 __device__ __forceinline__ uint64_t row_mask(const MaskArgs &m, int4 rb, int qb, int hm,
                                              int t0, int S) {
   uint64_t bits = range64(rb.x - t0, rb.y - t0) | range64(rb.z - t0, rb.w - t0);
-  if (m.bm_heads) {
+  if (m.kwords) {
+    bits &= m.kwords[((int64_t)hm * m.nqb + qb) * m.nM + (t0 >> 6)];
+  } else if (m.bm_heads) {
     const int last = (t0 + 63 < S ? t0 + 63 : S - 1);
     const int kb0 = m.kblk[t0], kb1 = m.kblk[last];
     const uint8_t *brow = m.bits + ((int64_t)hm * m.nqb + qb) * m.nkb;
@@ -423,7 +429,9 @@ __device__ __forceinline__ uint64_t col_mask(const MaskArgs &m, int4 cb, int kb,
                                              int r0, int S) {
   uint64_t bits = ~(range64(cb.x - r0, cb.y - r0) | range64(cb.z - r0, cb.w - r0));
   bits &= range64(0, S - r0);
-  if (m.bm_heads) {
+  if (m.rwords) {
+    bits &= m.rwords[((int64_t)hm * m.nkb + kb) * m.nM + (r0 >> 6)];
+  } else if (m.bm_heads) {
     const int last = (r0 + 63 < S ? r0 + 63 : S - 1);
     const int qb0 = m.qblk[r0], qb1 = m.qblk[last];
     const uint8_t *bcol = m.bits + (int64_t)hm * m.nqb * m.nkb + kb;

@@ -769,6 +769,24 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     L.qoffs = sect((int64_t)(bm.nqb + 1) * 4);
     L.koffs = sect((int64_t)(bm.nkb + 1) * 4);
   }
+  // Bitmap words of static plans whose blocks cut tiles: the mask of a
+  // partial tile then costs the kernels one 8-byte load per lane instead of
+  // a walk over the blocks the tile touches.  Dynamic plans walk the blocks
+  // (their bitmap changes on the device).
+  bool words = false;
+  if (has_bm && !dynamic) {
+    bool cut = false;
+    for (int64_t t = 0; t < nM && !cut; ++t) {
+      const int64_t a = t * kMicro, e = std::min<int64_t>(S, a + kMicro) - 1;
+      cut = bm.kblk[(size_t)a] != bm.kblk[(size_t)e] || bm.qblk[(size_t)a] != bm.qblk[(size_t)e];
+    }
+    const int64_t bytes = (int64_t)bm.heads * (bm.nqb + bm.nkb) * nM * 8;
+    words = cut && bytes <= kMaxMaskWordBytes;
+    if (words) {
+      L.kwords = sect((int64_t)bm.heads * bm.nqb * nM * 8);
+      L.rwords = sect((int64_t)bm.heads * bm.nkb * nM * 8);
+    }
+  }
   std::vector<int32_t> fsh_off, fsh_pos, bsh_off, bsh_pos;
   std::vector<std::array<int32_t, 4>> fsh_nat, bsh_nat;
   if (dynamic) {
@@ -834,6 +852,45 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     std::memcpy(blob + L.kblk, bm.kblk.data(), (size_t)S * 4);
     std::memcpy(blob + L.qoffs, bm.qoffs.data(), bm.qoffs.size() * 4);
     std::memcpy(blob + L.koffs, bm.koffs.data(), bm.koffs.size() * 4);
+  }
+  if (words) {
+    // The blocks a 64-wide tile touches, each with the bits of the tile it
+    // covers: word(tile, block line) = OR of the segments whose bitmap bit
+    // is on.
+    struct Seg { int32_t blk; uint64_t mask; };
+    auto segments = [&](const std::vector<int32_t> &blk_of, const std::vector<int32_t> &offs) {
+      std::vector<std::vector<Seg>> out((size_t)nM);
+      for (int64_t t = 0; t < nM; ++t) {
+        const int64_t a = t * kMicro, e = std::min<int64_t>(S, a + kMicro);
+        for (int32_t b = blk_of[(size_t)a]; b <= blk_of[(size_t)(e - 1)]; ++b) {
+          const int64_t lo = std::max<int64_t>(offs[(size_t)b], a) - a;
+          const int64_t hi = std::min<int64_t>(offs[(size_t)b + 1], e) - a;
+          const uint64_t top = hi == 64 ? ~0ull : ((1ull << hi) - 1ull);
+          out[(size_t)t].push_back({b, top & ~((1ull << lo) - 1ull)});
+        }
+      }
+      return out;
+    };
+    const auto kseg = segments(bm.kblk, bm.koffs), qseg = segments(bm.qblk, bm.qoffs);
+    uint64_t *kw = reinterpret_cast<uint64_t *>(blob + L.kwords);
+    uint64_t *rw = reinterpret_cast<uint64_t *>(blob + L.rwords);
+    for (int h = 0; h < bm.heads; ++h) {
+      const uint8_t *bh = bm.bits.data() + (size_t)h * bm.nqb * bm.nkb;
+      for (int32_t qb = 0; qb < bm.nqb; ++qb)
+        for (int64_t t = 0; t < nM; ++t) {
+          uint64_t w = 0;
+          for (const Seg &g : kseg[(size_t)t])
+            if (bh[(size_t)qb * bm.nkb + g.blk]) w |= g.mask;
+          kw[((int64_t)h * bm.nqb + qb) * nM + t] = w;
+        }
+      for (int32_t kb = 0; kb < bm.nkb; ++kb)
+        for (int64_t t = 0; t < nM; ++t) {
+          uint64_t w = 0;
+          for (const Seg &g : qseg[(size_t)t])
+            if (bh[(size_t)g.blk * bm.nkb + kb]) w |= g.mask;
+          rw[((int64_t)h * bm.nkb + kb) * nM + t] = w;
+        }
+    }
   }
   if (dynamic) {
     std::memcpy(blob + L.dyn_base, base.data(), base.size());
@@ -908,6 +965,7 @@ extern "C" attn_status attn_plan_get_layout(const attn_plan *plan, attn_plan_lay
   out->off_bwd_list = L.bwd_list; out->n_bwd_list = L.n_bwd_list;
   out->off_bits = L.bits; out->off_qblk = L.qblk; out->off_kblk = L.kblk;
   out->off_qoffs = L.qoffs; out->off_koffs = L.koffs;
+  out->off_kwords = L.kwords; out->off_rwords = L.rwords;
   out->off_bwd_slot = L.bwd_slot;
   out->off_bwd_reduce = L.bwd_reduce; out->n_bwd_reduce = L.n_bwd_reduce;
   out->n_slots = L.n_slots;

@@ -22,6 +22,7 @@ constexpr uint32_t kPartialBit = 0x80000000u;
 constexpr int kHeadShift = 24;   // dK/dV (Q-tile, head) entries: head in bits 24-30
 constexpr int kMaxEntryHeads = 128;
 constexpr int kMaxDynEntryHeads = 64;  // the device list compiler keeps a 64-bit head mask
+constexpr int64_t kMaxMaskWordBytes = int64_t(4) << 30;  // both bitmap word tables
 // Class of a 64x64 micro tile (stored as uint8 in a dynamic plan's blob).
 enum : uint8_t { kEmpty = 0, kPartial = 1, kFull = 2 };
 
@@ -31,6 +32,11 @@ struct Layout {
   int64_t fwd_items = -1, fwd_list = -1, bwd_items = -1, bwd_list = -1;
   int64_t bwd_slot = -1, bwd_reduce = -1;
   int64_t bits = -1, qblk = -1, kblk = -1, qoffs = -1, koffs = -1;
+  // static plans whose bitmap blocks cut 64-wide tiles: the bitmap part of
+  // the mask as 64-bit words, allowed keys of micro-tile J for row block qb
+  // [heads][nqb][nM] and allowed rows of micro-tile I for key block kb
+  // [heads][nkb][nM]
+  int64_t kwords = -1, rwords = -1;
   int64_t n_fwd_items = 0, n_fwd_list = 0, n_bwd_items = 0, n_bwd_list = 0;
   int64_t n_bwd_reduce = 0, n_slots = 0;
   // dynamic plans only: base micro-tile classes, (length, partial tiles) of

@@ -234,6 +234,46 @@ def test_narrow_dkdv_items_cover_mask_exactly(Hq, Hkv):
         _check_lists(p, spec, Hq, Hkv)
 
 
+@pytest.mark.parametrize("S,heads,kind", [(700, 2, "variable"), (333, 3, "distinct"), (512, 1, "uniform64"),
+                                           (1000, 4, "uniform96")])
+def test_bitmap_words_equal_the_bitmap(S, heads, kind):
+    """The plan's bitmap words against the bitmap itself: bit c of word
+    (h, qb, t) is bitmap[h][qb][kblk(64 t + c)] for keys below S, 0 beyond;
+    bit r of row word (h, kb, t) is bitmap[h][qblk(64 t + r)][kb].  Plans
+    whose blocks do not cut 64-wide tiles, and dynamic plans, have none."""
+    if kind == "variable":
+        qo = ko = syn.variable_partition(S, 20, 150, 4)
+        bits = syn.partition_bitmap(qo, ko, heads, 0.5, 5)
+    elif kind == "distinct":
+        qo, ko = syn.variable_partition(S, 20, 90, 6), syn.variable_partition(S, 30, 120, 7)
+        bits = syn.partition_bitmap(qo, ko, heads, 0.5, 8)
+    else:
+        qo, bits = syn.uniform_block_bitmap(S, int(kind[7:]), heads, 0.5, 9)
+        ko = qo
+    spec = syn.with_bitmap(syn.spec_causal(S), qo, ko, bits)
+    lay = lcm.Plan(1, S, heads, heads, 64, spec).layout()
+    if kind == "uniform64":
+        assert "kwords" not in lay and "rwords" not in lay
+        return
+    kblk = np.searchsorted(np.asarray(ko), np.arange(S), side="right") - 1
+    qblk = np.searchsorted(np.asarray(qo), np.arange(S), side="right") - 1
+    nM = (S + 63) // 64
+    pad = nM * 64 - S
+    b = np.asarray(bits, dtype=bool)
+    # allowed keys: [h][qb][key] -> words over 64-key tiles
+    keys = np.concatenate([b[:, :, kblk], np.zeros(b.shape[:2] + (pad,), dtype=bool)], axis=2)
+    rows = np.concatenate([b[:, qblk, :].transpose(0, 2, 1), np.zeros((b.shape[0], b.shape[2], pad), dtype=bool)], axis=2)
+
+    def words(x):
+        x = x.reshape(x.shape[0], x.shape[1], nM, 64).astype(np.uint64)
+        return (x << np.arange(64, dtype=np.uint64)).sum(axis=3, dtype=np.uint64)
+
+    assert np.array_equal(lay["kwords"], words(keys))
+    assert np.array_equal(lay["rwords"], words(rows))
+    assert "kwords" not in lcm.Plan(1, S, 4, 1, 64, dict(syn.with_bitmap(syn.spec_causal(S), qo, ko, bits[:1]),
+                                                         dynamic=True)).layout()
+
+
 def _empty_half_fraction(spec, S):
     """Of the 128-key (64-row, 128-key) tiles with an allowed pair, the
     fraction whose 64-key halves are not both non-empty: brute force over
