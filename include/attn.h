@@ -222,8 +222,10 @@ typedef struct {
   /* uint64 [bitmap heads][n_qblk][ceil(S/64)]: allowed keys of 64-key tile t
    * for rows of bitmap row block qb (bit c: key 64 t + c), and uint64
    * [bitmap heads][n_kblk][ceil(S/64)]: allowed rows of 64-row tile t for
-   * keys of column block kb; the bitmap part of the mask only.  Static plans
-   * whose blocks cut 64-wide tiles, up to 4 GiB for both; else -1. */
+   * keys of column block kb; the bitmap part of the mask only.  Plans whose
+   * blocks cut 64-wide tiles, up to 4 GiB for both (dynamic plans: for the
+   * creation bitmap; attn_plan_set_bitmap rebuilds them on the device);
+   * else -1. */
   int64_t off_kwords, off_rwords;
 } attn_plan_layout;
 

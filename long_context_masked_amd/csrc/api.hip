@@ -150,6 +150,17 @@ extern "C" attn_status attn_plan_set_bitmap(attn_plan *plan, const uint8_t *bits
   a.bcap = D.bcap;
   a.head_major = D.head_major ? 1 : 0;
   a.fkv = D.fkv;
+  a.bm_heads = plan->bitmap_heads;
+  if (L.kwords >= 0) {
+    a.kwords = reinterpret_cast<uint64_t *>(blob + L.kwords);
+    a.rwords = reinterpret_cast<uint64_t *>(blob + L.rwords);
+    a.kseg_off = reinterpret_cast<const int *>(blob + L.dyn_kseg_off);
+    a.kseg_blk = reinterpret_cast<const int *>(blob + L.dyn_kseg_blk);
+    a.kseg_mask = reinterpret_cast<const uint64_t *>(blob + L.dyn_kseg_mask);
+    a.rseg_off = reinterpret_cast<const int *>(blob + L.dyn_rseg_off);
+    a.rseg_blk = reinterpret_cast<const int *>(blob + L.dyn_rseg_blk);
+    a.rseg_mask = reinterpret_cast<const uint64_t *>(blob + L.dyn_rseg_mask);
+  }
   (void)hipGetLastError();
   const hipError_t e = launch_dyn(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "list rebuild launch failed: %s", hipGetErrorString(e));

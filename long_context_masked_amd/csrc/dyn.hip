@@ -21,6 +21,8 @@
 // Forward / dQ lists run over key tiles J ascending, dK/dV lists over
 // Q-tiles I descending (the order the host gives them).
 //
+// Plans with bitmap words get a third launch that rebuilds them.
+//
 // A second launch puts the work items back in longest-first order, the
 // order that keeps the tail of a launch short.  The item array is dealt to
 // XCD shares at creation (each XCD's workgroups serve a fixed set of heads,
@@ -250,6 +252,35 @@ __global__ __launch_bounds__(kSortThreads) void attn_dyn_sort_kernel(DynArgs a) 
   }
 }
 
+// Bitmap words for the new bitmap, one thread per word: the allowed keys of
+// key tile t for row block qb, [heads][nqb][nM], then the allowed rows of
+// Q-tile t for key block kb, [heads][nkb][nM]; each the OR of the tile's
+// block segments whose bit is on (the host's rule, on the same segments).
+__global__ __launch_bounds__(256) void attn_dyn_words_kernel(DynArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nk = (int64_t)a.bm_heads * a.nqb * a.nM;
+  const int64_t nr = (int64_t)a.bm_heads * a.nkb * a.nM;
+  if (i < nk) {
+    const int t = (int)(i % a.nM);
+    const int64_t hq = i / a.nM;  // h * nqb + qb
+    const uint8_t *row = a.src + hq * a.nkb;
+    uint64_t w = 0;
+    for (int s = a.kseg_off[t]; s < a.kseg_off[t + 1]; ++s)
+      if (row[a.kseg_blk[s]]) w |= a.kseg_mask[s];
+    a.kwords[i] = w;
+  } else if (i < nk + nr) {
+    const int64_t j = i - nk;
+    const int t = (int)(j % a.nM);
+    const int64_t hk = j / a.nM;  // h * nkb + kb
+    const int kb = (int)(hk % a.nkb), h = (int)(hk / a.nkb);
+    const uint8_t *col = a.src + (int64_t)h * a.nqb * a.nkb + kb;
+    uint64_t w = 0;
+    for (int s = a.rseg_off[t]; s < a.rseg_off[t + 1]; ++s)
+      if (col[(int64_t)a.rseg_blk[s] * a.nkb]) w |= a.rseg_mask[s];
+    a.rwords[j] = w;
+  }
+}
+
 hipError_t launch_dyn(const DynArgs &a0, hipStream_t st) {
   DynArgs a = a0;
   const int64_t n16 = a.nbits / 16;
@@ -261,6 +292,10 @@ hipError_t launch_dyn(const DynArgs &a0, hipStream_t st) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_dyn_sort_kernel, dim3((unsigned)(a.n_fshares + a.n_bshares)),
                      dim3(kSortThreads), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.kwords == nullptr) return e;
+  const int64_t nw = (int64_t)a.bm_heads * (a.nqb + a.nkb) * a.nM;
+  hipLaunchKernelGGL(attn_dyn_words_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

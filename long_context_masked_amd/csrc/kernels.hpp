@@ -391,6 +391,12 @@ struct DynArgs {
   int64_t bcap;            // dK/dV list capacity per slot (nM, or nM * bheads)
   int head_major;          // 1: XCD shares hold several KV heads, sorted by head first
   int fkv;                 // query heads per KV head (forward items carry a query head)
+  // bitmap words (or null): [bm_heads][nqb][nM] allowed keys, [bm_heads][nkb][nM]
+  // allowed rows, rebuilt from the tiles' block segments
+  uint64_t *kwords, *rwords;
+  const int *kseg_off, *kseg_blk, *rseg_off, *rseg_blk;
+  const uint64_t *kseg_mask, *rseg_mask;
+  int bm_heads;
 };
 
 // Zeros over half hh of a D-wide row (the two lane halves split it).

@@ -769,12 +769,15 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     L.qoffs = sect((int64_t)(bm.nqb + 1) * 4);
     L.koffs = sect((int64_t)(bm.nkb + 1) * 4);
   }
-  // Bitmap words of static plans whose blocks cut tiles: the mask of a
-  // partial tile then costs the kernels one 8-byte load per lane instead of
-  // a walk over the blocks the tile touches.  Dynamic plans walk the blocks
-  // (their bitmap changes on the device).
+  // Bitmap words of plans whose blocks cut tiles: the mask of a partial tile
+  // then costs the kernels one 8-byte load per lane instead of a walk over
+  // the blocks the tile touches.  A dynamic plan also keeps each tile's block
+  // segments, from which the device rebuilds the words for a new bitmap.
   bool words = false;
-  if (has_bm && !dynamic) {
+  struct Seg { int32_t blk; uint64_t mask; };
+  std::vector<std::vector<Seg>> kseg, qseg;
+  int64_t n_kseg = 0, n_qseg = 0;
+  if (has_bm) {
     bool cut = false;
     for (int64_t t = 0; t < nM && !cut; ++t) {
       const int64_t a = t * kMicro, e = std::min<int64_t>(S, a + kMicro) - 1;
@@ -785,6 +788,34 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     if (words) {
       L.kwords = sect((int64_t)bm.heads * bm.nqb * nM * 8);
       L.rwords = sect((int64_t)bm.heads * bm.nkb * nM * 8);
+      // The blocks a 64-wide tile touches, each with the bits of the tile it
+      // covers: word(tile, block line) = OR of the segments whose bitmap bit
+      // is on.
+      auto segments = [&](const std::vector<int32_t> &blk_of, const std::vector<int32_t> &offs,
+                          int64_t &count) {
+        std::vector<std::vector<Seg>> out((size_t)nM);
+        for (int64_t t = 0; t < nM; ++t) {
+          const int64_t a = t * kMicro, e = std::min<int64_t>(S, a + kMicro);
+          for (int32_t b = blk_of[(size_t)a]; b <= blk_of[(size_t)(e - 1)]; ++b) {
+            const int64_t lo = std::max<int64_t>(offs[(size_t)b], a) - a;
+            const int64_t hi = std::min<int64_t>(offs[(size_t)b + 1], e) - a;
+            const uint64_t top = hi == 64 ? ~0ull : ((1ull << hi) - 1ull);
+            out[(size_t)t].push_back({b, top & ~((1ull << lo) - 1ull)});
+            ++count;
+          }
+        }
+        return out;
+      };
+      kseg = segments(bm.kblk, bm.koffs, n_kseg);
+      qseg = segments(bm.qblk, bm.qoffs, n_qseg);
+      if (dynamic) {
+        L.dyn_kseg_off = sect((nM + 1) * 4);
+        L.dyn_kseg_blk = sect(n_kseg * 4);
+        L.dyn_kseg_mask = sect(n_kseg * 8);
+        L.dyn_rseg_off = sect((nM + 1) * 4);
+        L.dyn_rseg_blk = sect(n_qseg * 4);
+        L.dyn_rseg_mask = sect(n_qseg * 8);
+      }
     }
   }
   std::vector<int32_t> fsh_off, fsh_pos, bsh_off, bsh_pos;
@@ -854,24 +885,6 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
     std::memcpy(blob + L.koffs, bm.koffs.data(), bm.koffs.size() * 4);
   }
   if (words) {
-    // The blocks a 64-wide tile touches, each with the bits of the tile it
-    // covers: word(tile, block line) = OR of the segments whose bitmap bit
-    // is on.
-    struct Seg { int32_t blk; uint64_t mask; };
-    auto segments = [&](const std::vector<int32_t> &blk_of, const std::vector<int32_t> &offs) {
-      std::vector<std::vector<Seg>> out((size_t)nM);
-      for (int64_t t = 0; t < nM; ++t) {
-        const int64_t a = t * kMicro, e = std::min<int64_t>(S, a + kMicro);
-        for (int32_t b = blk_of[(size_t)a]; b <= blk_of[(size_t)(e - 1)]; ++b) {
-          const int64_t lo = std::max<int64_t>(offs[(size_t)b], a) - a;
-          const int64_t hi = std::min<int64_t>(offs[(size_t)b + 1], e) - a;
-          const uint64_t top = hi == 64 ? ~0ull : ((1ull << hi) - 1ull);
-          out[(size_t)t].push_back({b, top & ~((1ull << lo) - 1ull)});
-        }
-      }
-      return out;
-    };
-    const auto kseg = segments(bm.kblk, bm.koffs), qseg = segments(bm.qblk, bm.qoffs);
     uint64_t *kw = reinterpret_cast<uint64_t *>(blob + L.kwords);
     uint64_t *rw = reinterpret_cast<uint64_t *>(blob + L.rwords);
     for (int h = 0; h < bm.heads; ++h) {
@@ -890,6 +903,21 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
             if (bh[(size_t)g.blk * bm.nkb + kb]) w |= g.mask;
           rw[((int64_t)h * bm.nkb + kb) * nM + t] = w;
         }
+    }
+    if (dynamic) {
+      auto put = [&](const std::vector<std::vector<Seg>> &sg, int64_t off, int64_t blk, int64_t mask) {
+        int32_t *o = reinterpret_cast<int32_t *>(blob + off);
+        int32_t *b = reinterpret_cast<int32_t *>(blob + blk);
+        uint64_t *m = reinterpret_cast<uint64_t *>(blob + mask);
+        int32_t n = 0;
+        for (int64_t t = 0; t < nM; ++t) {
+          o[t] = n;
+          for (const Seg &g : sg[(size_t)t]) { b[n] = g.blk; m[n] = g.mask; ++n; }
+        }
+        o[nM] = n;
+      };
+      put(kseg, L.dyn_kseg_off, L.dyn_kseg_blk, L.dyn_kseg_mask);
+      put(qseg, L.dyn_rseg_off, L.dyn_rseg_blk, L.dyn_rseg_mask);
     }
   }
   if (dynamic) {

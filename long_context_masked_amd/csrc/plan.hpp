@@ -37,6 +37,11 @@ struct Layout {
   // [heads][nqb][nM] and allowed rows of micro-tile I for key block kb
   // [heads][nkb][nM]
   int64_t kwords = -1, rwords = -1;
+  // dynamic plans with bitmap words: the blocks each 64-wide tile touches,
+  // with the tile bits each covers (CSR by tile: offsets [nM + 1], block
+  // indices, masks), so that the device rebuilds the words for a new bitmap
+  int64_t dyn_kseg_off = -1, dyn_kseg_blk = -1, dyn_kseg_mask = -1;
+  int64_t dyn_rseg_off = -1, dyn_rseg_blk = -1, dyn_rseg_mask = -1;
   int64_t n_fwd_items = 0, n_fwd_list = 0, n_bwd_items = 0, n_bwd_list = 0;
   int64_t n_bwd_reduce = 0, n_slots = 0;
   // dynamic plans only: base micro-tile classes, (length, partial tiles) of

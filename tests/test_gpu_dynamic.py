@@ -93,11 +93,15 @@ def _check_lists_equal(dyn, spec_new, B, Hq, Hkv, d, bits_new):
     # the ordinary plan for the new bitmap, with the dynamic plan's dK/dV item
     # width (chosen from its creation bitmap)
     ref = lcm.Plan(B, spec_new["S"], Hq, Hkv, d, dict(spec_new, bwd_key_tile=dyn.stats["bwd_tile_cols"]))
-    fs, bs = lists_by_item(ref.layout())
+    rl = ref.layout()
+    fs, bs = lists_by_item(rl)
     dl = dyn.device_layout()
     fd, bd = lists_by_item(dl)
     assert fd == fs, "forward / dQ lists differ from the host compiler's"
     assert bd == bs, "dK/dV lists differ from the host compiler's"
+    assert ("kwords" in dl) == ("kwords" in rl)
+    if "kwords" in dl:  # bitmap words rebuilt on the device, against the host's
+        assert np.array_equal(dl["kwords"], rl["kwords"]) and np.array_equal(dl["rwords"], rl["rwords"])
     fresh = lcm.Plan(B, spec_new["S"], Hq, Hkv, d,
                      dict(spec_new, dynamic=True, bwd_key_tile=dyn.stats["bwd_tile_cols"]))
     _check_items(dl, fresh.layout(), Hkv)

@@ -240,7 +240,8 @@ def test_bitmap_words_equal_the_bitmap(S, heads, kind):
     """The plan's bitmap words against the bitmap itself: bit c of word
     (h, qb, t) is bitmap[h][qb][kblk(64 t + c)] for keys below S, 0 beyond;
     bit r of row word (h, kb, t) is bitmap[h][qblk(64 t + r)][kb].  Plans
-    whose blocks do not cut 64-wide tiles, and dynamic plans, have none."""
+    whose blocks do not cut 64-wide tiles have none; dynamic plans have the
+    same words for their creation bitmap."""
     if kind == "variable":
         qo = ko = syn.variable_partition(S, 20, 150, 4)
         bits = syn.partition_bitmap(qo, ko, heads, 0.5, 5)
@@ -270,8 +271,9 @@ def test_bitmap_words_equal_the_bitmap(S, heads, kind):
 
     assert np.array_equal(lay["kwords"], words(keys))
     assert np.array_equal(lay["rwords"], words(rows))
-    assert "kwords" not in lcm.Plan(1, S, 4, 1, 64, dict(syn.with_bitmap(syn.spec_causal(S), qo, ko, bits[:1]),
-                                                         dynamic=True)).layout()
+    # a dynamic plan holds the same words for its creation bitmap
+    dl = lcm.Plan(1, S, heads, heads, 64, dict(spec, dynamic=True)).layout()
+    assert np.array_equal(dl["kwords"], lay["kwords"]) and np.array_equal(dl["rwords"], lay["rwords"])
 
 
 def _empty_half_fraction(spec, S):
