@@ -182,6 +182,38 @@ def merge_rate(lcm, torch, dev, S=16384, Hq=64, d=128, reps=20):
             "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def reference_gemm(torch, dev, sizes=(8192, 16384)):
+    """Rate of the vendor GEMM on this machine, for context beside the kernels'
+    rates: torch.matmul of two contiguous n x n bf16 matrices (hipBLASLt),
+    HIP events on the current stream.  A plain GEMM has no softmax or mask
+    and streams each operand once per output tile; on this chip its rate sits
+    well below the nominal peak because the clock drops under full matrix
+    load, and the attention kernels meet the same limit."""
+    out = {"op": "torch.matmul, bf16 [n, n] x [n, n] (vendor BLAS), HIP events", "tflops": {}}
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev).manual_seed(0)
+    for n in sizes:
+        a = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+        b = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+        for _ in range(3):
+            c = a @ b
+        reps = max(3, int(4e13 / (2 * n ** 3)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            c = a @ b
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out["tflops"][str(n)] = round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+        del a, b, c
+    best = max(out["tflops"].values())
+    out["best_tflops"] = best
+    out["fraction_of_peak"] = _frac(best)
+    return out
+
+
 def dynamic_rebuild(lcm, torch, dev, tensors_for, reps=20, steps=3):
     """Dynamic block-sparse plans: time of one attn_plan_set_bitmap (the
     device list rebuild, HIP events on the launch stream) against the host
@@ -649,6 +681,9 @@ def main():
     run.free()
     log("merge of partial results")
     out["merge"] = merge_rate(lcm, torch, dev)
+    log("reference GEMM")
+    out["reference_gemm"] = reference_gemm(torch, dev)
+    out["roofline"]["frac_of_reference_gemm"] = round(achieved / out["reference_gemm"]["best_tflops"], 4)
     if args.workload == "sparse" and not args.no_dynamic:
         log("dynamic block-sparse: device list rebuild")
         dyn_run = Runner(lcm, torch, dev, [])

@@ -150,7 +150,10 @@ typedef struct {
  * tiles of the first item group have an empty 64-key half (bitmap blocks 64
  * keys wide; a dynamic plan decides on its creation bitmap);
  * stats.bwd_tile_cols reports it.  bwd_key_tile outside {0, 64, 128} is
- * ATTN_ERR_INVALID.
+ * ATTN_ERR_INVALID.  The lists of different mask heads (or, with one bitmap
+ * per query head, KV heads) are built on up to 16 host threads of the
+ * calling process and joined in head order, so the plan is the same for any
+ * thread count; the call returns after every thread has joined.
  */
 attn_status attn_plan_create(const attn_shape *shape, const attn_mask_desc *desc,
                              attn_plan **out);

@@ -27,7 +27,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"
 # lets max chains fold into v_max3_f32 without canonicalisation.
 HIP_FLAGS = COMMON + [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
                       "-packed-fp32-ops", "-fno-honor-nans", "-Wno-unused-command-line-argument"]
-CXX_FLAGS = COMMON + ["-Wall", "-Wextra", "-Wno-unused-parameter"]
+CXX_FLAGS = COMMON + ["-Wall", "-Wextra", "-Wno-unused-parameter", "-pthread"]
 
 
 def _run(cmd, verbose):
@@ -128,7 +128,7 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
     scan_transposed_reads(texts)
     objs = [os.path.join(OUT_DIR, s + ".o") for s in HIP_SOURCES + CXX_SOURCES]
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -22,6 +22,7 @@
 //  6. order work items longest first and lay everything out in one blob.
 #include <algorithm>
 #include <array>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -29,6 +30,8 @@
 #include <limits>
 #include <new>
 #include <set>
+#include <system_error>
+#include <thread>
 
 #include "plan.hpp"
 
@@ -389,6 +392,41 @@ extern "C" const char *attn_last_error(void) { return g_err.c_str(); }
 
 extern "C" const char *attn_version(void) { return "long_context_masked_amd 0.1 (gfx950)"; }
 
+// Host threads for plan compilation: the cores the process may use, at most
+// 16 (the work units are mask heads or KV heads, and a plan's memory grows
+// with the threads' scratch).
+static int host_threads() {
+  const unsigned hw = std::thread::hardware_concurrency();
+  return (int)std::max(1u, std::min(hw == 0 ? 1u : hw, 16u));
+}
+
+// f(i) for i in [0, n), on up to host_threads() threads (the caller's
+// included); each thread first builds its own scratch with make().  Returns
+// false if an allocation failed (the remaining work is then skipped).
+template <class Make, class F>
+static bool parallel_for(int n, Make make, F f) {
+  const int n_threads = std::max(1, std::min(n, host_threads()));
+  std::atomic<int> next{0};
+  std::atomic<bool> oom{false};
+  auto worker = [&]() {
+    try {
+      auto scratch = make();
+      for (int i = next++; i < n && !oom; i = next++) f(i, scratch);
+    } catch (const std::bad_alloc &) {
+      oom = true;
+    }
+  };
+  std::vector<std::thread> pool;
+  try {
+    for (int t = 1; t < n_threads; ++t) pool.emplace_back(worker);
+  } catch (const std::system_error &) {
+    // fewer threads: the ones started and the caller share the work
+  }
+  worker();
+  for (auto &t : pool) t.join();
+  return !oom;
+}
+
 static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc *desc,
                                     attn_plan **out) {
   if (!shp || !desc || !out) return fail(ATTN_ERR_INVALID, "NULL argument");
@@ -519,8 +557,11 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   std::vector<int64_t> nnz_head((size_t)n_mask_heads, nnz_base);
   // Tile class of a union over the mask heads `hs` (classifications in C):
   // bit 0 = some pair allowed, bit 1 = every pair allowed.
+  // Offsets are relative to the lists passed in (one mask head's, or one KV
+  // head's); the caller concatenates them in head order.
   auto lists_for = [&](const std::vector<const std::vector<uint8_t> *> &C, int64_t fslot0,
-                       bool do_fwd, int64_t bslot0, bool do_bwd) {
+                       bool do_fwd, int64_t bslot0, bool do_bwd, std::vector<uint32_t> &fwd_list,
+                       std::vector<uint32_t> &bwd_list) {
     if (do_fwd)
       for (int64_t qt = 0; qt < nFQ; ++qt) {
         const size_t slot = (size_t)(fslot0 + qt);
@@ -588,11 +629,16 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
         bwd_npart[slot] = npart;
       }
   };
-  if (per_qhead) {
-    // one KV head at a time: its G classifications, its forward groups and
-    // its dK/dV group
-    std::vector<std::vector<uint8_t>> cls((size_t)G);
-    for (int64_t kvh = 0; kvh < sh.Hkv; ++kvh) {
+  // Work units: one KV head (one bitmap per query head: its G
+  // classifications, its forward groups and its dK/dV group) or one mask
+  // head.  Units are independent; each builds its own lists, on as many host
+  // threads as there are cores, and the lists are then joined in unit order,
+  // so the plan does not depend on the thread count.
+  const int n_units = per_qhead ? (int)sh.Hkv : n_mask_heads;
+  std::vector<std::vector<uint32_t>> unit_f((size_t)n_units), unit_b((size_t)n_units);
+  auto run_unit = [&](int u, std::vector<std::vector<uint8_t>> &cls) {
+    if (per_qhead) {
+      const int64_t kvh = u;
       for (int g = 0; g < G; ++g) {
         const int hm = (int)(kvh * G + g);
         classify_bitmap(S, base, bm, hm, cls[(size_t)g]);
@@ -601,22 +647,50 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
       for (int g0 = 0; g0 < G; g0 += p->HG) {
         std::vector<const std::vector<uint8_t> *> C;
         for (int g = g0; g < g0 + p->HG; ++g) C.push_back(&cls[(size_t)g]);
-        lists_for(C, (int64_t)fgroup_of(kvh * G + g0) * nFQ, true, 0, false);
+        lists_for(C, (int64_t)fgroup_of(kvh * G + g0) * nFQ, true, 0, false, unit_f[(size_t)u],
+                  unit_b[(size_t)u]);
       }
       std::vector<const std::vector<uint8_t> *> C;
       for (int g = 0; g < G; ++g) C.push_back(&cls[(size_t)g]);
-      lists_for(C, 0, false, (int64_t)bgroup_of(kvh) * nBK, true);
-    }
-  } else {
-    std::vector<uint8_t> cls;
-    for (int hm = 0; hm < n_mask_heads; ++hm) {
+      lists_for(C, 0, false, (int64_t)bgroup_of(kvh) * nBK, true, unit_f[(size_t)u], unit_b[(size_t)u]);
+    } else {
+      const int hm = u;
       const std::vector<uint8_t> *C = &base;
       if (has_bm) {
-        classify_bitmap(S, base, bm, hm, cls);
-        C = &cls;
-        nnz_head[hm] = nnz_with_bitmap(S, rowb, bm, hm);
+        classify_bitmap(S, base, bm, hm, cls[0]);
+        C = &cls[0];
+        nnz_head[(size_t)hm] = nnz_with_bitmap(S, rowb, bm, hm);
       }
-      lists_for({C}, (int64_t)hm * nFQ, true, (int64_t)hm * nBK, true);
+      lists_for({C}, (int64_t)hm * nFQ, true, (int64_t)hm * nBK, true, unit_f[(size_t)u],
+                unit_b[(size_t)u]);
+    }
+  };
+  if (!parallel_for(n_units, [&]() { return std::vector<std::vector<uint8_t>>(per_qhead ? (size_t)G : 1); },
+                    run_unit)) {
+    delete p;
+    return fail(ATTN_ERR_NOMEM, "host work lists");
+  }
+  // Join the units' lists in unit order: a unit owns the forward slots of its
+  // list groups and the dK/dV slots of its group.
+  {
+    const int64_t fpu = (int64_t)n_fgroups / n_units * nFQ, bpu = (int64_t)n_bgroups / n_units * nBK;
+    size_t nf = 0, nb = 0;
+    for (int u = 0; u < n_units; ++u) { nf += unit_f[(size_t)u].size(); nb += unit_b[(size_t)u].size(); }
+    try {
+      fwd_list.reserve(nf);
+      bwd_list.reserve(nb);
+    } catch (const std::bad_alloc &) {
+      delete p;
+      return fail(ATTN_ERR_NOMEM, "host work lists");
+    }
+    for (int u = 0; u < n_units; ++u) {
+      const int64_t f0 = (int64_t)fwd_list.size(), b0 = (int64_t)bwd_list.size();
+      for (int64_t sl = u * fpu; sl < (u + 1) * fpu; ++sl) fwd_off[(size_t)sl] += f0;
+      for (int64_t sl = u * bpu; sl < (u + 1) * bpu; ++sl) bwd_off[(size_t)sl] += b0;
+      fwd_list.insert(fwd_list.end(), unit_f[(size_t)u].begin(), unit_f[(size_t)u].end());
+      bwd_list.insert(bwd_list.end(), unit_b[(size_t)u].begin(), unit_b[(size_t)u].end());
+      std::vector<uint32_t>().swap(unit_f[(size_t)u]);
+      std::vector<uint32_t>().swap(unit_b[(size_t)u]);
     }
   }
   if (dynamic) {
@@ -887,7 +961,8 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
   if (words) {
     uint64_t *kw = reinterpret_cast<uint64_t *>(blob + L.kwords);
     uint64_t *rw = reinterpret_cast<uint64_t *>(blob + L.rwords);
-    for (int h = 0; h < bm.heads; ++h) {
+    // one bitmap head per task; heads fill disjoint rows of both tables
+    parallel_for(bm.heads, []() { return 0; }, [&](int h, int) {
       const uint8_t *bh = bm.bits.data() + (size_t)h * bm.nqb * bm.nkb;
       for (int32_t qb = 0; qb < bm.nqb; ++qb)
         for (int64_t t = 0; t < nM; ++t) {
@@ -903,7 +978,7 @@ static attn_status plan_create_impl(const attn_shape *shp, const attn_mask_desc 
             if (bh[(size_t)g.blk * bm.nkb + kb]) w |= g.mask;
           rw[((int64_t)h * bm.nkb + kb) * nM + t] = w;
         }
-    }
+    });
     if (dynamic) {
       auto put = [&](const std::vector<std::vector<Seg>> &sg, int64_t off, int64_t blk, int64_t mask) {
         int32_t *o = reinterpret_cast<int32_t *>(blob + off);

@@ -234,6 +234,32 @@ def test_narrow_dkdv_items_cover_mask_exactly(Hq, Hkv):
         _check_lists(p, spec, Hq, Hkv)
 
 
+@pytest.mark.parametrize("Hq,Hkv,bm_heads", [(16, 16, 16), (16, 2, 16), (16, 2, 2)])
+def test_plan_independent_of_host_threads(Hq, Hkv, bm_heads):
+    """The plan compiler builds each head's lists on its own host thread and
+    joins them in head order: the blob is the same on every build, and each
+    head's forward entries follow the previous head's."""
+    S = 1500
+    offs, bits = syn.variable_block_bitmap(S, 20, 150, bm_heads, 0.5, seed=11)
+    spec = syn.with_bitmap(syn.spec_causal(S), offs, offs, bits)
+    blobs = []
+    for _ in range(3):
+        p = lcm.Plan(1, S, Hq, Hkv, 128, spec)
+        lay = L.Layout()
+        L.check(L.lib().attn_plan_get_layout(p.handle, C.byref(lay)))
+        blobs.append(np.ctypeslib.as_array((C.c_uint8 * lay.blob_bytes).from_address(lay.blob)).copy())
+        del p
+    assert all(np.array_equal(blobs[0], b) for b in blobs[1:])
+    p = lcm.Plan(1, S, Hq, Hkv, 128, spec)
+    items = p.layout()["fwd_items"]
+    first = {}
+    for qt, h0, off, n in items:
+        first[int(h0)] = min(first.get(int(h0), 1 << 62), int(off))
+    heads = sorted(first)
+    assert [first[h] for h in heads] == sorted(first[h] for h in heads)
+    _check_lists(p, spec, Hq, Hkv)
+
+
 @pytest.mark.parametrize("S,heads,kind", [(700, 2, "variable"), (333, 3, "distinct"), (512, 1, "uniform64"),
                                            (1000, 4, "uniform96")])
 def test_bitmap_words_equal_the_bitmap(S, heads, kind):
