@@ -264,7 +264,9 @@ void desc_cache() {
 
 // Several threads share the descriptor cache: lookups, uploads into their
 // own buffers, launches, releases and (one thread) cache clears, plus plan
-// creation and the thread-local error string.  Run under ThreadSanitizer.
+// creation (with bitmaps of several heads, whose lists the compiler builds
+// on threads of its own) and the thread-local error string.  Run under
+// ThreadSanitizer.
 void threads() {
   constexpr int NT = 4, IT = 150, NMASK = 40;
   std::vector<std::thread> ts;
@@ -302,6 +304,22 @@ void threads() {
         const std::string e = attn_last_error();
         if (e.empty()) ++fails[t];
         if (make(1, 64 + i, 4, 2, 64, blank(ATTN_MASK_CAUSAL), false) != ATTN_OK) ++fails[t];
+        if (it % 10 == 0) {
+          // bitmaps of several heads: the plan compiler builds their lists on
+          // host threads of its own, inside each calling thread
+          const int S2 = 300 + i;
+          std::vector<int32_t> qo{0};
+          while (qo.back() < S2) qo.push_back(std::min(S2, qo.back() + 16 + (int)(next() % 100)));
+          const int nq = (int)qo.size() - 1, heads = (it % 20 == 0) ? 8 : 2;
+          std::vector<uint8_t> b((size_t)heads * nq * nq);
+          for (auto &x : b) x = (uint8_t)(next() % 2);
+          attn_mask_desc bm = blank(ATTN_MASK_CAUSAL);
+          bm.block_bitmap = b.data();
+          bm.bitmap_heads = heads;
+          bm.n_qblk = bm.n_kblk = nq;
+          bm.q_blk_offsets = bm.k_blk_offsets = qo.data();
+          if (make(1, S2, 8, 2, 64, bm, false) != ATTN_OK) ++fails[t];
+        }
         if (t == 0 && it % 37 == 36) attn_desc_cache_clear();
       }
     });
