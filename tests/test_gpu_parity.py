@@ -306,7 +306,7 @@ def test_smoke_entry_point():
     __graft_entry__.smoke()
 
 
-def _random_configs(n=14, seed=2026):
+def _random_configs(n=14, seed=2026, tag="r"):
     """Seeded random shapes, masks and plan options: S in [65, 900], KV heads
     1-16 with groups of 1-4 (16 KV heads put two heads in each XCD share),
     both head dims, batches of 1-2, every base family, bitmaps per KV head
@@ -350,11 +350,11 @@ def _random_configs(n=14, seed=2026):
         tile = int(rng.choice([0, 0, 64, 128]))
         if tile:
             spec = dict(spec, bwd_key_tile=tile)
-        out.append((f"r{i}_S{S}_B{B}_{Hq}x{Hkv}_d{d}_{base['family']}_bm{bm}_k{tile}", spec, B, Hq, Hkv, d))
+        out.append((f"{tag}{i}_S{S}_B{B}_{Hq}x{Hkv}_d{d}_{base['family']}_bm{bm}_k{tile}", spec, B, Hq, Hkv, d))
     return out
 
 
-RANDOM = _random_configs()
+RANDOM = _random_configs() + _random_configs(16, 4049, "q")
 
 
 @pytest.mark.parametrize("label,spec,B,Hq,Hkv,d", RANDOM, ids=[c[0] for c in RANDOM])
